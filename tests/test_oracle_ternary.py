@@ -1,0 +1,146 @@
+"""Pins of the ternary oracle against the Ternary post and closed forms."""
+import numpy as np
+
+from oracle import fpformat, ternary
+from conftest import load_golden
+
+import wq_inputs
+
+
+def _ints(v):
+    return [int(t) for t in v]
+
+
+def test_format_sizes():
+    g = load_golden("ptq1_0_layout.txt")
+    assert ternary.BLOCK_BYTES == int(g["block_bytes"][0])
+    assert ternary.Q8_BYTES == int(g["q8_1_bytes"][0])
+    blk = ternary.encode_ptq1_0(np.zeros((1, 128), np.int8), np.zeros((1, 1), np.uint16))
+    assert blk.shape == (1, 1, 28)
+    # trit counts per section: 16 bytes x 5 + 8 bytes x 5 = 120, and 8 in qh
+    kinds = [ternary.trit_position(e)[0] for e in range(128)]
+    assert kinds.count("qs") == int(g["qs_trits"][0]) and kinds.count("qh") == int(g["qh_trits"][0])
+    # superblock arithmetic: 192 + 13 + 10 (eight 10-bit mantissas) + 1 bytes
+    sb = 192 + 13 + 8 * 10 // 8 + 1
+    assert sb == int(g["superblock_bytes"][0])
+    assert 8 * ternary.BLOCK_BYTES == int(g["plain_bytes_per_1024"][0])
+    assert (8 * ternary.BLOCK_BYTES - sb) * 28 == 8 * ternary.BLOCK_BYTES
+
+
+def test_trit_positions_match_post():
+    g = load_golden("ptq1_0_layout.txt")
+    for digit, e in enumerate(_ints(g["qs_byte0_elements"])):
+        assert ternary.trit_position(e) == ("qs", 0, digit)
+    for digit, e in enumerate(_ints(g["qs_byte16_elements"])):
+        assert ternary.trit_position(e) == ("qs", 16, digit)
+    # every (byte, slot) is used exactly once
+    slots = {ternary.trit_position(e) for e in range(128)}
+    assert len(slots) == 128
+
+
+def test_digit_placement_by_value():
+    # trit +1 (digit 2) at element 32 only, 0 (digit 1) elsewhere: byte 0 is
+    # 1 + 3 + 2*9 + 27 + 81 = 130; every other qs byte is 121; qh bytes 0x55
+    t = np.zeros((1, 128), np.int8)
+    t[0, 32] = 1
+    b = ternary.encode_ptq1_0(t, np.array([[0x3C00]], np.uint16))[0, 0]
+    assert b[0] == 130 and all(v == 121 for v in b[1:24])
+    assert b[24] == 0x55 and b[25] == 0x55 and b[26] == 0x00 and b[27] == 0x3C
+    # the tail: element 121 -> qh[1] bits 0..1; element 126 -> qh[0] bits 6..7
+    t = np.full((1, 128), -1, np.int8)
+    t[0, 121] = 1
+    t[0, 126] = 0
+    b = ternary.encode_ptq1_0(t, np.zeros((1, 1), np.uint16))[0, 0]
+    assert b[24] == 0x40 and b[25] == 0x02 and all(v == 0 for v in b[:24])
+
+
+def test_ptq1_0_round_trip_exhaustive_bytes():
+    # every byte value 0..242 decodes to five digits and re-encodes to itself
+    blocks = np.zeros((1, 243, 28), np.uint8)
+    for v in range(243):
+        blocks[0, v, :24] = v
+        blocks[0, v, 24:26] = 0x55
+    t, d = ternary.decode_ptq1_0(blocks)
+    assert np.array_equal(ternary.encode_ptq1_0(t, d), blocks)
+    for v in range(243):
+        digits = [(v // 3 ** j) % 3 for j in range(5)]
+        assert sum(u * 3 ** j for j, u in enumerate(digits)) == v
+        assert int(t[0, 128 * v + 0]) + 1 == digits[0]
+        assert int(t[0, 128 * v + 64]) + 1 == digits[4]
+
+
+def test_ptq1_0_round_trip_random():
+    p = wq_inputs.ternary_gemv(k=512, n=9, cmax=1)
+    blk = ternary.encode_ptq1_0(p.trits, p.d_bits)
+    t, d = ternary.decode_ptq1_0(blk)
+    assert np.array_equal(t, p.trits) and np.array_equal(d, p.d_bits)
+    assert blk[:, :, :24].max() <= 242
+
+
+def test_q8_1_closed_forms():
+    # integer x with amax 127: d = 1 exactly, q = x, s = sum(x)
+    x = np.zeros((2, 64), np.float32)
+    x[0, :32] = np.arange(-16, 16)
+    x[0, 5] = 127
+    x[0, 32:] = 0                       # an all-zero block: d = 0, q = 0
+    x[1, :32] = np.arange(32) * 2.0 - 31.0
+    x[1, 0] = -63.5                     # amax 63.5 -> d = 0.5, q = 2x
+    x[1, 32:] = 127.0
+    blk = ternary.quantize_q8_1(x)
+    q, d, s = ternary.decode_q8_1(blk)
+    assert d[0, 0] == 0x3C00 and np.array_equal(q[0, :32], x[0, :32].astype(np.int8))
+    assert fpformat.f16_bits_to_f32(s[0, :1])[0] == x[0, :32].sum()
+    assert d[0, 1] == 0 and s[0, 1] == 0 and np.all(q[0, 32:] == 0)
+    assert d[1, 0] == 0x3800 and np.array_equal(q[1, :32], (2 * x[1, :32]).astype(np.int8))
+    assert np.all(q[1, 32:] == 127) and d[1, 1] == 0x3C00
+
+
+def test_q8_1_ties_and_bounds():
+    # d = 1: ties 0.5 1.5 2.5 -0.5 -1.5 round to even
+    x = np.zeros((1, 32), np.float32)
+    x[0, :6] = [127, 0.5, 1.5, 2.5, -0.5, -1.5]
+    q, _, _ = ternary.decode_q8_1(ternary.quantize_q8_1(x))
+    assert list(q[0, :6]) == [127, 0, 2, 2, 0, -2]
+    rng = np.random.default_rng(3)
+    xr = rng.standard_normal((4, 1024)).astype(np.float32)
+    q, d, _ = ternary.decode_q8_1(ternary.quantize_q8_1(xr))
+    dd = np.repeat(fpformat.f16_bits_to_f32(d), 32, axis=1)
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    assert np.all(np.abs(xr - q * dd) <= dd / 2 * (1 + 1e-3))
+
+
+def test_ternary_unit_scale_exact():
+    p = wq_inputs.ternary_gemv(k=512, n=20, cmax=3, unit_scale=True)
+    wb = ternary.encode_ptq1_0(p.trits, p.d_bits)
+    xb = ternary.quantize_q8_1(p.x)
+    q, d, _ = ternary.decode_q8_1(xb)
+    assert np.all(d == 0x3C00) and np.array_equal(q, p.x.astype(np.int8))
+    y = ternary.gemv_ternary(wb, xb)
+    exact = p.x.astype(np.int64) @ p.trits.astype(np.int64).T
+    assert np.array_equal(y, exact.astype(np.float64))
+
+
+def test_ternary_special_cases():
+    rng = np.random.default_rng(11)
+    k, n = 256, 4
+    x = rng.standard_normal((2, k)).astype(np.float32)
+    xb = ternary.quantize_q8_1(x)
+    q, dbits, _ = ternary.decode_q8_1(xb)
+    dx = np.repeat(fpformat.f16_bits_to_f32(dbits).astype(np.float64), 32, axis=1)
+    dw = rng.uniform(0.01, 0.05, (n, k // 128)).astype(np.float32)
+    dwb = fpformat.f32_to_f16_bits(dw)
+    dwf = fpformat.f16_bits_to_f32(dwb).astype(np.float64)
+    # all trits zero -> 0
+    y = ternary.gemv_ternary(ternary.encode_ptq1_0(np.zeros((n, k), np.int8), dwb), xb)
+    assert np.all(y == 0)
+    # all trits +1 -> sum over blocks of d_w * d_x * q
+    y = ternary.gemv_ternary(ternary.encode_ptq1_0(np.ones((n, k), np.int8), dwb), xb)
+    ref = np.einsum("ck,rk->cr", dx * q, np.repeat(dwf, 128, axis=1))
+    np.testing.assert_allclose(y, ref, rtol=1e-12)
+    # one nonzero trit picks out one product
+    t = np.zeros((n, k), np.int8)
+    t[2, 77] = -1
+    y = ternary.gemv_ternary(ternary.encode_ptq1_0(t, dwb), xb)
+    for c in range(2):
+        assert y[c, 2] == -dwf[2, 0] * dx[c, 77] * q[c, 77]
+        assert np.all(np.delete(y[c], 2) == 0)
