@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Throughput of the weight-quantised GEMV/GEMM path on one MI355X.
+
+Headline (the JSON `value`): weight GB/s of the decode-shape W4A16 GEMV --
+both projections of one layer, K=5120,N=17280 and K=17280,N=5120, int4 codes
+with bf16 group-128 scales and zero 8, bf16 x, bf16 out -- over a batch of
+c = 1, 2 and 4 activation columns.  One step is those six GEMV calls.  Each
+call reads a different copy of the weights from a rotating set larger than
+the 256 MB Infinity Cache, so every weight byte comes from HBM.
+
+The same run also times the other rows of the path (quantise + pack, the
+small-batch GEMV, the 8192^3 W4A16 GEMM, the ternary GEMV) and reports them
+under "rows"; and, on rank 0, times the CPU oracle on a bounded sample
+("cpu_baseline").
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4 GEMV weight GB/s (% of HBM peak); W4A16 GEMM TFLOP/s (% of MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def sha_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_src):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "gemv_w4_decode_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_val or m_sha.group(1) != sha_of(kernel_src):
+        return None
+    return float(m_val.group(1))
+
+
+class Timer:
+    """Per-launch HIP event pairs on the launching (current) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.s = self.torch.cuda.Event(enable_timing=True)
+        self.e = self.torch.cuda.Event(enable_timing=True)
+        self.s.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.e.record()
+        self.pairs.append((self.s, self.e))
+
+    def ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def copies_for(nbytes, minimum=2):
+    return max(minimum, int((MALL_BYTES * 1.25) // max(nbytes, 1)) + 1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the secondary rows")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="also run one plain device copy of this size (PMC scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by output rows with no collective, see the design notes",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_wq_quantize_amd as g
+    import wq_inputs
+
+    if not os.path.exists(g.LIB_PATH):
+        from gemm_wq_quantize_amd import build as b
+        b.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("device", torch.cuda.get_device_name(dev))
+
+    # ------------------------------------------------------------ decode GEMV
+    shapes = wq_inputs.DECODE_SHAPES
+    batches = (1, 2, 4)
+    sets = []
+    for (k, n) in shapes:
+        p = wq_inputs.decode_int4(k, n, cmax=4)
+        pk = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        g.wq_pack_int4(torch.from_numpy(p.codes).to(dev), g.LAYOUT_GFX950, pk)
+        sc = torch.from_numpy(p.scale_bits).view(torch.bfloat16).to(dev)
+        wbytes = pk.numel() + sc.numel() * 2
+        ncopy = copies_for(wbytes)
+        copies = [(pk, sc)] + [(pk.clone(), sc.clone()) for _ in range(ncopy - 1)]
+        x = torch.from_numpy(p.x_bits).view(torch.bfloat16).to(dev)
+        out = torch.empty((4, n), dtype=torch.bfloat16, device=dev)
+        sets.append(dict(k=k, n=n, copies=copies, x=x, out=out, wbytes=wbytes))
+        log(f"decode K={k} N={n}: {wbytes / 1e6:.2f} MB of weights x {ncopy} copies")
+    torch.cuda.synchronize()
+
+    calls = [(si, c) for si in range(len(sets)) for c in batches]
+    rot = [0]
+
+    def step(timer=None):
+        for si, c in calls:
+            s = sets[si]
+            pk, sc = s["copies"][rot[0] % len(s["copies"])]
+            rot[0] += 1
+            xc = s["x"][:c]
+            if timer is None:
+                g.wq_gemv_w4(pk, 1, sc, None, 8.0, s["k"], 128, xc, s["out"][:c])
+            else:
+                with timer:
+                    g.wq_gemv_w4(pk, 1, sc, None, 8.0, s["k"], 128, xc, s["out"][:c])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # region timing: no per-launch events inside, so nothing but the kernels
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    region_ms = t_start.elapsed_time(t_end)
+    ms_per_step = region_ms / args.steps
+    wbytes_step = sum(sets[si]["wbytes"] for si, _ in calls)
+    value = wbytes_step / (ms_per_step * 1e-3) / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall:.3f} s), "
+        f"{value:.1f} GB/s of weights")
+
+    # per-launch durations (separate pass with an event pair around each launch)
+    timer = Timer(torch)
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    durs = np.array(timer.ms()).reshape(args.steps, len(calls))
+    per_call = {}
+    alg_total, dur_total = 0.0, 0.0
+    for j, (si, c) in enumerate(calls):
+        s = sets[si]
+        alg = s["wbytes"] + 2 * s["k"] * c + 2 * s["n"] * c
+        d = float(np.mean(durs[:, j]))
+        alg_total += alg
+        dur_total += d
+        per_call[f"K{s['k']}_N{s['n']}_c{c}"] = {
+            "us": round(d * 1e3, 2), "weight_GBs": round(s["wbytes"] / (d * 1e-3) / 1e9, 1),
+            "alg_GBs": round(alg / (d * 1e-3) / 1e9, 1)}
+    n_launch = len(calls)
+    achieved = (alg_total / n_launch) / ((dur_total / n_launch) * 1e-3) / 1e9
+    traffic = read_traffic(os.path.join(ROOT, "gemm_wq_quantize_amd", "csrc", "gemv_w4.hip"))
+    log("per launch:", json.dumps(per_call))
+
+    rows = {"gemv_w4_decode": per_call}
+    if not args.no_rows:
+        rows.update(secondary_rows(g, torch, np, wq_inputs, dev, log))
+
+    if args.calibrate_copy_mb:
+        nb = args.calibrate_copy_mb << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {nb} bytes done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, wq_inputs, log)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4*bf16->f32",
+        "data": "synthetic (seeded wq_inputs: codes U{0..15}, bf16 scales U(0.002,0.02), bf16 x N(0,1))",
+        "config": {
+            "workload": "decode W4A16 GEMV, K=5120,N=17280 and K=17280,N=5120, group 128, "
+                        "zero 8, bf16 x and out, batch c in {1,2,4}; one step = the 6 calls",
+            "weight_bytes_per_step": wbytes_step,
+            "hbm_resident": "rotating weight copies > 256 MB Infinity Cache",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_gemv_w4",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": round(alg_total / n_launch),
+            "avg_launch_us": round(dur_total / n_launch * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def timed(torch, fn, iters):
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    fn(0)
+    torch.cuda.synchronize()
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters  # ms
+
+
+def secondary_rows(g, torch, np, wq_inputs, dev, log):
+    rows = {}
+    # quantise + pack and the small-batch GEMV (bf16 group-128 scales)
+    qrow, srow = {}, {}
+    for (k, n) in wq_inputs.SMALL_BATCH_SHAPES:
+        p = wq_inputs.small_batch_int4(k, n, cmax=32)
+        w = torch.from_numpy(p.w_f16).view(torch.float16).to(dev)
+        nc = copies_for(w.numel() * 2)
+        ws = [w] + [w.clone() for _ in range(nc - 1)]
+        pk = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((n, k // 128), dtype=torch.bfloat16, device=dev)
+        ms = timed(torch, lambda i: g.wq_quantize_pack_int4(ws[i % nc], 128, 1, pk, sc), 20)
+        qbytes = w.numel() * 2 + pk.numel() + sc.numel() * 2
+        qrow[f"K{k}_N{n}"] = {"us": round(ms * 1e3, 2), "GBs": round(qbytes / (ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(qbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        wb = pk.numel() + sc.numel() * 2
+        nc2 = copies_for(wb)
+        cps = [(pk, sc)] + [(pk.clone(), sc.clone()) for _ in range(nc2 - 1)]
+        x = torch.from_numpy(p.x_bits).view(torch.bfloat16).to(dev)
+        out = torch.empty((32, n), dtype=torch.bfloat16, device=dev)
+        for c in (8, 16, 32):
+            ms = timed(torch, lambda i: g.wq_gemv_w4(cps[i % nc2][0], 1, cps[i % nc2][1], None, 8.0,
+                                                      k, 128, x[:c], out[:c]), 50)
+            flops = 2.0 * n * k * c
+            srow[f"K{k}_N{n}_c{c}"] = {
+                "us": round(ms * 1e3, 2), "weight_GBs": round(wb / (ms * 1e-3) / 1e9, 1),
+                "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                "frac_valu_fp32": round(flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)}
+        del ws, cps
+        torch.cuda.empty_cache()
+    rows["quantize_pack_int4"] = qrow
+    rows["gemv_w4_small_batch"] = srow
+    log("quantise / small batch:", json.dumps(qrow), json.dumps(srow))
+
+    # 8192^3 W4A16 GEMM
+    q = wq_inputs.large_gemm(n_rows=1)
+    a = torch.from_numpy(q.a_bits).view(torch.bfloat16).to(dev)
+    b = torch.empty((q.n, q.k // 2), dtype=torch.uint8, device=dev)
+    g.wq_pack_int4(torch.from_numpy(q.codes).to(dev), 1, b)
+    sc = torch.from_numpy(q.scale_bits).view(torch.bfloat16).to(dev)
+    c = torch.empty((q.m, q.n), dtype=torch.bfloat16, device=dev)
+    ms = timed(torch, lambda i: g.wq_gemm_w4a16(a, b, 1, sc, q.k, 8.0, c), 10)
+    tf = 2.0 * q.m * q.n * q.k / (ms * 1e-3) / 1e12
+    rows["gemm_w4a16_8192"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                               "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)}
+    log("gemm 8192^3:", json.dumps(rows["gemm_w4a16_8192"]))
+    del a, b, c
+    torch.cuda.empty_cache()
+
+    # ternary GEMV, K=5120 N=17280
+    t = wq_inputs.ternary_gemv(5120, 17280, cmax=8)
+    wb = torch.empty((17280, 40, 28), dtype=torch.uint8, device=dev)
+    g.wq_pack_ptq1_0(torch.from_numpy(t.trits).to(dev),
+                     torch.from_numpy(t.d_bits).view(torch.int16).to(dev), wb)
+    nc = copies_for(wb.numel())
+    wcs = [wb] + [wb.clone() for _ in range(nc - 1)]
+    xq = torch.empty((8, 160, 36), dtype=torch.uint8, device=dev)
+    g.wq_quantize_q8_1(torch.from_numpy(t.x).to(dev), xq)
+    y = torch.empty((8, 17280), dtype=torch.float32, device=dev)
+    trow = {}
+    for cc in (1, 4, 8):
+        ms = timed(torch, lambda i: g.wq_gemv_ternary(wcs[i % nc], xq[:cc], 5120, y[:cc]), 50)
+        trow[f"K5120_N17280_c{cc}"] = {
+            "us": round(ms * 1e3, 2), "weight_GBs": round(wb.numel() / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(wb.numel() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    rows["gemv_ternary"] = trow
+    log("ternary:", json.dumps(trow))
+    return rows
+
+
+def cpu_baseline(np, wq_inputs, log):
+    """The oracle, untouched, on one step of the same workload (6 GEMVs)."""
+    from oracle import int4 as o4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    total_bytes, total_s = 0, 0.0
+    for (k, n) in wq_inputs.DECODE_SHAPES:
+        p = wq_inputs.decode_int4(k, n, cmax=4)
+        packed = o4.pack(p.codes, 1)
+        for c in (1, 2, 4):
+            t0 = time.perf_counter()
+            o4.gemv_w4(packed, 1, p.scales, None, 8.0, 128, p.x[:c])
+            total_s += time.perf_counter() - t0
+            total_bytes += packed.nbytes + p.scale_bits.nbytes
+    v = total_bytes / total_s / 1e9
+    log(f"cpu oracle: {total_s:.2f} s for one step, {v:.3f} GB/s, {threads} threads")
+    return {"value": round(v, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "one full step: the 6 decode GEMVs (both shapes, c = 1, 2, 4), "
+                      f"{total_s:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

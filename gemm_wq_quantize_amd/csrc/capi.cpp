@@ -1,0 +1,152 @@
+// C ABI of libwq: argument validation, then one launch on the caller's
+// stream.  Every check happens before any HIP call, so a rejected call
+// enqueues nothing and touches no output.
+#include "../../include/wq.h"
+#include "wq_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// group is k itself, or a power of two >= 32 dividing k
+bool valid_group(int64_t group, int64_t k) {
+  if (group == k) return true;
+  return is_pow2(group) && group >= 32 && group <= k && k % group == 0;
+}
+
+int dtype_size(int dt) { return dt == WQ_F32 ? 4 : 2; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_EHIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int wq_abi_version(void) { return 1; }
+
+const char* wq_status_string(int status) {
+  switch (status) {
+    case WQ_OK: return "WQ_OK";
+    case WQ_EINVAL: return "WQ_EINVAL: null pointer, bad enum or negative size";
+    case WQ_EALIGN: return "WQ_EALIGN: pointer misaligned for this call";
+    case WQ_ESHAPE: return "WQ_ESHAPE: sizes violate this call's divisibility or limits";
+    case WQ_EUNSUPPORTED: return "WQ_EUNSUPPORTED: request not implemented by this build";
+    case WQ_EHIP: return "WQ_EHIP: HIP runtime error at launch";
+    default: return "unknown wq_status";
+  }
+}
+
+int wq_pack_int4(const uint8_t* codes, int64_t n, int64_t k, int layout, uint8_t* packed,
+                 void* stream) {
+  if (n < 0 || k < 0 || (layout != WQ_LAYOUT_PLAIN && layout != WQ_LAYOUT_GFX950)) return WQ_EINVAL;
+  if (n == 0 || k == 0) return WQ_OK;
+  if (!codes || !packed) return WQ_EINVAL;
+  if (k % 8 != 0) return WQ_ESHAPE;
+  if (!aligned(codes, 4) || !aligned(packed, 4)) return WQ_EALIGN;
+  if (n * k / 8 / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  return hip_status(wq::launch_pack_int4(codes, n, k, layout, packed, as_stream(stream)));
+}
+
+int wq_quantize_pack_int4(const uint16_t* w, int64_t n, int64_t k, int64_t group, int layout,
+                          uint8_t* packed, void* scales, int scale_dtype, void* stream) {
+  if (n < 0 || k < 0 || group < 0) return WQ_EINVAL;
+  if (layout != WQ_LAYOUT_PLAIN && layout != WQ_LAYOUT_GFX950) return WQ_EINVAL;
+  if (scale_dtype != WQ_F32 && scale_dtype != WQ_BF16) return WQ_EINVAL;
+  if (n == 0 || k == 0) return WQ_OK;
+  if (!w || !packed || !scales) return WQ_EINVAL;
+  if (k % 32 != 0 || !valid_group(group, k)) return WQ_ESHAPE;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, dtype_size(scale_dtype)))
+    return WQ_EALIGN;
+  if (n * (k / group) * 64 / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  return hip_status(wq::launch_quantize_pack_int4(w, n, k, group, layout, packed, scales,
+                                                  scale_dtype == WQ_BF16, as_stream(stream)));
+}
+
+int wq_gemv_w4(const uint8_t* packed, int layout, const void* scales, int scale_dtype,
+               const void* zeros, float zero_const, int64_t n, int64_t k, int64_t group,
+               const void* x, int x_dtype, int64_t c, void* out, int out_dtype, void* stream) {
+  if (n < 0 || k < 0 || c < 0 || group < 0) return WQ_EINVAL;
+  if (layout != WQ_LAYOUT_PLAIN && layout != WQ_LAYOUT_GFX950) return WQ_EINVAL;
+  if (scale_dtype != WQ_F32 && scale_dtype != WQ_BF16) return WQ_EINVAL;
+  if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
+  if (out_dtype != WQ_F32 && out_dtype != WQ_BF16) return WQ_EINVAL;
+  if (n == 0 || c == 0) return WQ_OK;
+  if (!packed || !scales || !x || !out) return WQ_EINVAL;
+  if (k == 0 || k % 32 != 0 || !valid_group(group, k) || c > 32) return WQ_ESHAPE;
+  if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(scales, dtype_size(scale_dtype)) ||
+      (zeros && !aligned(zeros, dtype_size(scale_dtype))) || !aligned(out, dtype_size(out_dtype)))
+    return WQ_EALIGN;
+  if (n / 8 + 1 > kMaxGrid) return WQ_ESHAPE;
+  wq::GemvArgs a;
+  a.packed = packed;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.x = x;
+  a.out = out;
+  a.n = n;
+  a.k = k;
+  a.group = group;
+  a.c = c;
+  a.zero_const = zero_const;
+  a.layout = layout;
+  a.scale_bf16 = scale_dtype == WQ_BF16;
+  a.x_bf16 = x_dtype == WQ_BF16;
+  a.out_bf16 = out_dtype == WQ_BF16;
+  return hip_status(wq::launch_gemv_w4(a, as_stream(stream)));
+}
+
+int wq_gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* scales,
+                  int64_t group, float zero_const, int64_t m, int64_t n, int64_t k,
+                  uint16_t* c_out, void* stream) {
+  if (m < 0 || n < 0 || k < 0 || group < 0) return WQ_EINVAL;
+  if (layout != WQ_LAYOUT_PLAIN && layout != WQ_LAYOUT_GFX950) return WQ_EINVAL;
+  if (m == 0 || n == 0) return WQ_OK;
+  if (!a || !b || !scales || !c_out) return WQ_EINVAL;
+  if (k == 0 || k % 64 != 0) return WQ_ESHAPE;
+  if (layout != WQ_LAYOUT_GFX950 || group != k) return WQ_EUNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c_out, 16) || !aligned(scales, 2))
+    return WQ_EALIGN;
+  if (((m + 255) / 256) * ((n + 255) / 256) > kMaxGrid) return WQ_ESHAPE;
+  return hip_status(wq::launch_gemm_w4a16(a, b, scales, zero_const, m, n, k, c_out,
+                                          as_stream(stream)));
+}
+
+int wq_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k, uint8_t* blocks,
+                   void* stream) {
+  if (n < 0 || k < 0) return WQ_EINVAL;
+  if (n == 0 || k == 0) return WQ_OK;
+  if (!trits || !d || !blocks) return WQ_EINVAL;
+  if (k % 128 != 0) return WQ_ESHAPE;
+  if (!aligned(trits, 16) || !aligned(d, 2) || !aligned(blocks, 4)) return WQ_EALIGN;
+  if (n * (k / 128) / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  return hip_status(wq::launch_pack_ptq1_0(trits, d, n, k, blocks, as_stream(stream)));
+}
+
+int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* stream) {
+  if (c < 0 || k < 0) return WQ_EINVAL;
+  if (c == 0 || k == 0) return WQ_OK;
+  if (!x || !x_q8) return WQ_EINVAL;
+  if (k % 32 != 0) return WQ_ESHAPE;
+  if (!aligned(x, 16) || !aligned(x_q8, 4)) return WQ_EALIGN;
+  if (c * k / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  return hip_status(wq::launch_quantize_q8_1(x, c, k, x_q8, as_stream(stream)));
+}
+
+int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k, int64_t c,
+                    float* out, void* stream) {
+  if (n < 0 || k < 0 || c < 0) return WQ_EINVAL;
+  if (n == 0 || c == 0) return WQ_OK;
+  if (!w_blocks || !x_q8 || !out) return WQ_EINVAL;
+  if (k == 0 || k % 128 != 0 || c > 16) return WQ_ESHAPE;
+  if (!aligned(w_blocks, 4) || !aligned(x_q8, 4) || !aligned(out, 4)) return WQ_EALIGN;
+  if (n / 32 + 1 > kMaxGrid) return WQ_ESHAPE;
+  return hip_status(wq::launch_gemv_ternary(w_blocks, x_q8, n, k, c, out, as_stream(stream)));
+}
+
+}  // extern "C"

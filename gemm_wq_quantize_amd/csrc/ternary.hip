@@ -1,0 +1,285 @@
+// Ternary path (gfx950): PTQ1_0 block packing, the q8_1 activation
+// quantiser and the ternary x int8 GEMV.
+//
+// Formats: Ternary post, section 2 (struct ptq1_0: qs[24] with 120 trits,
+// qh[2] with 8 trits, fp16 d), section 3.1 (block_q8_1: fp16 d, fp16 s,
+// int8 qs[32]) and section 3.2 (trit placement: element e < 80 is digit
+// e >> 4 of byte e & 15; element 80 + e is digit e >> 3 of byte 16 + (e & 7);
+// the last 8 are 2-bit fields of qh).  A trit t is stored as the digit
+// u = t + 1, a qs byte is sum_j u_j 3^j (digit 0 least significant), and
+// tail element 120 + e sits in qh[e & 1] at bits 2 * (e >> 1).
+//
+// GEMV: y[j][r] = sum_b d_w[r][b/4] * d_x[j][b] * S[r][j][b] with exact int32
+// sub-block sums S = sum_{i<32} t * q = sum u * q - sum q (v_dot4 on digits),
+// the per-block sums of q taken from the int8 data, never from the fp16 s.
+#include "wq_internal.h"
+
+namespace wq {
+namespace {
+
+constexpr int PT_BYTES = 28;
+constexpr int Q8_BYTES = 36;
+
+// ---------------------------------------------------------------- packing
+__global__ __launch_bounds__(256) void k_pack_ptq1_0(const int8_t* __restrict__ trits,
+                                                     const uint16_t* __restrict__ d,
+                                                     uint32_t* __restrict__ blocks,
+                                                     int64_t nblocks) {
+  int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint4* src = reinterpret_cast<const uint4*>(trits + b * 128);
+  uint32_t u[128];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint4 v = src[i];
+    uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[16 * i + 4 * q + e] = (uint32_t)((int)(int8_t)(w4[q] >> (8 * e)) + 1);
+  }
+  uint32_t bytes[26];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)  // byte i: elements i + 16 j
+    bytes[i] = u[i] + 3 * u[i + 16] + 9 * u[i + 32] + 27 * u[i + 48] + 81 * u[i + 64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)  // byte 16 + i: elements 80 + i + 8 j
+    bytes[16 + i] = u[80 + i] + 3 * u[88 + i] + 9 * u[96 + i] + 27 * u[104 + i] + 81 * u[112 + i];
+  bytes[24] = u[120] | u[122] << 2 | u[124] << 4 | u[126] << 6;
+  bytes[25] = u[121] | u[123] << 2 | u[125] << 4 | u[127] << 6;
+  uint32_t* dst = blocks + b * 7;
+#pragma unroll
+  for (int i = 0; i < 6; ++i)
+    dst[i] = bytes[4 * i] | bytes[4 * i + 1] << 8 | bytes[4 * i + 2] << 16 | bytes[4 * i + 3] << 24;
+  dst[6] = bytes[24] | bytes[25] << 8 | (uint32_t)d[b] << 16;
+}
+
+// ---------------------------------------------------------------- q8_1
+// One 32-lane team per block of 32 activations.
+__global__ __launch_bounds__(256) void k_quantize_q8_1(const float* __restrict__ x,
+                                                       uint8_t* __restrict__ out,
+                                                       int64_t nblocks) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = gid >> 5;
+  const int lane = threadIdx.x & 31;
+  const bool active = b < nblocks;
+  const float v = active ? x[gid] : 0.f;
+  float amax = fabsf(v);
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const uint32_t dbits = f32_to_f16_rne(amax / 127.0f);  // IEEE divide, RNE to fp16
+  const float dv = f16_to_f32(dbits);
+  int q = 0;
+  if (dv != 0.f) {
+    float r = rintf(v / dv);
+    r = fminf(fmaxf(r, -127.f), 127.f);
+    q = (int)r;
+  }
+  int qs = q;
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) qs += __shfl_xor(qs, off);
+  if (!active) return;
+  uint8_t* blk = out + b * Q8_BYTES;
+  blk[4 + lane] = (uint8_t)(int8_t)q;
+  if (lane == 0) {
+    const uint32_t sbits = f32_to_f16_rne(dv * (float)qs);
+    *reinterpret_cast<uint32_t*>(blk) = dbits | sbits << 16;
+  }
+}
+
+// ---------------------------------------------------------------- GEMV
+// Lane layout: a wave covers 8 rows x 8 consecutive blocks (1024 k) per
+// tile; a 256-lane workgroup covers 32 rows.  The activation tile (int8 q in
+// k order, plus per-32 d and sum q) is staged in LDS once per workgroup.
+//
+// Digit decode: a 243-entry LDS table maps a qs byte to its digits u0..u3 in
+// bytes 0..3 and u4 in bits 4-5 of byte 0.  Four table words (four
+// consecutive qs bytes b..b+3, one digit position j each = elements
+// 16j + b .. 16j + b + 3) are transposed with v_perm so each dword holds one
+// digit position of four neighbouring bytes -- exactly four consecutive
+// elements, which v_dot4 multiplies with four consecutive int8 activations.
+constexpr int T_BLOCKS = 8;              // blocks per lane-row per tile
+constexpr int T_K = T_BLOCKS * 128;      // 1024 k per tile
+constexpr int T_SUB = T_K / 32;          // 32 activation blocks per tile
+
+__device__ __forceinline__ void transpose4(uint32_t l0, uint32_t l1, uint32_t l2, uint32_t l3,
+                                           uint32_t& d0, uint32_t& d1, uint32_t& d2,
+                                           uint32_t& d3, uint32_t& d4) {
+  // perm(hi, lo, sel): selector bytes 0-3 pick lo's bytes, 4-7 pick hi's
+  const uint32_t a = __builtin_amdgcn_perm(l1, l0, 0x05010400u);  // l0b0 l1b0 l0b1 l1b1
+  const uint32_t b = __builtin_amdgcn_perm(l3, l2, 0x05010400u);  // l2b0 l3b0 l2b1 l3b1
+  const uint32_t c = __builtin_amdgcn_perm(l1, l0, 0x07030602u);  // l0b2 l1b2 l0b3 l1b3
+  const uint32_t e = __builtin_amdgcn_perm(l3, l2, 0x07030602u);  // l2b2 l3b2 l2b3 l3b3
+  const uint32_t r0 = __builtin_amdgcn_perm(b, a, 0x05040100u);   // byte0 of l0..l3
+  d0 = r0 & 0x03030303u;
+  d4 = (r0 >> 4) & 0x03030303u;
+  d1 = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  d2 = __builtin_amdgcn_perm(e, c, 0x05040100u);
+  d3 = __builtin_amdgcn_perm(e, c, 0x07060302u);
+}
+
+template <int C>
+__global__ __launch_bounds__(256) void k_gemv_ternary(const uint32_t* __restrict__ w,
+                                                      const uint8_t* __restrict__ xq,
+                                                      float* __restrict__ out, int64_t n,
+                                                      int64_t k, int c) {
+  __shared__ uint32_t lut[256];
+  __shared__ uint4 xs[C * T_K / 16];      // int8 q, k order, per column
+  __shared__ int xsum[C * T_SUB];         // sum of q per activation block
+  __shared__ float xd[C * T_SUB];         // d per activation block
+
+  const int tid = threadIdx.x;
+  {
+    uint32_t v = tid, ent = 0;
+    uint32_t u0 = v % 3, u1 = (v / 3) % 3, u2 = (v / 9) % 3, u3 = (v / 27) % 3, u4 = (v / 81) % 3;
+    ent = u0 | u1 << 8 | u2 << 16 | u3 << 24 | u4 << 4;
+    lut[tid] = ent;  // entries >= 243 are never indexed by valid data
+  }
+
+  const int lane = tid & 63;
+  const int sub = lane & 7;                 // block within the tile
+  const int64_t row0 = (int64_t)blockIdx.x * 32 + (tid >> 6) * 8 + (lane >> 3);
+  const int64_t row = min(row0, n - 1);
+  const int64_t bpr = k / 128;              // blocks per row
+  const int ntiles = (int)((bpr + T_BLOCKS - 1) / T_BLOCKS);
+
+  float acc[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) acc[j] = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t blk = (int64_t)t * T_BLOCKS + sub;
+    const bool valid = blk < bpr;
+    uint32_t wd[7];
+    const uint32_t* src = w + (row * bpr + (valid ? blk : 0)) * 7;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) wd[i] = src[i];
+
+    __syncthreads();
+    // stage: C columns x 32 activation blocks; one lane per (column, block)
+    for (int idx = tid; idx < C * T_SUB; idx += 256) {
+      const int col = idx / T_SUB, sb = idx % T_SUB;
+      const int64_t gsb = (int64_t)t * T_SUB + sb;  // activation block index in the row
+      uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      uint32_t hd = 0;
+      if (col < c && gsb < k / 32) {
+        const uint32_t* s = reinterpret_cast<const uint32_t*>(xq + ((int64_t)col * (k / 32) + gsb) * Q8_BYTES);
+        hd = s[0];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = s[1 + i];
+      }
+      uint4* dst = &xs[(col * T_K + sb * 32) / 16];
+      dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+      dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+      int sum = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum = __builtin_amdgcn_sdot4((int)q[i], 0x01010101, sum, false);
+      xsum[col * T_SUB + sb] = sum;
+      xd[col * T_SUB + sb] = f16_to_f32(hd & 0xFFFFu);
+    }
+    __syncthreads();
+
+    if (valid) {
+      // decode the 128 digits into 32 dwords in k order (dw[i] = elements 4i..4i+3)
+      uint32_t dg[32];
+      // section 1: qs bytes 0..15, element 16 j + b
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t v = wd[g];
+        const uint32_t l0 = lut[v & 0xFF], l1 = lut[(v >> 8) & 0xFF];
+        const uint32_t l2 = lut[(v >> 16) & 0xFF], l3 = lut[v >> 24];
+        uint32_t d0, d1, d2, d3, d4;
+        transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
+        dg[g] = d0; dg[4 + g] = d1; dg[8 + g] = d2; dg[12 + g] = d3; dg[16 + g] = d4;
+      }
+      // section 2: qs bytes 16..23, element 80 + 8 j + b
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t v = wd[4 + g];
+        const uint32_t l0 = lut[v & 0xFF], l1 = lut[(v >> 8) & 0xFF];
+        const uint32_t l2 = lut[(v >> 16) & 0xFF], l3 = lut[v >> 24];
+        uint32_t d0, d1, d2, d3, d4;
+        transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
+        dg[20 + g] = d0; dg[22 + g] = d1; dg[24 + g] = d2; dg[26 + g] = d3; dg[28 + g] = d4;
+      }
+      // qh: elements 120..127; h bits 2e' of byte (e' & 1) -> digit of 120 + e'
+      {
+        const uint32_t h = wd[6] & 0xFFFFu;
+        dg[30] = (h | (h << 14)) & 0x03030303u;
+        dg[31] = ((h >> 4) | (h << 10)) & 0x03030303u;
+      }
+      const float dw = f16_to_f32(wd[6] >> 16);
+#pragma unroll
+      for (int col = 0; col < C; ++col) {
+        const uint4* xv = &xs[(col * T_K + sub * 128) / 16];
+        float part = 0.f;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {  // activation block within the 128
+          const uint4 x0 = xv[2 * s4], x1 = xv[2 * s4 + 1];
+          int sacc = -xsum[col * T_SUB + sub * 4 + s4];
+          sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 0], (int)x0.x, sacc, false);
+          sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 1], (int)x0.y, sacc, false);
+          sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 2], (int)x0.z, sacc, false);
+          sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 3], (int)x0.w, sacc, false);
+          sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 4], (int)x1.x, sacc, false);
+          sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 5], (int)x1.y, sacc, false);
+          sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 6], (int)x1.z, sacc, false);
+          sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 7], (int)x1.w, sacc, false);
+          part = fmaf(xd[col * T_SUB + sub * 4 + s4], (float)sacc, part);
+        }
+        acc[col] = fmaf(dw, part, acc[col]);
+      }
+    }
+  }
+  // sum the 8 lanes of each row (fixed order)
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    float v = acc[j];
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    acc[j] = v;
+  }
+  if (sub == 0 && row0 < n) {
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      if (j < c) out[j * n + row0] = acc[j];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
+                              uint8_t* blocks, hipStream_t s) {
+  const int64_t nb = n * (k / 128);
+  hipLaunchKernelGGL(k_pack_ptq1_0, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, trits, d,
+                     reinterpret_cast<uint32_t*>(blocks), nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* xq, hipStream_t s) {
+  const int64_t nb = c * (k / 32);
+  hipLaunchKernelGGL(k_quantize_q8_1, dim3((unsigned)((nb * 32 + 255) / 256)), dim3(256), 0, s, x,
+                     xq, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
+                               int64_t c, float* out, hipStream_t s) {
+  const unsigned blocks = (unsigned)((n + 31) / 32);
+  const uint32_t* wp = reinterpret_cast<const uint32_t*>(w);
+#define WQ_TG(C) hipLaunchKernelGGL(k_gemv_ternary<C>, dim3(blocks), dim3(256), 0, s, wp, xq, out, n, k, (int)c)
+  switch (c) {
+    case 1: WQ_TG(1); break;
+    case 2: WQ_TG(2); break;
+    case 3: WQ_TG(3); break;
+    case 4: WQ_TG(4); break;
+    default:
+      if (c <= 8) { WQ_TG(8); } else { WQ_TG(16); }
+      break;
+  }
+#undef WQ_TG
+  return hipGetLastError();
+}
+
+}  // namespace wq

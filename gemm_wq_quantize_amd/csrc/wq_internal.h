@@ -1,0 +1,65 @@
+// Internal helpers and launcher declarations of libwq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// float32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// float32 -> fp16 bit pattern, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Launchers: validated arguments only.  Each returns hipSuccess or the
+// launch error.
+hipError_t launch_pack_int4(const uint8_t* codes, int64_t n, int64_t k, int layout,
+                            uint8_t* packed, hipStream_t s);
+hipError_t launch_quantize_pack_int4(const uint16_t* w, int64_t n, int64_t k, int64_t group,
+                                     int layout, uint8_t* packed, void* scales, bool scale_bf16,
+                                     hipStream_t s);
+
+struct GemvArgs {
+  const uint8_t* packed;
+  const void* scales;
+  const void* zeros;
+  const void* x;
+  void* out;
+  int64_t n, k, group, c;
+  float zero_const;
+  int layout;
+  bool scale_bf16, x_bf16, out_bf16;
+};
+hipError_t launch_gemv_w4(const GemvArgs& a, hipStream_t s);
+
+hipError_t launch_gemm_w4a16(const uint16_t* a, const uint8_t* b, const uint16_t* scales,
+                             float zero_const, int64_t m, int64_t n, int64_t k, uint16_t* c,
+                             hipStream_t s);
+
+hipError_t launch_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
+                              uint8_t* blocks, hipStream_t s);
+hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* xq,
+                                hipStream_t s);
+hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
+                               int64_t c, float* out, hipStream_t s);
+
+}  // namespace wq

@@ -1,0 +1,189 @@
+/*
+ * wq.h -- C ABI of libwq: weight-quantised GEMV / GEMM for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Pages cited (titles; section names in brackets):
+ *   Paddle PR    "[PHI] add int4 weight only quant kernel, add int4 weight
+ *                only permute kernel" (PaddlePaddle/Paddle #64091)
+ *   Vulkan post  "怎样在安卓端利用 Vulkan 编写 4-bit 专用算子：直接在 GPU 上
+ *                进行解量化与计算融合"
+ *   Helion issue "int4 gemm kernel" (pytorch/helion #508)
+ *   Ternary post "三值量化模型的无损压缩"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array argument is a caller-owned DEVICE pointer (HIP global
+ *    memory) unless stated otherwise.  The library keeps no pointer after
+ *    the call returns and never frees or allocates caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    All work is enqueued asynchronously on it; no call synchronises.
+ *  - Return value: WQ_OK (0) or a negative wq_status.  Argument errors are
+ *    detected BEFORE anything is enqueued; then nothing runs and the output
+ *    buffers are untouched.  A launch failure returns WQ_EHIP.  Faults
+ *    during execution surface at the caller's next synchronisation.
+ *  - Empty problems (a zero n, c or m) return WQ_OK and enqueue nothing.
+ *  - Matrices are row-major and densely packed (no strides).
+ *  - Calls that write the same output concurrently on different streams
+ *    race; calls on one stream are ordered.
+ *
+ * int4 formats (Vulkan post [1 packing strategy]; Paddle PR ["int4量化
+ * kernel", "int4 permute kernel"]; Helion issue [matmul_bf16_int4])
+ * ----------------------------------------------------------------------
+ *  A weight matrix W has N output rows and K inputs; code q[n][k] in 0..15
+ *  stands for (q - zero) * scale.  Packed storage is [N][K/2] bytes, row n
+ *  contiguous along K.  Within row n, the little-endian 32-bit word m holds
+ *  the eight codes k = 8m .. 8m+7:
+ *    WQ_LAYOUT_PLAIN   nibble p (bits 4p..4p+3) holds k = 8m + p, i.e. byte
+ *                      i = q[2i] | q[2i+1] << 4 (low nibble = even k).
+ *    WQ_LAYOUT_GFX950  nibble p holds k = 8m + {0,2,4,6,1,3,5,7}[p], so that
+ *                      (word >> 4j) & 0x000F000F yields codes (2j, 2j+1) in
+ *                      the two 16-bit halves -- one OR makes two bf16.
+ *  Scales (and optional zeros) are [N][K/group] in the scale dtype; group is
+ *  a power of two >= 32 that divides K, or K itself (one scale per row).
+ *
+ * Ternary formats (Ternary post [2 weight compression], [3.1 data format],
+ * [3.2 dequantisation])
+ * ------------------------------------------------------------------------
+ *  PTQ1_0 block, 28 bytes per 128 trits: qs[24] (120 trits, five per byte),
+ *  qh[2] (8 trits, two bits each), fp16 d.  A trit t is stored as the digit
+ *  u = t + 1; a qs byte is sum_j u_j 3^j (digit 0 least significant).
+ *  Element e < 80: byte e & 15, digit e >> 4.  Element 80 + e (e < 40):
+ *  byte 16 + (e & 7), digit e >> 3.  Element 120 + e (e < 8): qh[e & 1],
+ *  bits 2*(e >> 1) .. +1.  Weights are [N][K/128] blocks, row-major.
+ *  block_q8_1, 36 bytes per 32 activations: fp16 d, fp16 s = d * sum(q),
+ *  int8 q[32].  Activations are [c][K/32] blocks.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WQ_OK = 0,
+  WQ_EINVAL = -1,       /* null pointer, bad enum, negative size            */
+  WQ_EALIGN = -2,       /* a pointer is not aligned as the call requires    */
+  WQ_ESHAPE = -3,       /* sizes violate the call's divisibility/limits     */
+  WQ_EUNSUPPORTED = -4, /* valid request this build does not implement      */
+  WQ_EHIP = -5          /* the HIP runtime reported an error at launch      */
+} wq_status;
+
+typedef enum { WQ_F32 = 0, WQ_F16 = 1, WQ_BF16 = 2 } wq_dtype;
+typedef enum { WQ_LAYOUT_PLAIN = 0, WQ_LAYOUT_GFX950 = 1 } wq_layout;
+
+/* Version of this ABI (bumped on any incompatible change). */
+int wq_abi_version(void);
+
+/* Human-readable name of a wq_status value (static storage, never NULL). */
+const char* wq_status_string(int status);
+
+/*
+ * wq_pack_int4 -- pack unsigned 4-bit codes into a packed layout.
+ *   codes  [n][k] uint8, one code (0..15) per byte; values >= 16 are
+ *          truncated to their low nibble.
+ *   packed [n][k/2] uint8 out, in `layout`.
+ * Requires k % 8 == 0, both pointers 4-byte aligned.
+ * Defines: Vulkan post [1 packing strategy]; Paddle PR ["int4 permute
+ * kernel"] for the gfx950 within-word order.
+ */
+int wq_pack_int4(const uint8_t* codes, int64_t n, int64_t k, int layout,
+                 uint8_t* packed, void* stream);
+
+/*
+ * wq_quantize_pack_int4 -- fp16 weights to int4 codes + scales, packed.
+ *   w      [n][k] fp16 (IEEE binary16 bit patterns).
+ *   group  128-style power of two >= 32 dividing k, or k (per row).
+ *   packed [n][k/2] uint8 out in `layout`.
+ *   scales [n][k/group] out, scale_dtype WQ_F32 or WQ_BF16.
+ * The zero point is 8.  Per row and group: scale = absmax / 7 (float32
+ * IEEE divide) rounded to the scale dtype (RNE); code = clamp(rint(w /
+ * scale), -8, 7) + 8 with a float32 IEEE divide by the STORED scale; an
+ * all-zero group stores scale 0 and codes 8.  (The pages give only the
+ * packing -- Paddle PR ["int4量化kernel"]; the formula is this library's
+ * reading.)  NaN/Inf weights are outside the contract.
+ * Requires k % 32 == 0; w and packed 16-byte aligned, scales 4-byte aligned.
+ */
+int wq_quantize_pack_int4(const uint16_t* w, int64_t n, int64_t k, int64_t group,
+                          int layout, uint8_t* packed, void* scales, int scale_dtype,
+                          void* stream);
+
+/*
+ * wq_gemv_w4 -- out[j][r] = sum_k (q[r][k] - z[r][g]) * s[r][g] * x[j][k],
+ * g = k / group, for j < c (Ternary post [3 MMVQ], the batched form with x
+ * indexed [c][k]; dequantisation as in the Vulkan post [2 GLSL shader]).
+ *   packed  [n][k/2] uint8 in `layout`.
+ *   scales  [n][k/group], scale_dtype WQ_F32 or WQ_BF16.
+ *   zeros   NULL (then every zero point is zero_const) or [n][k/group] in
+ *           the scale dtype.
+ *   x       [c][k], x_dtype WQ_F32 or WQ_BF16.
+ *   out     [c][n], out_dtype WQ_F32 or WQ_BF16 (RNE).
+ * Accumulates in float32; the result does not depend on the stream or on
+ * timing (bitwise repeatable).  Requires 1 <= c <= 32 (0 is a no-op),
+ * k % 32 == 0, packed and x 16-byte aligned, scales/zeros/out 4-byte aligned
+ * (out 2-byte for bf16).
+ */
+int wq_gemv_w4(const uint8_t* packed, int layout, const void* scales, int scale_dtype,
+               const void* zeros, float zero_const, int64_t n, int64_t k, int64_t group,
+               const void* x, int x_dtype, int64_t c, void* out, int out_dtype,
+               void* stream);
+
+/*
+ * wq_gemm_w4a16 -- C[i][j] = sum_k A[i][k] * (q[j][k] - zero_const) * s[j]
+ * (Helion issue [matmul_bf16_int4]; B is stored output-major [n][k/2], the
+ * transpose of the issue's (K/2, N) int8 view, with a per-column scale).
+ *   a       [m][k] bf16.
+ *   b       [n][k/2] uint8 in `layout` (WQ_LAYOUT_GFX950 only).
+ *   scales  [n] bf16 (group must equal k).
+ *   c_out   [m][n] bf16 (RNE of the float32 accumulator).
+ * Requires k % 64 == 0; a, b and c_out 16-byte aligned, scales 2-byte
+ * aligned.  Any m and n (ragged tiles are masked).  Every zero_const is
+ * exact for integer zero points (|q - z| <= 15 is a bf16 integer); other
+ * values are rounded to bf16 per weight.
+ */
+int wq_gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* scales,
+                  int64_t group, float zero_const, int64_t m, int64_t n, int64_t k,
+                  uint16_t* c_out, void* stream);
+
+/*
+ * wq_pack_ptq1_0 -- trits and block scales to PTQ1_0 blocks.
+ *   trits   [n][k] int8 in {-1, 0, 1} (other values: outside the contract).
+ *   d       [n][k/128] fp16 bit patterns.
+ *   blocks  [n][k/128][28] uint8 out.
+ * Requires k % 128 == 0, trits 16-byte aligned, blocks 4-byte aligned.
+ */
+int wq_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
+                   uint8_t* blocks, void* stream);
+
+/*
+ * wq_quantize_q8_1 -- float32 activations to block_q8_1 (Ternary post [3.1]).
+ *   x      [c][k] float32.
+ *   x_q8   [c][k/32][36] uint8 out.
+ * Per 32 values: d = fp16(amax / 127) (float32 divide, RNE);
+ * q = clamp(rint(x / float(d)), -127, 127) (float32 divide); s =
+ * fp16(float(d) * sum(q)); amax == 0 gives d = s = 0, q = 0.
+ * Requires k % 32 == 0, x 16-byte aligned, x_q8 4-byte aligned.
+ */
+int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* stream);
+
+/*
+ * wq_gemv_ternary -- out[j][r] = sum_b d_w[r][b/4] * d_x[j][b] * S[r][j][b]
+ * with the exact integer sums S = sum_{i<32} t * q over each activation
+ * block b (Ternary post [3 MMVQ], [3.1], [3.2]).  The stored s of the
+ * activation blocks is not used: the integer sum of q replaces it.
+ *   w_blocks  [n][k/128] PTQ1_0 blocks.
+ *   x_q8      [c][k/32] block_q8_1.
+ *   out       [c][n] float32.
+ * Requires 1 <= c <= 16 (0 is a no-op), k % 128 == 0, w_blocks and x_q8
+ * 4-byte aligned, out 4-byte aligned.
+ */
+int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k,
+                    int64_t c, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -76,13 +76,12 @@ def quantize_int4(w_f16_bits: np.ndarray, group: int, scale_dtype: str):
             raise ValueError(scale_dtype)
         scales[:, g] = s
         bits[:, g] = b
-        for r in range(n):
-            if s[r] == 0.0:
-                codes[r, g * group:(g + 1) * group] = 8
-                continue
-            quot = (blk[r] / s[r]).astype(np.float32)        # fp32 IEEE divide
-            q = np.clip(np.rint(quot), -8, 7).astype(np.int32) + 8
-            codes[r, g * group:(g + 1) * group] = q.astype(np.uint8)
+        zero = s == 0.0
+        safe = np.where(zero, np.float32(1.0), s)
+        quot = (blk / safe[:, None]).astype(np.float32)      # fp32 IEEE divide
+        q = np.clip(np.rint(quot), -8, 7).astype(np.int32) + 8
+        q[zero, :] = 8                                       # all-zero group
+        codes[:, g * group:(g + 1) * group] = q.astype(np.uint8)
     return codes, scales, bits
 
 

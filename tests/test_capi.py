@@ -1,0 +1,81 @@
+"""CPU checks of the C-ABI library: it builds, loads, exports every symbol
+that include/wq.h declares, and rejects bad arguments before any HIP call
+(so no GPU is needed: every call below fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gemm_wq_quantize_amd as g
+    if not os.path.exists(g.LIB_PATH):
+        from gemm_wq_quantize_amd import build
+        build.build()
+    return g.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "wq.h")).read()
+    return sorted(set(re.findall(r"^(?:const\s+)?\w+\**\s+\**(wq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("wq_pack_int4", "wq_quantize_pack_int4", "wq_gemv_w4", "wq_gemm_w4a16",
+                 "wq_pack_ptq1_0", "wq_quantize_q8_1", "wq_gemv_ternary", "wq_status_string",
+                 "wq_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    import gemm_wq_quantize_amd as g
+    assert g.wq_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert g.status_string(st).startswith("WQ_")
+    assert g.status_string(-99) == "unknown wq_status"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)      # never dereferenced: validation fails first
+ODD = P(0x1001)
+
+
+def test_validation_errors_without_gpu(lib):
+    import gemm_wq_quantize_amd as g
+    # empty problems are no-ops that succeed without touching pointers
+    assert lib.wq_gemv_w4(None, 1, None, 2, None, 8.0, 0, 128, 128, None, 2, 1, None, 2, None) == 0
+    assert lib.wq_gemv_ternary(None, None, 10, 128, 0, None, None) == 0
+    # null pointers / bad enums / negative sizes
+    assert lib.wq_pack_int4(None, 4, 8, 1, FAKE, None) == g.WQ_EINVAL
+    assert lib.wq_pack_int4(FAKE, 4, 8, 7, FAKE, None) == g.WQ_EINVAL
+    assert lib.wq_pack_int4(FAKE, -1, 8, 1, FAKE, None) == g.WQ_EINVAL
+    assert lib.wq_gemv_w4(FAKE, 1, FAKE, 5, None, 8.0, 4, 128, 128, FAKE, 2, 1, FAKE, 2, None) == g.WQ_EINVAL
+    # shapes
+    assert lib.wq_pack_int4(FAKE, 4, 12, 1, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_quantize_pack_int4(FAKE, 4, 256, 96, 1, FAKE, FAKE, 2, None) == g.WQ_ESHAPE
+    assert lib.wq_quantize_pack_int4(FAKE, 4, 48, 48, 1, FAKE, FAKE, 2, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_w4(FAKE, 1, FAKE, 2, None, 8.0, 4, 256, 128, FAKE, 2, 33, FAKE, 2, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_w4(FAKE, 1, FAKE, 2, None, 8.0, 4, 250, 250, FAKE, 2, 1, FAKE, 2, None) == g.WQ_ESHAPE
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 96, 8.0, 64, 64, 96, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 100, 1, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 128, 17, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_pack_ptq1_0(FAKE, FAKE, 2, 64, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_quantize_q8_1(FAKE, 2, 48, FAKE, None) == g.WQ_ESHAPE
+    # unsupported combinations
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 0, FAKE, 128, 8.0, 64, 64, 128, FAKE, None) == g.WQ_EUNSUPPORTED
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 128, 8.0, 64, 64, 256, FAKE, None) == g.WQ_EUNSUPPORTED
+    # alignment
+    assert lib.wq_gemv_w4(ODD, 1, FAKE, 2, None, 8.0, 4, 128, 128, FAKE, 2, 1, FAKE, 2, None) == g.WQ_EALIGN
+    assert lib.wq_quantize_pack_int4(FAKE, 4, 256, 128, 1, ODD, FAKE, 2, None) == g.WQ_EALIGN
+    assert lib.wq_gemm_w4a16(ODD, FAKE, 1, FAKE, 128, 8.0, 64, 64, 128, FAKE, None) == g.WQ_EALIGN
+    assert lib.wq_gemv_ternary(ODD, FAKE, 4, 128, 1, FAKE, None) == g.WQ_EALIGN

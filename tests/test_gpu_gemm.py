@@ -1,0 +1,91 @@
+"""GPU parity: the W4A16 MFMA GEMM against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import wq_inputs
+from oracle import fpformat, int4 as o4
+from tolerances import check_bf16_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def G():
+    import gemm_wq_quantize_amd as g
+    return g
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+
+def run(a_bits, codes, scale_bits, zc=8.0):
+    g = G()
+    m, k = a_bits.shape
+    n = codes.shape[0]
+    b = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda")
+    g.wq_pack_int4(torch.from_numpy(codes).cuda(), 1, b)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    g.wq_gemm_w4a16(bf16_dev(a_bits), b, 1, bf16_dev(scale_bits), k, zc, c)
+    torch.cuda.synchronize()
+    return c
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 520, 512), (256, 256, 64), (64, 8, 128), (1, 1000, 192),
+                                   (513, 257, 1088)])
+def test_gemm_ragged(m, n, k):
+    say("gemm", m, n, k)
+    p = wq_inputs.large_gemm(m, n, k, n_rows=m, seed=m + n)
+    c = run(p.a_bits, p.codes, p.scale_bits).float().cpu().numpy()
+    a = fpformat.bf16_bits_to_f32(p.a_bits)
+    s = fpformat.bf16_bits_to_f32(p.scale_bits).reshape(n, 1)
+    ref = o4.gemm_w4a16_rows(a, o4.pack(p.codes, 1), 1, s, 8.0, k)
+    check_bf16_rows(c, ref)
+
+
+def test_gemm_integer_exact():
+    say("gemm integer exact")
+    rng = np.random.default_rng(4)
+    m, n, k = 320, 384, 1024
+    a = rng.integers(-4, 5, (m, k)).astype(np.float32)
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    ones = fpformat.f32_to_bf16_bits(np.ones(n, np.float32))
+    c = run(fpformat.f32_to_bf16_bits(a), codes, ones)
+    exact = a.astype(np.int64) @ (codes.astype(np.int64) - 8).T
+    want = fpformat.f32_to_bf16_bits(exact.astype(np.float32))
+    assert np.array_equal(c.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+def test_gemm_zero_point_other_than_8():
+    say("gemm zero point 5")
+    rng = np.random.default_rng(6)
+    m, n, k = 128, 256, 256
+    a = rng.integers(-3, 4, (m, k)).astype(np.float32)
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    ones = fpformat.f32_to_bf16_bits(np.ones(n, np.float32))
+    c = run(fpformat.f32_to_bf16_bits(a), codes, ones, zc=5.0)
+    exact = a.astype(np.int64) @ (codes.astype(np.int64) - 5).T
+    want = fpformat.f32_to_bf16_bits(exact.astype(np.float32))
+    assert np.array_equal(c.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+def test_gemm_8192_sampled_rows():
+    p = wq_inputs.large_gemm()
+    say("gemm 8192^3, sampled rows", len(p.rows))
+    c = run(p.a_bits, p.codes, p.scale_bits)
+    rows = torch.from_numpy(p.rows).cuda()
+    got = c.index_select(0, rows).float().cpu().numpy()
+    a = fpformat.bf16_bits_to_f32(p.a_bits[p.rows])
+    s = fpformat.bf16_bits_to_f32(p.scale_bits).reshape(-1, 1)
+    ref = o4.gemm_w4a16_rows(a, o4.pack(p.codes, 1), 1, s, 8.0, p.k)
+    check_bf16_rows(got, ref)
+    # every other row: finite and of the expected magnitude (property at any size)
+    allc = c.float()
+    assert torch.isfinite(allc).all()
+    rms = allc.pow(2).mean(dim=1).sqrt().cpu().numpy()
+    expect = float(np.sqrt(np.mean(ref ** 2)))
+    assert np.all(np.abs(rms / expect - 1) < 0.1)

@@ -1,0 +1,103 @@
+"""GPU parity: PTQ1_0 packing, q8_1 quantiser and the ternary GEMV."""
+import numpy as np
+import pytest
+import torch
+
+import wq_inputs
+from oracle import ternary as ot
+from tolerances import check_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def G():
+    import gemm_wq_quantize_amd as g
+    return g
+
+
+def gpu_blocks(trits, d_bits):
+    n, k = trits.shape
+    out = torch.empty((n, k // 128, 28), dtype=torch.uint8, device="cuda")
+    G().wq_pack_ptq1_0(torch.from_numpy(trits).cuda(),
+                       torch.from_numpy(d_bits).view(torch.int16).cuda(), out)
+    return out
+
+
+def gpu_q8(x):
+    c, k = x.shape
+    out = torch.empty((c, k // 32, 36), dtype=torch.uint8, device="cuda")
+    G().wq_quantize_q8_1(torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda(), out)
+    return out
+
+
+def gpu_gemv(wb, xq, k):
+    n, c = wb.shape[0], xq.shape[0]
+    out = torch.empty((c, n), dtype=torch.float32, device="cuda")
+    G().wq_gemv_ternary(wb, xq, k, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (33, 1024), (17280, 5120)])
+def test_pack_ptq1_0_bit_exact(n, k):
+    say("ptq1_0 pack", n, k)
+    p = wq_inputs.ternary_gemv(k, n, cmax=1, seed=n)
+    got = gpu_blocks(p.trits, p.d_bits).cpu().numpy()
+    assert np.array_equal(got, ot.encode_ptq1_0(p.trits, p.d_bits))
+
+
+@pytest.mark.parametrize("c,k", [(1, 32), (3, 4096), (8, 5120)])
+def test_quantize_q8_1_bit_exact(c, k):
+    say("q8_1", c, k)
+    rng = np.random.default_rng(c * k)
+    x = rng.standard_normal((c, k)).astype(np.float32)
+    x[0, :32] = 0.0                                   # zero block
+    if k >= 64:
+        x[0, 32:64] = np.arange(32) - 15.5            # ties at d = 16/127...
+    assert np.array_equal(gpu_q8(x).cpu().numpy(), ot.quantize_q8_1(x))
+
+
+@pytest.mark.parametrize("k,n", [(5120, 17280), (17280, 1000), (384, 77)])
+def test_ternary_gemv(k, n):
+    p = wq_inputs.ternary_gemv(k, n, cmax=16)
+    wb = gpu_blocks(p.trits, p.d_bits)
+    wref = ot.encode_ptq1_0(p.trits, p.d_bits)
+    cs = (1, 4, 8) if k == 5120 else (1, 3, 5, 16)
+    for c in cs:
+        say("ternary gemv", k, n, c)
+        xq = gpu_q8(p.x[:c])
+        xref = ot.quantize_q8_1(p.x[:c])
+        assert np.array_equal(xq.cpu().numpy(), xref)
+        check_f32(gpu_gemv(wb, xq, k), ot.gemv_ternary(wref, xref))
+
+
+@pytest.mark.parametrize("k,n", [(5120, 4000), (17280, 300)])
+def test_ternary_unit_scale_exact(k, n):
+    say("ternary unit scale", k, n)
+    p = wq_inputs.ternary_gemv(k, n, cmax=8, unit_scale=True)
+    wb = gpu_blocks(p.trits, p.d_bits)
+    xq = gpu_q8(p.x)
+    got = gpu_gemv(wb, xq, k)
+    exact = p.x.astype(np.int64) @ p.trits.astype(np.int64).T
+    assert np.array_equal(got, exact.astype(np.float64))
+
+
+def test_ternary_special_cases():
+    say("ternary all-zero / all-one trits")
+    k, n = 1024, 40
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4, k)).astype(np.float32)
+    d = wq_inputs.to_f16_bits(rng.uniform(0.01, 0.05, (n, k // 128)))
+    xq = gpu_q8(x)
+    xref = ot.quantize_q8_1(x)
+    for t in (np.zeros((n, k), np.int8), np.ones((n, k), np.int8), -np.ones((n, k), np.int8)):
+        got = gpu_gemv(gpu_blocks(t, d), xq, k)
+        ref = ot.gemv_ternary(ot.encode_ptq1_0(t, d), xref)
+        if not t.any():
+            assert np.all(got == 0)
+        else:
+            check_f32(got, ref)
