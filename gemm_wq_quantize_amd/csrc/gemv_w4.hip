@@ -23,6 +23,8 @@
 // v_cvt_f32_ubyte on the masked nibbles and fp32 FMAs.
 #include "wq_internal.h"
 
+#include <algorithm>
+
 namespace wq {
 namespace {
 
@@ -46,6 +48,27 @@ __device__ __forceinline__ float load_param(const void* p, int64_t i, int bf16) 
               : reinterpret_cast<const float*>(p)[i];
 }
 
+// (x & mask) | bits in one v_and_or_b32: gfx9 VOP3 encodings take no
+// literal, so the mask comes from an SGPR and the OR-ed bits from a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask_s, uint32_t bits_v) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask_s), "v"(bits_v));
+  return r;
+}
+
+// A VGPR holding constant c (for and_or's third operand).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+// bf16 pair (128 + q_{2j}, 128 + q_{2j+1}) of gfx950-layout word w, given
+// the magic 0x43004300 in a VGPR.
+__device__ __forceinline__ uint32_t pair_bf16_fast(uint32_t w, int j, uint32_t magic_v) {
+  return and_or(j == 0 ? w : w >> (4 * j), 0x000F000Fu, magic_v);
+}
+
 // bf16 pair (128 + q_{2j}, 128 + q_{2j+1}) of word w.
 template <int LAYOUT>
 __device__ __forceinline__ uint32_t pair_bf16(uint32_t w, int j) {
@@ -63,7 +86,7 @@ __device__ __forceinline__ float code_f32(uint32_t w, int e) {
 }
 
 template <int R, int C, bool XBF16, int LAYOUT>
-__global__ __launch_bounds__(256) void k_gemv_w4(KArgs p) {
+__global__ __launch_bounds__(256) void k_gemv_w4_tiled(KArgs p) {
   // x tile in LDS, 16-byte units arranged so lane i of a half-wave reads
   // unit i of each piece with no bank conflict: [col][piece][chunk].
   constexpr int UPC = XBF16 ? 4 : 8;  // 16-byte units per chunk (32 k)
@@ -233,39 +256,604 @@ __global__ __launch_bounds__(256) void k_gemv_w4(KArgs p) {
   }
 }
 
+
+// Streaming variant for bf16 activations (the decode path).  Same lane
+// layout as k_gemv_w4_tiled, but:
+//  * x is staged once per stage of sc_tiles tiles (the whole K when it fits
+//    the LDS budget), so a workgroup passes at most a few barriers;
+//  * weight and scale loads run D tiles ahead in a register ring, so every
+//    lane keeps D x R 16-byte loads in flight;
+//  * loads are raw buffer loads relative to the workgroup's first row (32-bit
+//    offsets, one scalar descriptor), and rows past the end read as zero.
+template <int R, int C, int LAYOUT, int D>
+__global__ __launch_bounds__(256) void k_gemv_w4_stream(KArgs p, int sc_tiles) {
+  extern __shared__ uint4 smem[];
+  const int sch = TILE_CHUNKS * sc_tiles;                       // chunks per stage
+  uint4* xs = smem;                                             // [C][4][sch]
+  float* sxs = reinterpret_cast<float*>(smem + C * 4 * sch);    // [C][sch]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 31;
+  const int hw = tid >> 5;
+  const int64_t wg_row0 = (int64_t)blockIdx.x * 8 * R;
+  const int64_t nchunks = p.k / 32;
+  const int64_t rowbytes = p.k / 2;
+  const int nit = (int)((nchunks + TILE_CHUNKS - 1) / TILE_CHUNKS);
+  const int64_t ngroups = p.gshift < 0 ? 1 : (nchunks >> p.gshift);
+  const int esz = p.scale_bf16 ? 2 : 4;
+  const bool has_zeros = p.zeros != nullptr;
+
+  // scalar descriptors over this workgroup's rows only
+  const int64_t wg_rows = min((int64_t)8 * R, p.n - wg_row0);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.packed + wg_row0 * rowbytes), 0, (int)(wg_rows * rowbytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)p.scales + wg_row0 * ngroups * esz), 0, (int)(wg_rows * ngroups * esz),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(has_zeros ? (const char*)p.zeros + wg_row0 * ngroups * esz : (const char*)p.scales), 0,
+      (int)(wg_rows * ngroups * esz), 0x00020000);
+
+  uint4 wv[D][R];
+  float sc[D][R], zb[D][R];
+  float acc[R][C];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < C; ++j) acc[r][j] = 0.f;
+
+  // local row of (half-wave, r) is hw * R + r
+#define WQ_ISSUE(SLOT, IT)                                                                   \
+  do {                                                                                       \
+    const int ch_ = (IT) * TILE_CHUNKS + lane;                                               \
+    const bool ok_ = ch_ < nchunks;                                                          \
+    const int g_ = p.gshift < 0 ? 0 : (ch_ >> p.gshift);                                     \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                          \
+      const int lr_ = hw * R + r;                                                            \
+      if (ok_) {                                                                             \
+        wv[SLOT][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(        \
+                          wrs, (int)(lr_ * rowbytes) + ch_ * 16, 0, 0));                      \
+        const int so_ = (int)((lr_ * ngroups + g_) * esz);                                   \
+        float s_, z_ = p.zero_const;                                                         \
+        if (p.scale_bf16) {                                                                  \
+          s_ = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(srs, so_, 0, 0));            \
+          if (has_zeros) z_ = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(zrs, so_, 0, 0)); \
+        } else {                                                                             \
+          s_ = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, so_, 0, 0));        \
+          if (has_zeros) z_ = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zrs, so_, 0, 0)); \
+        }                                                                                    \
+        sc[SLOT][r] = s_;                                                                    \
+        zb[SLOT][r] = 128.f + z_;                                                            \
+      } else {                                                                               \
+        wv[SLOT][r] = make_uint4(0, 0, 0, 0);                                                \
+        sc[SLOT][r] = 0.f;                                                                   \
+        zb[SLOT][r] = 0.f;                                                                   \
+      }                                                                                      \
+    }                                                                                        \
+  } while (0)
+
+#pragma unroll
+  for (int d = 0; d < D; ++d) WQ_ISSUE(d, d);
+
+  for (int base = 0; base < nit; base += D) {
+    if (base % sc_tiles == 0) {
+      // stage x for tiles [base, base + sc_tiles) and the per-chunk sums of x
+      __syncthreads();
+      const int64_t k0 = (int64_t)base * TILE_K;
+      const int units = C * 128 * sc_tiles;
+      for (int idx = tid; idx < units; idx += 256) {
+        const int col = idx / (128 * sc_tiles);
+        const int u = idx % (128 * sc_tiles);
+        const int t2 = u >> 7, v = u & 127;
+        const int ch = v >> 2, piece = v & 3;
+        const int64_t kk = k0 + (int64_t)u * 8;
+        uint4 xv = make_uint4(0, 0, 0, 0);
+        if (col < p.c && kk < p.k)
+          xv = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) + col * p.k + kk);
+        xs[(col * 4 + piece) * sch + t2 * TILE_CHUNKS + ch] = xv;
+        float ps = ((bf16_to_f32(xv.x & 0xFFFFu) + bf16_to_f32(xv.x >> 16)) +
+                    (bf16_to_f32(xv.y & 0xFFFFu) + bf16_to_f32(xv.y >> 16))) +
+                   ((bf16_to_f32(xv.z & 0xFFFFu) + bf16_to_f32(xv.z >> 16)) +
+                    (bf16_to_f32(xv.w & 0xFFFFu) + bf16_to_f32(xv.w >> 16)));
+        ps += __shfl_xor(ps, 1);
+        ps += __shfl_xor(ps, 2);
+        if (piece == 0) sxs[col * sch + t2 * TILE_CHUNKS + ch] = ps;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int it = base + d;
+      if (it * TILE_CHUNKS + lane < nchunks) {
+        uint32_t wp[R][16];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t w4[4] = {wv[d][r].x, wv[d][r].y, wv[d][r].z, wv[d][r].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wp[r][4 * q + j] = pair_bf16<LAYOUT>(w4[q], j);
+        }
+        const int xo = (it % sc_tiles) * TILE_CHUNKS + lane;
+#pragma unroll
+        for (int col = 0; col < C; ++col) {
+          uint32_t xv[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 v = xs[(col * 4 + q) * sch + xo];
+            xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+          }
+          const float sx = sxs[col * sch + xo];
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            float dd = -zb[d][r] * sx;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              dd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e]),
+                                                   __builtin_bit_cast(bf16x2, xv[e]), dd, false);
+            acc[r][col] = fmaf(sc[d][r], dd, acc[r][col]);
+          }
+        }
+      }
+      WQ_ISSUE(d, it + D);
+    }
+  }
+#undef WQ_ISSUE
+
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float v = acc[r][j];
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      acc[r][j] = v;
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if (j >= p.c) break;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = wg_row0 + hw * R + r;
+        if (row < p.n) {
+          if (p.out_bf16)
+            reinterpret_cast<uint16_t*>(p.out)[j * p.n + row] = (uint16_t)f32_to_bf16_rne(acc[r][j]);
+          else
+            reinterpret_cast<float*>(p.out)[j * p.n + row] = acc[r][j];
+        }
+      }
+    }
+  }
+}
+
+// Persistent variant for bf16 activations whose whole x fits in LDS (the
+// decode batches).  One workgroup of NT lanes per CU; workgroup w owns a
+// contiguous, balanced block of rows (+-1 row).  Its work is a list of items
+// (row-group of R rows, tile of 1024 k) in row-group-major order, cut into
+// NT/32 equal contiguous ranges, one per half-wave, so every half-wave
+// streams the same number of 16-byte loads and keeps D items in flight from
+// start to finish.  x, its per-chunk sums and the workgroup's scales (and
+// zeros) are staged in LDS once.  A half-wave reduces its partial for a
+// row-group when it leaves it and parks it in an LDS slot; the slots of each
+// row-group are summed in half-wave order at the end (fixed order: bitwise
+// repeatable).
+//
+// The item loop has no branches around loads and no divisions: the
+// (row-group, tile) position advances incrementally, offsets are 32-bit
+// and relative to the workgroup's rows, and an item that must not load
+// (past the half-wave's range, or a chunk past K) gets an offset beyond the
+// buffer, which the buffer unit answers with zeros -- zero codes, zero x and
+// a zero scale contribute exactly nothing.
+constexpr uint32_t OOB = 0x80000000u;
+
+template <int NT, int R, int C, int LAYOUT, int D, bool HZ>
+__global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int maxrows) {
+  constexpr int NHW = NT / 32;
+  extern __shared__ uint4 smem[];
+  const int nchunks = (int)(p.k / 32);
+  const int nit = (nchunks + TILE_CHUNKS - 1) / TILE_CHUNKS;
+  const int nch = nit * TILE_CHUNKS;                              // chunks in LDS
+  const int ngroups = p.gshift < 0 ? 1 : (nchunks >> p.gshift);
+  uint4* xs = smem;                                               // [C][4][nch]
+  float* sxs = reinterpret_cast<float*>(smem + C * 4 * nch);      // [C][nch]
+  float* slots = sxs + C * nch;                                   // [NHW][sph][R][C]
+  int* hwtab = reinterpret_cast<int*>(slots + NHW * sph * R * C); // [NHW][3]: i0, i1, rg_first
+  // scales (and zeros) in LDS in their own dtype: [maxrows][ngroups] each
+  char* sbytes = reinterpret_cast<char*>(hwtab + NHW * 3);
+  const int esz = p.scale_bf16 ? 2 : 4;
+  char* zbytes = sbytes + maxrows * ngroups * esz;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 31;
+  const int hw = tid >> 5;
+  // this workgroup's rows (n < 2^31 is checked by the launcher)
+  const int n32 = (int)p.n;
+  const int q = n32 / (int)gridDim.x, rem = n32 % (int)gridDim.x;
+  const int r0 = (int)blockIdx.x * q + min((int)blockIdx.x, rem);
+  const int count = q + ((int)blockIdx.x < rem ? 1 : 0);
+  const int nrg = (count + R - 1) / R;
+  const int items = nrg * nit;
+  const int i0 = (hw * items) / NHW, i1 = ((hw + 1) * items) / NHW;
+  const int rg_first = i0 / nit;
+  if (lane == 0) {
+    hwtab[hw * 3 + 0] = i0;
+    hwtab[hw * 3 + 1] = i1;
+    hwtab[hw * 3 + 2] = rg_first;
+  }
+
+  const int rowbytes = (int)(p.k / 2);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.packed + (int64_t)r0 * rowbytes), 0, count * rowbytes, 0x00020000);
+
+  // issue position: row-group ig, tile itile, items left to issue
+  int ig = rg_first, itile = i0 - rg_first * nit, left = i1 - i0;
+  uint4 wv[D][R];
+  auto issue = [&](uint4 (&w)[R]) {
+    const int ch = itile * TILE_CHUNKS + lane;
+    const bool ok = left > 0 && ch < nchunks;
+    const uint32_t wo = ok ? (uint32_t)(ig * R * rowbytes + ch * 16) : OOB;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                 wrs, wo + (uint32_t)(r * rowbytes), 0, 0));
+    --left;
+    if (++itile == nit) { itile = 0; ++ig; }
+  };
+
+  // Staging loads are issued before the weight prologue: loads complete in
+  // issue order, so waiting for them must not also wait for the weights.
+  constexpr int XU = 10, SU = 4;  // per-lane staging loads (launcher bounds both)
+  const int xunits = C * nch * 4;
+  uint4 xr[XU];
+#pragma unroll
+  for (int i = 0; i < XU; ++i) {
+    const int idx = tid + i * NT;
+    xr[i] = make_uint4(0, 0, 0, 0);
+    if (idx < xunits) {
+      const int col = idx / (nch * 4);
+      const int kk = (idx - col * nch * 4) * 8;
+      if (col < p.c && kk < p.k)
+        xr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) + col * p.k + kk);
+    }
+  }
+  const int nsc = count * ngroups;
+  const int64_t sbase = (int64_t)r0 * ngroups;
+  uint32_t sr[SU], zr[SU];  // raw scale / zero bits
+#pragma unroll
+  for (int i = 0; i < SU; ++i) {
+    const int idx = tid + i * NT;
+    sr[i] = 0u;
+    zr[i] = 0u;
+    if (idx < nsc) {
+      if (p.scale_bf16) {
+        sr[i] = reinterpret_cast<const uint16_t*>(p.scales)[sbase + idx];
+        if (HZ) zr[i] = reinterpret_cast<const uint16_t*>(p.zeros)[sbase + idx];
+      } else {
+        sr[i] = reinterpret_cast<const uint32_t*>(p.scales)[sbase + idx];
+        if (HZ) zr[i] = reinterpret_cast<const uint32_t*>(p.zeros)[sbase + idx];
+      }
+    }
+  }
+
+  // weight prologue: D items in flight per half-wave
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(wv[d]);
+
+  // x (zero beyond k and beyond c) and the per-chunk sums of x into LDS
+#pragma unroll
+  for (int i = 0; i < XU; ++i) {
+    const int idx = tid + i * NT;
+    if (i * NT >= xunits) break;  // uniform over the workgroup
+    const uint4 xv = xr[i];
+    float ps = ((bf16_to_f32(xv.x & 0xFFFFu) + bf16_to_f32(xv.x >> 16)) +
+                (bf16_to_f32(xv.y & 0xFFFFu) + bf16_to_f32(xv.y >> 16))) +
+               ((bf16_to_f32(xv.z & 0xFFFFu) + bf16_to_f32(xv.z >> 16)) +
+                (bf16_to_f32(xv.w & 0xFFFFu) + bf16_to_f32(xv.w >> 16)));
+    ps += __shfl_xor(ps, 1);
+    ps += __shfl_xor(ps, 2);
+    if (idx < xunits) {
+      const int col = idx / (nch * 4);
+      const int u = idx - col * nch * 4;
+      const int ch = u >> 2, piece = u & 3;
+      xs[(col * 4 + piece) * nch + ch] = xv;
+      if (piece == 0) sxs[col * nch + ch] = ps;
+    }
+  }
+  // this workgroup's scales (and zeros); rows past count read 0
+#pragma unroll
+  for (int i = 0; i < SU; ++i) {
+    const int idx = tid + i * NT;
+    if (idx < maxrows * ngroups) {
+      if (p.scale_bf16) {
+        reinterpret_cast<uint16_t*>(sbytes)[idx] = (uint16_t)sr[i];
+        if (HZ) reinterpret_cast<uint16_t*>(zbytes)[idx] = (uint16_t)zr[i];
+      } else {
+        reinterpret_cast<uint32_t*>(sbytes)[idx] = sr[i];
+        if (HZ) reinterpret_cast<uint32_t*>(zbytes)[idx] = zr[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  const float zconst = 128.f + p.zero_const;
+  const uint32_t magic_v = vconst(0x43004300u);
+  float acc[R][C];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < C; ++j) acc[r][j] = 0.f;
+
+  // butterfly over the half-wave, then lanes 0 .. R*C-1 park one value each
+  auto flush = [&](int rg) {
+    float* dst = slots + ((hw * sph + (rg - rg_first)) * R) * C;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        float v = acc[r][j];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 1);
+        if (lane == r * C + j) dst[r * C + j] = v;
+        acc[r][j] = 0.f;
+      }
+  };
+
+  // consume position: row-group cg, tile ct
+  int cg = rg_first, ct = i0 - rg_first * nit;
+  for (int base = i0; base < i1; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (base + d < i1) {
+        const int xo = ct * TILE_CHUNKS + lane;
+        const int g = p.gshift < 0 ? 0 : (xo >> p.gshift);
+        uint32_t wp[R][16];
+        float sc[R], zb[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t w4[4] = {wv[d][r].x, wv[d][r].y, wv[d][r].z, wv[d][r].w};
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              wp[r][4 * qq + j] = LAYOUT == 1 ? pair_bf16_fast(w4[qq], j, magic_v)
+                                              : pair_bf16<LAYOUT>(w4[qq], j);
+          const int si = (cg * R + r) * ngroups + g;
+          if (p.scale_bf16) {
+            sc[r] = bf16_to_f32(reinterpret_cast<const uint16_t*>(sbytes)[si]);
+            zb[r] = HZ ? 128.f + bf16_to_f32(reinterpret_cast<const uint16_t*>(zbytes)[si]) : zconst;
+          } else {
+            sc[r] = reinterpret_cast<const float*>(sbytes)[si];
+            zb[r] = HZ ? 128.f + reinterpret_cast<const float*>(zbytes)[si] : zconst;
+          }
+        }
+        issue(wv[d]);  // the ring slot is free once unpacked
+#pragma unroll
+        for (int col = 0; col < C; ++col) {
+          uint32_t xv[16];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const uint4 v = xs[(col * 4 + qq) * nch + xo];
+            xv[4 * qq + 0] = v.x; xv[4 * qq + 1] = v.y; xv[4 * qq + 2] = v.z; xv[4 * qq + 3] = v.w;
+          }
+          const float sx = sxs[col * nch + xo];
+          float d0[R], d1[R];
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            d0[r] = -zb[r] * sx;
+            d1[r] = 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 16; e += 2)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              d0[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e]),
+                                                      __builtin_bit_cast(bf16x2, xv[e]), d0[r], false);
+              d1[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e + 1]),
+                                                      __builtin_bit_cast(bf16x2, xv[e + 1]), d1[r], false);
+            }
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r][col] = fmaf(sc[r], d0[r] + d1[r], acc[r][col]);
+        }
+        if (++ct == nit) {
+          flush(cg);
+          ct = 0;
+          ++cg;
+        }
+      }
+    }
+  }
+  if (i1 > i0 && ct != 0) flush(cg);
+  __syncthreads();
+
+  // sum the parked partials of each (row-group, r, column) in half-wave order
+  for (int idx = tid; idx < nrg * R * C; idx += NT) {
+    const int rg = idx / (R * C);
+    const int rc = idx - rg * R * C;
+    const int r = rc / C, col = rc - r * C;
+    if (col >= p.c || rg * R + r >= count) continue;
+    const int ilo = rg * nit, ihi = ilo + nit;
+    // half-wave h owns items [floor(h*items/NHW), floor((h+1)*items/NHW)); the
+    // one owning item i is floor(((i + 1) * NHW - 1) / items)
+    const int hlo = ((ilo + 1) * NHW - 1) / items, hhi = (ihi * NHW - 1) / items;
+    float v = 0.f;
+    for (int h = hlo; h <= hhi; ++h) {
+      const int a = hwtab[h * 3 + 0], b = hwtab[h * 3 + 1];
+      if (b > a && a < ihi && b > ilo) v += slots[((h * sph + (rg - hwtab[h * 3 + 2])) * R + r) * C + col];
+    }
+    const int64_t row = (int64_t)r0 + rg * R + r;
+    if (p.out_bf16)
+      reinterpret_cast<uint16_t*>(p.out)[col * p.n + row] = (uint16_t)f32_to_bf16_rne(v);
+    else
+      reinterpret_cast<float*>(p.out)[col * p.n + row] = v;
+  }
+}
+
+constexpr int STREAM_LDS_BUDGET = 48 * 1024;  // bytes of LDS per workgroup
+
+// D: weight tiles in flight per lane (4 for the decode batches; fewer for
+// wide batches, whose LDS stage must then be shorter).
+template <int R, int C, int D>
+hipError_t launch_stream(const KArgs& ka, int layout, hipStream_t s) {
+  const int nit = (int)((ka.k / 32 + TILE_CHUNKS - 1) / TILE_CHUNKS);
+  const int per_tile = C * TILE_CHUNKS * (64 + 4);  // x units + chunk sums, bytes
+  int sc_tiles = STREAM_LDS_BUDGET / per_tile;
+  if (sc_tiles >= nit) {
+    sc_tiles = nit;  // one stage holds all of x
+  } else {
+    sc_tiles = (sc_tiles / D) * D;  // stages start at ring boundaries
+    if (sc_tiles < D) sc_tiles = D;
+  }
+  const size_t lds = (size_t)per_tile * sc_tiles;
+  const unsigned blocks = (unsigned)((ka.n + 8 * R - 1) / (8 * R));
+  if (layout == 1)
+    hipLaunchKernelGGL((k_gemv_w4_stream<R, C, 1, D>), dim3(blocks), dim3(256), lds, s, ka, sc_tiles);
+  else
+    hipLaunchKernelGGL((k_gemv_w4_stream<R, C, 0, D>), dim3(blocks), dim3(256), lds, s, ka, sc_tiles);
+  return hipGetLastError();
+}
+
+
+// ---- persistent launcher
+constexpr int PERSIST_LDS_MAX = 160 * 1024;  // all of a gfx950 CU's LDS
+
+#ifndef WQ_P_NT
+#define WQ_P_NT 1024
+#endif
+#ifndef WQ_P_R
+#define WQ_P_R 2
+#endif
+#ifndef WQ_P_D
+#define WQ_P_D 2
+#endif
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+// Largest number of row-groups one half-wave touches, over the two row
+// counts (q and q + 1) the workgroups get.
+int persist_slots(int64_t n, int grid, int R, int nit, int nhw) {
+  const int64_t q = n / grid;
+  int best = 1;
+  for (int64_t cnt = q; cnt <= q + 1; ++cnt) {
+    const int64_t items = ((cnt + R - 1) / R) * nit;
+    for (int h = 0; h < nhw; ++h) {
+      const int64_t a = h * items / nhw, b = (h + 1) * items / nhw;
+      if (b > a) best = std::max(best, (int)((b - 1) / nit - a / nit + 1));
+    }
+  }
+  return best;
+}
+
+// Returns hipErrorInvalidValue (without launching) when x does not fit in LDS.
+template <int C>
+hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
+  constexpr int NT = WQ_P_NT, R = WQ_P_R, D = WQ_P_D, NHW = NT / 32;
+  if (ka.n >= (int64_t(1) << 31) || ka.k >= (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int64_t nchunks = ka.k / 32;
+  const int nit = (int)((nchunks + TILE_CHUNKS - 1) / TILE_CHUNKS);
+  const int64_t nch = (int64_t)nit * TILE_CHUNKS;
+  const int64_t ngroups = ka.gshift < 0 ? 1 : (nchunks >> ka.gshift);
+  int grid = cu_count();
+  if ((int64_t)grid * R > ka.n) grid = (int)std::max<int64_t>(1, ka.n / R);
+  const int maxrows = (int)((ka.n + grid - 1) / grid);
+  const int sph = persist_slots(ka.n, grid, R, nit, NHW);
+  const bool hz = ka.zeros != nullptr;
+  const int64_t lds = C * nch * (64 + 4) + (int64_t)NHW * sph * R * C * 4 + NHW * 3 * 4 +
+                      (int64_t)maxrows * ngroups * (ka.scale_bf16 ? 2 : 4) * (hz ? 2 : 1);
+  if (lds > PERSIST_LDS_MAX) return hipErrorInvalidValue;
+  // per-lane staging registers of the kernel (x: 10 units, scales: 4)
+  if (C * nch * 4 > 10 * NT || (int64_t)maxrows * ngroups > 4 * NT) return hipErrorInvalidValue;
+  const void* fns[2][2] = {
+      {reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, 0, D, false>),
+       reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, 0, D, true>)},
+      {reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, 1, D, false>),
+       reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, 1, D, true>)}};
+  static bool attr_set[2][2] = {{false, false}, {false, false}};
+  if (!attr_set[layout][hz]) {
+    hipFuncSetAttribute(fns[layout][hz], hipFuncAttributeMaxDynamicSharedMemorySize, PERSIST_LDS_MAX);
+    attr_set[layout][hz] = true;
+  }
+  int sph_arg = sph, maxrows_arg = maxrows;
+  void* args[] = {const_cast<KArgs*>(&ka), &sph_arg, &maxrows_arg};
+  return hipLaunchKernel(fns[layout][hz], dim3(grid), dim3(NT), args, (size_t)lds, s);
+}
+
+#ifndef WQ_STREAM_ROWS
+#define WQ_STREAM_ROWS 0
+#endif
+
+template <int C>
+hipError_t launch_stream_c(const KArgs& ka, int layout, hipStream_t s) {
+#ifndef WQ_NO_PERSIST
+  if constexpr (C <= 4) {
+    hipError_t e = launch_persist<C>(ka, layout, s);
+    if (e != hipErrorInvalidValue) return e;
+  }
+#endif
+  constexpr int D = C <= 4 ? 4 : (C <= 8 ? 2 : 1);
+  // rows per half-wave: 2 when that still leaves >= 4 workgroups per CU
+  if (WQ_STREAM_ROWS == 2 || (WQ_STREAM_ROWS == 0 && C <= 4 && ka.n >= 16 * 1024))
+    return launch_stream<2, C, D>(ka, layout, s);
+  return launch_stream<1, C, D>(ka, layout, s);
+}
+
 template <int R, int C, bool XBF16>
 hipError_t launch_rc(const KArgs& ka, int layout, hipStream_t s) {
   const int64_t rows_per_wg = 8 * R;
   const unsigned blocks = (unsigned)((ka.n + rows_per_wg - 1) / rows_per_wg);
   if (layout == 1)
-    hipLaunchKernelGGL((k_gemv_w4<R, C, XBF16, 1>), dim3(blocks), dim3(256), 0, s, ka);
+    hipLaunchKernelGGL((k_gemv_w4_tiled<R, C, XBF16, 1>), dim3(blocks), dim3(256), 0, s, ka);
   else
-    hipLaunchKernelGGL((k_gemv_w4<R, C, XBF16, 0>), dim3(blocks), dim3(256), 0, s, ka);
+    hipLaunchKernelGGL((k_gemv_w4_tiled<R, C, XBF16, 0>), dim3(blocks), dim3(256), 0, s, ka);
   return hipGetLastError();
 }
 
 template <int C, bool XBF16>
 hipError_t launch_c(const KArgs& ka, int layout, hipStream_t s) {
-  // rows per half-wave: keep enough workgroups to spread over 256 CUs and
-  // keep registers in bounds for wide batches and fp32 activations
-  const int64_t target_wgs = 1024;
-  if (XBF16 && C <= 4 && ka.n >= 32 * target_wgs) return launch_rc<4, C, XBF16>(ka, layout, s);
-  if (C <= 8 && ka.n >= 16 * target_wgs) return launch_rc<2, C, XBF16>(ka, layout, s);
+  // fp32 activations and the widest batches: rows per half-wave chosen to
+  // keep enough workgroups and registers in bounds
+  if (C <= 8 && ka.n >= 16 * 1024) return launch_rc<2, C, XBF16>(ka, layout, s);
   return launch_rc<1, C, XBF16>(ka, layout, s);
 }
 
-template <bool XBF16>
-hipError_t launch_x(const KArgs& ka, int layout, hipStream_t s) {
+hipError_t launch_bf16(const KArgs& ka, int layout, hipStream_t s) {
   switch (ka.c) {
-    case 1: return launch_c<1, XBF16>(ka, layout, s);
-    case 2: return launch_c<2, XBF16>(ka, layout, s);
-    case 3: return launch_c<3, XBF16>(ka, layout, s);
-    case 4: return launch_c<4, XBF16>(ka, layout, s);
+    case 1: return launch_stream_c<1>(ka, layout, s);
+    case 2: return launch_stream_c<2>(ka, layout, s);
+    case 3: return launch_stream_c<3>(ka, layout, s);
+    case 4: return launch_stream_c<4>(ka, layout, s);
     default: break;
   }
-  if (ka.c <= 8) return launch_c<8, XBF16>(ka, layout, s);
-  if (ka.c <= 16) return launch_c<16, XBF16>(ka, layout, s);
-  return launch_c<32, XBF16>(ka, layout, s);
+  if (ka.c <= 8) return launch_stream_c<8>(ka, layout, s);
+  if (ka.c <= 16) return launch_stream_c<16>(ka, layout, s);
+  return launch_c<32, true>(ka, layout, s);
+}
+
+hipError_t launch_f32(const KArgs& ka, int layout, hipStream_t s) {
+  switch (ka.c) {
+    case 1: return launch_c<1, false>(ka, layout, s);
+    case 2: return launch_c<2, false>(ka, layout, s);
+    case 3: return launch_c<3, false>(ka, layout, s);
+    case 4: return launch_c<4, false>(ka, layout, s);
+    default: break;
+  }
+  if (ka.c <= 8) return launch_c<8, false>(ka, layout, s);
+  if (ka.c <= 16) return launch_c<16, false>(ka, layout, s);
+  return launch_c<32, false>(ka, layout, s);
 }
 
 }  // namespace
@@ -290,7 +878,7 @@ hipError_t launch_gemv_w4(const GemvArgs& a, hipStream_t s) {
     while ((int64_t(32) << sh) < a.group) ++sh;
     ka.gshift = sh;
   }
-  return a.x_bf16 ? launch_x<true>(ka, a.layout, s) : launch_x<false>(ka, a.layout, s);
+  return a.x_bf16 ? launch_bf16(ka, a.layout, s) : launch_f32(ka, a.layout, s);
 }
 
 }  // namespace wq
