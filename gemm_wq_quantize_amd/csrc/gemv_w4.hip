@@ -24,6 +24,7 @@
 #include "wq_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace wq {
 namespace {
@@ -427,6 +428,17 @@ __global__ __launch_bounds__(256) void k_gemv_w4_stream(KArgs p, int sc_tiles) {
   }
 }
 
+// Sum over the 32 lanes of each half-wave with DPP (no LDS, no branch): the
+// total lands in lanes 16..31 of each half-wave.
+__device__ __forceinline__ float halfwave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad xor 1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad xor 2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror 4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror 8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast 15
+  return v;
+}
+
 // Persistent variant for bf16 activations whose whole x fits in LDS (the
 // decode batches).  One workgroup of NT lanes per CU; workgroup w owns a
 // contiguous, balanced block of rows (+-1 row).  Its work is a list of items
@@ -439,17 +451,19 @@ __global__ __launch_bounds__(256) void k_gemv_w4_stream(KArgs p, int sc_tiles) {
 // row-group are summed in half-wave order at the end (fixed order: bitwise
 // repeatable).
 //
-// The item loop has no branches around loads and no divisions: the
-// (row-group, tile) position advances incrementally, offsets are 32-bit
-// and relative to the workgroup's rows, and an item that must not load
-// (past the half-wave's range, or a chunk past K) gets an offset beyond the
-// buffer, which the buffer unit answers with zeros -- zero codes, zero x and
-// a zero scale contribute exactly nothing.
+// The ring of loads stays in flight only if no load sits under a branch (the
+// compiler's wait counting merges conservatively at joins), so the item loop
+// issues every load unconditionally: an item that must not load (past the
+// half-wave's range, or a chunk past K) gets an offset beyond the buffer,
+// which the buffer unit answers with zeros, and past-the-range items get a
+// zero scale -- they contribute exactly nothing.  Offsets are 32-bit,
+// relative to the workgroup's rows, and advance by additions only.
 constexpr uint32_t OOB = 0x80000000u;
 
-template <int NT, int R, int C, int LAYOUT, int D, bool HZ>
+template <int NT, int R, int C, int LAYOUT, int D, bool HZ, bool SBF>
 __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int maxrows) {
   constexpr int NHW = NT / 32;
+  using SType = typename std::conditional<SBF, uint16_t, float>::type;
   extern __shared__ uint4 smem[];
   const int nchunks = (int)(p.k / 32);
   const int nit = (nchunks + TILE_CHUNKS - 1) / TILE_CHUNKS;
@@ -459,10 +473,8 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
   float* sxs = reinterpret_cast<float*>(smem + C * 4 * nch);      // [C][nch]
   float* slots = sxs + C * nch;                                   // [NHW][sph][R][C]
   int* hwtab = reinterpret_cast<int*>(slots + NHW * sph * R * C); // [NHW][3]: i0, i1, rg_first
-  // scales (and zeros) in LDS in their own dtype: [maxrows][ngroups] each
-  char* sbytes = reinterpret_cast<char*>(hwtab + NHW * 3);
-  const int esz = p.scale_bf16 ? 2 : 4;
-  char* zbytes = sbytes + maxrows * ngroups * esz;
+  SType* sls = reinterpret_cast<SType*>(hwtab + NHW * 3);         // [maxrows][ngroups] scales
+  SType* zls = sls + maxrows * ngroups;                           // [maxrows][ngroups] zeros
 
   const int tid = threadIdx.x;
   const int lane = tid & 31;
@@ -483,22 +495,28 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
   }
 
   const int rowbytes = (int)(p.k / 2);
+  const int rgbytes = R * rowbytes;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.packed + (int64_t)r0 * rowbytes), 0, count * rowbytes, 0x00020000);
 
-  // issue position: row-group ig, tile itile, items left to issue
-  int ig = rg_first, itile = i0 - rg_first * nit, left = i1 - i0;
+  // issue position: byte offset of (row-group, tile) for this lane, tile,
+  // items left to issue
+  int itile = i0 - rg_first * nit, left = i1 - i0;
+  int ioff = rg_first * rgbytes + itile * (TILE_CHUNKS * 16) + lane * 16;
   uint4 wv[D][R];
   auto issue = [&](uint4 (&w)[R]) {
-    const int ch = itile * TILE_CHUNKS + lane;
-    const bool ok = left > 0 && ch < nchunks;
-    const uint32_t wo = ok ? (uint32_t)(ig * R * rowbytes + ch * 16) : OOB;
+    const bool ok = left > 0 && itile * TILE_CHUNKS + lane < nchunks;
+    const uint32_t wo = ok ? (uint32_t)ioff : OOB;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                  wrs, wo + (uint32_t)(r * rowbytes), 0, 0));
     --left;
-    if (++itile == nit) { itile = 0; ++ig; }
+    ioff += TILE_CHUNKS * 16;
+    if (++itile == nit) {
+      itile = 0;
+      ioff += rgbytes - nit * (TILE_CHUNKS * 16);
+    }
   };
 
   // Staging loads are issued before the weight prologue: loads complete in
@@ -519,20 +537,15 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
   }
   const int nsc = count * ngroups;
   const int64_t sbase = (int64_t)r0 * ngroups;
-  uint32_t sr[SU], zr[SU];  // raw scale / zero bits
+  SType sr[SU], zr[SU];
 #pragma unroll
   for (int i = 0; i < SU; ++i) {
     const int idx = tid + i * NT;
-    sr[i] = 0u;
-    zr[i] = 0u;
+    sr[i] = SType(0);
+    zr[i] = SType(0);
     if (idx < nsc) {
-      if (p.scale_bf16) {
-        sr[i] = reinterpret_cast<const uint16_t*>(p.scales)[sbase + idx];
-        if (HZ) zr[i] = reinterpret_cast<const uint16_t*>(p.zeros)[sbase + idx];
-      } else {
-        sr[i] = reinterpret_cast<const uint32_t*>(p.scales)[sbase + idx];
-        if (HZ) zr[i] = reinterpret_cast<const uint32_t*>(p.zeros)[sbase + idx];
-      }
+      sr[i] = reinterpret_cast<const SType*>(p.scales)[sbase + idx];
+      if (HZ) zr[i] = reinterpret_cast<const SType*>(p.zeros)[sbase + idx];
     }
   }
 
@@ -565,13 +578,8 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
   for (int i = 0; i < SU; ++i) {
     const int idx = tid + i * NT;
     if (idx < maxrows * ngroups) {
-      if (p.scale_bf16) {
-        reinterpret_cast<uint16_t*>(sbytes)[idx] = (uint16_t)sr[i];
-        if (HZ) reinterpret_cast<uint16_t*>(zbytes)[idx] = (uint16_t)zr[i];
-      } else {
-        reinterpret_cast<uint32_t*>(sbytes)[idx] = sr[i];
-        if (HZ) reinterpret_cast<uint32_t*>(zbytes)[idx] = zr[i];
-      }
+      sls[idx] = sr[i];
+      if (HZ) zls[idx] = zr[i];
     }
   }
   __syncthreads();
@@ -584,89 +592,95 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
 #pragma unroll
     for (int j = 0; j < C; ++j) acc[r][j] = 0.f;
 
-  // butterfly over the half-wave, then lanes 0 .. R*C-1 park one value each
-  auto flush = [&](int rg) {
-    float* dst = slots + ((hw * sph + (rg - rg_first)) * R) * C;
+  // consume position: row-group cg (first scale of its rows: srow0), tile ct
+  int cg = rg_first, ct = i0 - rg_first * nit;
+  int srow0 = cg * R * ngroups;
+  const int nsteps = i1 - i0;
+  for (int base = 0; base < nsteps; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const bool valid = base + d < nsteps;
+      const int xo = ct * TILE_CHUNKS + lane;
+      const int g = p.gshift < 0 ? 0 : (xo >> p.gshift);
+      uint32_t wp[R][16];
+      float sc[R], zb[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w4[4] = {wv[d][r].x, wv[d][r].y, wv[d][r].z, wv[d][r].w};
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            wp[r][4 * qq + j] = LAYOUT == 1 ? pair_bf16_fast(w4[qq], j, magic_v)
+                                            : pair_bf16<LAYOUT>(w4[qq], j);
+        const int si = srow0 + r * ngroups + g;
+        float sv, zv;
+        if constexpr (SBF) {
+          sv = bf16_to_f32(sls[si]);
+          zv = HZ ? 128.f + bf16_to_f32(zls[si]) : zconst;
+        } else {
+          sv = sls[si];
+          zv = HZ ? 128.f + zls[si] : zconst;
+        }
+        sc[r] = valid ? sv : 0.f;  // past-the-range items contribute nothing
+        zb[r] = zv;
+      }
+      issue(wv[d]);  // the ring slot is free once unpacked
+#pragma unroll
+      for (int col = 0; col < C; ++col) {
+        uint32_t xv[16];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const uint4 v = xs[(col * 4 + qq) * nch + xo];
+          xv[4 * qq + 0] = v.x; xv[4 * qq + 1] = v.y; xv[4 * qq + 2] = v.z; xv[4 * qq + 3] = v.w;
+        }
+        const float sx = sxs[col * nch + xo];
+        float d0[R], d1[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          d0[r] = -zb[r] * sx;
+          d1[r] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; e += 2)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            d0[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e]),
+                                                    __builtin_bit_cast(bf16x2, xv[e]), d0[r], false);
+            d1[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e + 1]),
+                                                    __builtin_bit_cast(bf16x2, xv[e + 1]), d1[r], false);
+          }
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][col] = fmaf(sc[r], d0[r] + d1[r], acc[r][col]);
+      }
+      if (valid && ++ct == nit) {
+        // leaving row-group cg: park its partials (lane 31 of the half-wave
+        // holds the sum after halfwave_sum), then start the next one
+        float* dst = slots + ((hw * sph + (cg - rg_first)) * R) * C;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int j = 0; j < C; ++j) {
+            const float v = halfwave_sum(acc[r][j]);
+            if (lane == 31) dst[r * C + j] = v;
+            acc[r][j] = 0.f;
+          }
+        ct = 0;
+        ++cg;
+        srow0 += R * ngroups;
+      }
+    }
+  }
+  if (nsteps > 0 && ct != 0) {
+    float* dst = slots + ((hw * sph + (cg - rg_first)) * R) * C;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        float v = acc[r][j];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 1);
-        if (lane == r * C + j) dst[r * C + j] = v;
-        acc[r][j] = 0.f;
+        const float v = halfwave_sum(acc[r][j]);
+        if (lane == 31) dst[r * C + j] = v;
       }
-  };
-
-  // consume position: row-group cg, tile ct
-  int cg = rg_first, ct = i0 - rg_first * nit;
-  for (int base = i0; base < i1; base += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (base + d < i1) {
-        const int xo = ct * TILE_CHUNKS + lane;
-        const int g = p.gshift < 0 ? 0 : (xo >> p.gshift);
-        uint32_t wp[R][16];
-        float sc[R], zb[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t w4[4] = {wv[d][r].x, wv[d][r].y, wv[d][r].z, wv[d][r].w};
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              wp[r][4 * qq + j] = LAYOUT == 1 ? pair_bf16_fast(w4[qq], j, magic_v)
-                                              : pair_bf16<LAYOUT>(w4[qq], j);
-          const int si = (cg * R + r) * ngroups + g;
-          if (p.scale_bf16) {
-            sc[r] = bf16_to_f32(reinterpret_cast<const uint16_t*>(sbytes)[si]);
-            zb[r] = HZ ? 128.f + bf16_to_f32(reinterpret_cast<const uint16_t*>(zbytes)[si]) : zconst;
-          } else {
-            sc[r] = reinterpret_cast<const float*>(sbytes)[si];
-            zb[r] = HZ ? 128.f + reinterpret_cast<const float*>(zbytes)[si] : zconst;
-          }
-        }
-        issue(wv[d]);  // the ring slot is free once unpacked
-#pragma unroll
-        for (int col = 0; col < C; ++col) {
-          uint32_t xv[16];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const uint4 v = xs[(col * 4 + qq) * nch + xo];
-            xv[4 * qq + 0] = v.x; xv[4 * qq + 1] = v.y; xv[4 * qq + 2] = v.z; xv[4 * qq + 3] = v.w;
-          }
-          const float sx = sxs[col * nch + xo];
-          float d0[R], d1[R];
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            d0[r] = -zb[r] * sx;
-            d1[r] = 0.f;
-          }
-#pragma unroll
-          for (int e = 0; e < 16; e += 2)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              d0[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e]),
-                                                      __builtin_bit_cast(bf16x2, xv[e]), d0[r], false);
-              d1[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e + 1]),
-                                                      __builtin_bit_cast(bf16x2, xv[e + 1]), d1[r], false);
-            }
-#pragma unroll
-          for (int r = 0; r < R; ++r) acc[r][col] = fmaf(sc[r], d0[r] + d1[r], acc[r][col]);
-        }
-        if (++ct == nit) {
-          flush(cg);
-          ct = 0;
-          ++cg;
-        }
-      }
-    }
   }
-  if (i1 > i0 && ct != 0) flush(cg);
   __syncthreads();
 
   // sum the parked partials of each (row-group, r, column) in half-wave order
@@ -777,19 +791,22 @@ hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
   if (lds > PERSIST_LDS_MAX) return hipErrorInvalidValue;
   // per-lane staging registers of the kernel (x: 10 units, scales: 4)
   if (C * nch * 4 > 10 * NT || (int64_t)maxrows * ngroups > 4 * NT) return hipErrorInvalidValue;
-  const void* fns[2][2] = {
-      {reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, 0, D, false>),
-       reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, 0, D, true>)},
-      {reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, 1, D, false>),
-       reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, 1, D, true>)}};
-  static bool attr_set[2][2] = {{false, false}, {false, false}};
-  if (!attr_set[layout][hz]) {
-    hipFuncSetAttribute(fns[layout][hz], hipFuncAttributeMaxDynamicSharedMemorySize, PERSIST_LDS_MAX);
-    attr_set[layout][hz] = true;
+  const int sb = ka.scale_bf16 ? 1 : 0;
+#define WQ_PFN(L, Z, S) reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, L, D, Z, S>)
+  const void* fns[2][2][2] = {{{WQ_PFN(0, false, false), WQ_PFN(0, false, true)},
+                               {WQ_PFN(0, true, false), WQ_PFN(0, true, true)}},
+                              {{WQ_PFN(1, false, false), WQ_PFN(1, false, true)},
+                               {WQ_PFN(1, true, false), WQ_PFN(1, true, true)}}};
+#undef WQ_PFN
+  const void* fn = fns[layout][hz][sb];
+  static bool attr_set[2][2][2] = {};
+  if (!attr_set[layout][hz][sb]) {
+    hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, PERSIST_LDS_MAX);
+    attr_set[layout][hz][sb] = true;
   }
   int sph_arg = sph, maxrows_arg = maxrows;
   void* args[] = {const_cast<KArgs*>(&ka), &sph_arg, &maxrows_arg};
-  return hipLaunchKernel(fns[layout][hz], dim3(grid), dim3(NT), args, (size_t)lds, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, (size_t)lds, s);
 }
 
 #ifndef WQ_STREAM_ROWS
