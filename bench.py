@@ -56,27 +56,6 @@ def read_traffic(kernel_src):
     return float(m_val.group(1))
 
 
-class Timer:
-    """Per-launch HIP event pairs on the launching (current) stream."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
-
-    def __enter__(self):
-        self.s = self.torch.cuda.Event(enable_timing=True)
-        self.e = self.torch.cuda.Event(enable_timing=True)
-        self.s.record()
-        return self
-
-    def __exit__(self, *exc):
-        self.e.record()
-        self.pairs.append((self.s, self.e))
-
-    def ms(self):
-        return [s.elapsed_time(e) for s, e in self.pairs]
-
-
 def copies_for(nbytes, minimum=2):
     return max(minimum, int((MALL_BYTES * 1.25) // max(nbytes, 1)) + 1)
 
@@ -129,33 +108,50 @@ def main():
     torch.cuda.synchronize()
 
     calls = [(si, c) for si in range(len(sets)) for c in batches]
-    rot = [0]
+    ncopy = min(len(s["copies"]) for s in sets)
 
-    def step(timer=None):
-        for si, c in calls:
-            s = sets[si]
-            pk, sc = s["copies"][rot[0] % len(s["copies"])]
-            rot[0] += 1
-            xc = s["x"][:c]
-            if timer is None:
-                g.wq_gemv_w4(pk, 1, sc, None, 8.0, s["k"], 128, xc, s["out"][:c])
-            else:
-                with timer:
-                    g.wq_gemv_w4(pk, 1, sc, None, 8.0, s["k"], 128, xc, s["out"][:c])
+    def call(si, c, j):
+        s = sets[si]
+        pk, sc = s["copies"][j % len(s["copies"])]
+        g.wq_gemv_w4(pk, 1, sc, None, 8.0, s["k"], 128, s["x"][:c], s["out"][:c])
 
-    for _ in range(args.warmup):
-        step()
+    # One HIP graph per rotation index: a step is the 6 calls, each on its own
+    # weight copy; step i replays graph i % ncopy.  Graph replay removes the
+    # per-launch host and dispatch gaps, which would otherwise be a large part
+    # of a 10 us kernel.
+    def step_eager(i):
+        for t, (si, c) in enumerate(calls):
+            call(si, c, i * len(calls) + t)
+
+    for (si, c) in calls:  # eager first calls: one-time set-up happens outside capture
+        call(si, c, 0)
+    torch.cuda.synchronize()
+    graphs = []
+    cap = torch.cuda.Stream()
+    for j in range(ncopy):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(gr, stream=cap):
+                for t, (si, c) in enumerate(calls):
+                    call(si, c, j * len(calls) + t)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % ncopy].replay()
+        step_eager(i)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    # region timing: no per-launch events inside, so nothing but the kernels
+    # The timed region: K steps launched back to back on the current stream
+    # (what a caller sees), bracketed by events and synchronisations.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step_eager(i)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -166,27 +162,50 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall:.3f} s), "
         f"{value:.1f} GB/s of weights")
 
-    # per-launch durations (separate pass with an event pair around each launch)
-    timer = Timer(torch)
-    for _ in range(args.steps):
-        step(timer)
+    # the same steps replayed from HIP graphs (no host launch gaps)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % ncopy].replay()
+    e1.record()
     torch.cuda.synchronize()
-    durs = np.array(timer.ms()).reshape(args.steps, len(calls))
+    graph_ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    n_launch = len(calls)
+    alg_step = sum(sets[si]["wbytes"] + 2 * sets[si]["k"] * c + 2 * sets[si]["n"] * c
+                   for si, c in calls)
+
+    # per-configuration breakdown: a graph of ncopy launches of one call each
     per_call = {}
-    alg_total, dur_total = 0.0, 0.0
-    for j, (si, c) in enumerate(calls):
+    for (si, c) in calls:
         s = sets[si]
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(gr, stream=cap):
+                for j in range(ncopy):
+                    call(si, c, j)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        d = e0.elapsed_time(e1) / (10 * ncopy)
         alg = s["wbytes"] + 2 * s["k"] * c + 2 * s["n"] * c
-        d = float(np.mean(durs[:, j]))
-        alg_total += alg
-        dur_total += d
         per_call[f"K{s['k']}_N{s['n']}_c{c}"] = {
             "us": round(d * 1e3, 2), "weight_GBs": round(s["wbytes"] / (d * 1e-3) / 1e9, 1),
-            "alg_GBs": round(alg / (d * 1e-3) / 1e9, 1)}
-    n_launch = len(calls)
-    achieved = (alg_total / n_launch) / ((dur_total / n_launch) * 1e-3) / 1e9
+            "alg_GBs": round(alg / (d * 1e-3) / 1e9, 1),
+            "frac_hbm": round(alg / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     traffic = read_traffic(os.path.join(ROOT, "gemm_wq_quantize_amd", "csrc", "gemv_w4.hip"))
     log("per launch:", json.dumps(per_call))
+    # roofline of the kernel: algorithmic bytes of one launch over its average
+    # duration, both averaged over the six configurations of a step
+    avg_launch_ms = sum(v["us"] for v in per_call.values()) / len(per_call) * 1e-3
+    achieved = (alg_step / n_launch) / (avg_launch_ms * 1e-3) / 1e9
 
     rows = {"gemv_w4_decode": per_call}
     if not args.no_rows:
@@ -234,8 +253,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "alg_bytes_per_launch": round(alg_total / n_launch),
-            "avg_launch_us": round(dur_total / n_launch * 1e3, 3),
+            "alg_bytes_per_launch": round(alg_step / n_launch),
+            "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+            "graph_replay_ms_per_step": round(graph_ms_per_step, 5),
         },
         "cpu_baseline": cpu,
         "rows": rows,
@@ -244,16 +264,26 @@ def main():
 
 
 def timed(torch, fn, iters):
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
+    """Average ms per call of fn(i), i = 0..iters-1, captured in one HIP graph
+    and replayed (launch gaps excluded)."""
     fn(0)
     torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(gr, stream=cap):
+            for i in range(iters):
+                fn(i)
+    gr.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
     s.record()
-    for i in range(iters):
-        fn(i)
+    for _ in range(3):
+        gr.replay()
     e.record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / iters  # ms
+    return s.elapsed_time(e) / (3 * iters)  # ms
 
 
 def secondary_rows(g, torch, np, wq_inputs, dev, log):
