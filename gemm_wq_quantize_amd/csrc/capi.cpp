@@ -108,7 +108,7 @@ int wq_gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_
   if (layout != WQ_LAYOUT_PLAIN && layout != WQ_LAYOUT_GFX950) return WQ_EINVAL;
   if (m == 0 || n == 0) return WQ_OK;
   if (!a || !b || !scales || !c_out) return WQ_EINVAL;
-  if (k == 0 || k % 64 != 0) return WQ_ESHAPE;
+  if (k == 0 || k % 64 != 0 || k > (int64_t(1) << 22)) return WQ_ESHAPE;  // 32-bit tile offsets
   if (layout != WQ_LAYOUT_GFX950 || group != k) return WQ_EUNSUPPORTED;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c_out, 16) || !aligned(scales, 2))
     return WQ_EALIGN;

@@ -138,7 +138,7 @@ int wq_gemv_w4(const uint8_t* packed, int layout, const void* scales, int scale_
  *   b       [n][k/2] uint8 in `layout` (WQ_LAYOUT_GFX950 only).
  *   scales  [n] bf16 (group must equal k).
  *   c_out   [m][n] bf16 (RNE of the float32 accumulator).
- * Requires k % 64 == 0; a, b and c_out 16-byte aligned, scales 2-byte
+ * Requires k % 64 == 0 and k <= 2^22; a, b and c_out 16-byte aligned, scales 2-byte
  * aligned.  Any m and n (ragged tiles are masked).  Every zero_const is
  * exact for integer zero points (|q - z| <= 15 is a bf16 integer); other
  * values are rounded to bf16 per weight.
