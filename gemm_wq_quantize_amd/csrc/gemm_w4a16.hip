@@ -9,11 +9,17 @@
 //
 // Tiling.  A 256-lane workgroup computes a 256 x 256 tile of C with four
 // waves in a 2 x 2 grid; each wave owns 128 x 128 = 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16.  K advances 64 per step through a two-stage LDS
-// ring: the next step's A (256 x 64 bf16) and packed B (256 x 32 bytes) are
-// fetched with buffer loads into registers while the current step's MFMAs
-// run, then written to the other LDS stage.  B stays packed in LDS (4x less
-// LDS traffic than a bf16 tile).
+// v_mfma_f32_32x32x16_bf16.  K advances 64 per step through a three-stage LDS
+// ring filled by buffer loads that write LDS directly (no register staging):
+// while step t is multiplied, steps t+1 and t+2 are in flight, so one step of
+// MFMA work (about 0.85 us) never has to cover a whole memory latency.  B
+// stays packed in LDS (4x less LDS traffic than a bf16 tile).
+//
+// K order inside a 64-k step.  The MFMA sums over its 16 k slots in any
+// order, so A and B only have to agree on which k each slot holds.  Lane
+// half h of 16-k step s takes the 8 k of chunk 4h + s (chunk = 8 consecutive
+// k = one packed B word = 16 bytes of A).  A lane then needs the four packed
+// B words 4h .. 4h+3 of a row over the whole step: one ds_read_b128.
 //
 // Dequantisation.  One 32-bit B word is exactly the 8 consecutive k one lane
 // feeds to the MFMA.  Each bf16 pair (128 + q_{2j}, 128 + q_{2j+1}) comes out
@@ -30,15 +36,14 @@
 namespace wq {
 namespace {
 
-#ifndef WQ_G_UNROLL
-#define WQ_G_UNROLL 2  // unroll of the 16-k steps inside one LDS stage
-#endif
-#define WQ_PRAGMA(x) _Pragma(#x)
-#define WQ_UNROLL(n) WQ_PRAGMA(unroll n)
-
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int A_LD = BK + 8;   // bf16 elements per LDS row of A (16-byte pad)
-constexpr int B_LDW = BK / 8;  // 32-bit words per LDS row of packed B
+constexpr int NSTAGE = 3;
+constexpr int A_STAGE = BM * BK * 2;          // bytes: 256 rows x 128 B
+constexpr int B_STAGE = BN * BK / 2;          // bytes: 256 rows x 32 B
+constexpr int STAGE = A_STAGE + B_STAGE;      // 40 KiB
+constexpr int LOADS_PER_STAGE = (STAGE / 16) / 256;  // 16-byte loads per lane: 10
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 struct GArgs {
   const uint16_t* a;
@@ -73,14 +78,48 @@ __device__ __forceinline__ bf16x8 unpack8(uint32_t w, uint32_t magic_v) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// LDS word position of packed-B word `wd` of tile row `n` (XOR swizzle so
-// the 32 rows one MFMA operand read touches fall in distinct banks).
-__device__ __forceinline__ int b_slot(int n, int wd) { return n * B_LDW + (wd ^ ((n >> 2) & 7)); }
+// Buffer descriptor in SGPRs: raw (stride 0), num_records bytes; offsets at
+// or past num_records read as zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+  r[3] = 0x00020000;
+  return r;
+}
 
-__global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * A_LD];
-  __shared__ __attribute__((aligned(16))) uint32_t sb[2][BN * B_LDW];
+// 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane
+// (lds_base wave-uniform).  Issued from asm so that the compiler does not
+// wait for these loads before every LDS read; completion is awaited with
+// explicit vmcnt waits below.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
 
+// A-tile swizzle: physical 16-byte column of k-chunk c in row r is c ^ swz(r)
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+#ifndef WQ_G_SCHED
+#define WQ_G_SCHED 1  // 1: interleave MFMA / VALU / LDS reads with scheduling-group barriers
+#endif
+
+// One workgroup tile.  WN (the wave's column half) is a template argument so
+// that the row-sum split below indexes fragments at compile time.
+template <int WN>
+__device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (*rsx)[4][32]) {
   // ---- tile order: XCD-aware renumbering, then bands of 8 tile-rows
   const int nwg = p.tiles_m * p.tiles_n;
   int id = blockIdx.x;
@@ -94,50 +133,46 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int rows_a = (int)min((int64_t)BM, p.m - m0);
   const int rows_b = (int)min((int64_t)BN, p.n - n0);
-  const int kbytes_a = (int)(p.k * 2);   // bytes per A row
-  const int kbytes_b = (int)(p.k / 2);   // bytes per packed B row
+  const uint32_t kbytes_a = (uint32_t)(p.k * 2);   // bytes per A row
+  const uint32_t kbytes_b = (uint32_t)(p.k / 2);   // bytes per packed B row
 
-  // buffer descriptors over this tile's rows; rows past M / N read as zero
-  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.a + m0 * p.k), 0, rows_a * kbytes_a, 0x00020000);
-  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.b + n0 * (p.k / 2)), 0, rows_b * kbytes_b, 0x00020000);
+  // descriptors over this tile's rows; rows past M / N read as zero
+  const i32x4 ars = make_rsrc(p.a + m0 * p.k, (uint32_t)rows_a * kbytes_a);
+  const i32x4 brs = make_rsrc(p.b + n0 * (p.k / 2), (uint32_t)rows_b * kbytes_b);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
-  // global -> register staging: A unit u = tid + 256 i (row u/8, 16 B chunk
-  // u%8); B unit u = tid + 256 i (row u/2, half u%2)
-  const int a_off0 = (tid >> 3) * kbytes_a + (tid & 7) * 16;  // + i * 32 rows
-  const int b_off0 = (tid >> 1) * kbytes_b + (tid & 1) * 16;  // + i * 128 rows
+  // ---- global -> LDS assignment.  Load i (0..7) of wave w fills A slots
+  // (16 B each) s = 64 (4 i + w) + lane: row s / 8, slot column s % 8
+  // holding k-chunk (s % 8) ^ swz(row).  The LDS serves 16 lanes of a
+  // ds_read_b128 per cycle from 64 banks; the 16 rows those lanes read
+  // (same chunk) then fall on 16 distinct 16-byte bank groups.  Loads 8, 9
+  // fill B slots laid out [half][row]: half h = load - 8, row 64 w + lane.
+  uint32_t a_voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = (i * 4 + wave) * 64 + lane;
+    const int row = s >> 3, chunk = (s & 7) ^ swz(row);
+    a_voff[i] = (uint32_t)row * kbytes_a + (uint32_t)chunk * 16;
+  }
+  const uint32_t b_voff = (uint32_t)(wave * 64 + lane) * kbytes_b;
 
-  uint4 ra[8], rb[2];
-  auto gload = [&](int kt) {
-    const int ka = kt * BK * 2, kb = kt * BK / 2;
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (uint32_t)(kt % NSTAGE) * STAGE;
+    const uint32_t ka = (uint32_t)kt * (BK * 2), kb = (uint32_t)kt * (BK / 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                  ars, a_off0 + i * 32 * kbytes_a + ka, 0, 0));
+      dma16(ars, a_voff[i] + ka,
+            __builtin_amdgcn_readfirstlane(st + (uint32_t)(i * 4 + wave) * 1024));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                  brs, b_off0 + i * 128 * kbytes_b + kb, 0, 0));
-  };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 3) + 32 * i, cu = tid & 7;
-      *reinterpret_cast<uint4*>(&sa[st][row * A_LD + cu * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (tid >> 1) + 128 * i, half = tid & 1;
-      const uint32_t v4[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sb[st][b_slot(row, half * 4 + q)] = v4[q];
-    }
+    for (int h = 0; h < 2; ++h)
+      dma16(brs, b_voff + kb + (uint32_t)h * 16,
+            __builtin_amdgcn_readfirstlane(st + A_STAGE + (uint32_t)h * (BN * 16) +
+                                           (uint32_t)wave * 1024));
   };
 
   floatx16 acc[4][4];
@@ -147,67 +182,102 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  float rs[4] = {0.f, 0.f, 0.f, 0.f};  // partial row sums of A (row lane%32, k half lane/32)
+  // Row sums of A: this wave sums row blocks 2 WN and 2 WN + 1 only (the
+  // wave of the other column half sums the other two); lane l holds row
+  // l%32's partial over k half l/32.
+  float rs[2] = {0.f, 0.f};
 
   const int nk = (int)(p.k / BK);
   const int lr = lane & 31;   // operand row (A) / column (B) within a 32-block
-  const int lh = lane >> 5;   // which 8-k half of the 16-k step
+  const int lh = lane >> 5;   // k half: chunks 4 lh .. 4 lh + 3 of every step
   const uint32_t magic_v = vconst(0x43004300u);
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // LDS byte offsets (within a stage) of this lane's operands
+  int a_rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_rd[i] = (wm * 128 + i * 32 + lr) * 128;
+  const int a_sw = swz(lr);  // == swz(row) for all four rows
+  int b_rd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b_rd[j] = A_STAGE + lh * (BN * 16) + (WN * 128 + j * 32 + lr) * 16;
+
+  issue(0);
+  if (nk > 1) issue(1);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    WQ_UNROLL(WQ_G_UNROLL)
+    // this step's loads are done once only the next step's remain in flight
+    if (kt + 1 < nk) wait_vmcnt<LOADS_PER_STAGE>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's share landed; stage (kt+2)%3 is free
+    if (kt + 2 < nk) issue(kt + 2);
+
+    const uint8_t* st = smem + (kt % NSTAGE) * STAGE;
+    uint4 bw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bw[j] = *reinterpret_cast<const uint4*>(st + b_rd[j]);
+#pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
+      const int chunk = lh * 4 + ks;
       bf16x8 af[4], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + lr;
-        af[i] = *reinterpret_cast<const bf16x8*>(&sa[st][row * A_LD + ks * 16 + lh * 8]);
-      }
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(st + a_rd[i] + ((chunk ^ a_sw) << 4));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = wn * 128 + j * 32 + lr;
-        bfr[j] = unpack8(sb[st][b_slot(row, ks * 2 + lh)], magic_v);
+        const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
+        bfr[j] = unpack8(w, magic_v);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int ii = 0; ii < 2; ++ii) {
+        const bf16x8 x = af[2 * WN + ii];
         // (pairs taken with shufflevector: extracting lanes of a bit-cast
         // u32x4 was folded onto the first dword by this compiler)
-        float t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(af[i], af[i], 0, 1), ones, rs[i], false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(af[i], af[i], 2, 3), ones, t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(af[i], af[i], 4, 5), ones, t, false);
-        rs[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(af[i], af[i], 6, 7), ones, t, false);
+        float t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, rs[ii], false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, t, false);
+        rs[ii] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, t, false);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+#if WQ_G_SCHED
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+        if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+#endif
     }
-    if (kt + 1 < nk) lstore(st ^ 1);
-    __syncthreads();
   }
+
+  // ---- row sums: complete the k halves, swap halves of the row blocks
+  // with the other column half's wave through LDS.
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii) {
+    rs[ii] += __shfl_xor(rs[ii], 32);
+    if (lh == 0) rsx[wm][2 * WN + ii][lr] = rs[ii];
+  }
+  __syncthreads();
 
   // ---- epilogue: fold out the offset, scale per column, bf16 RNE, store.
   // Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  // Row sums: lane l holds row l%32's partial over its k half; add the other half.
   const float zb = 128.f + p.zero_const;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) rs[i] += __shfl_xor(rs[i], 32);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float rsum[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) rsum[e] = __shfl(rs[i], 8 * (e / 4) + 4 * lh + (e % 4));
+    for (int g = 0; g < 4; ++g) {
+      const floatx4 v = *reinterpret_cast<const floatx4*>(&rsx[wm][i][8 * g + 4 * lh]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rsum[4 * g + e] = v[e];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + lr;
+      const int64_t col = n0 + WN * 128 + j * 32 + lr;
       const bool cok = col < p.n;
       const float s = cok ? bf16_to_f32(p.scales[col]) : 0.f;
 #pragma unroll
@@ -218,6 +288,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  __shared__ __attribute__((aligned(16))) float rsx[2][4][32];  // row sums [wm][row block][row]
+  // wave-uniform branch (the wave index is moved to a scalar register)
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1>(p, smem, rsx);
+  else gemm_tile<0>(p, smem, rsx);
 }
 
 }  // namespace
