@@ -116,6 +116,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 #define WQ_G_SCHED 1  // 1: interleave MFMA / VALU / LDS reads with scheduling-group barriers
 #endif
 
+// Epilogue staging: half the tile (128 rows x 256 bf16) at a time, rows
+// padded by 16 bytes so that the two rows one 2-byte LDS write touches (4
+// apart) fall in different banks.
+constexpr int C_PITCH = BN * 2 + 16;
+static_assert(128 * C_PITCH <= NSTAGE * STAGE, "epilogue staging fits the ring");
+
 // One workgroup tile.  WN (the wave's column half) is a template argument so
 // that the row-sum split below indexes fragments at compile time.
 template <int WN>
@@ -160,10 +166,17 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     a_voff[i] = (uint32_t)row * kbytes_a + (uint32_t)chunk * 16;
   }
   const uint32_t b_voff = (uint32_t)(wave * 64 + lane) * kbytes_b;
+  const int nk = (int)(p.k / BK);
 
+  // Step kt's loads into stage kt % 3.  Steps past the end are issued too
+  // (the loop then has no branch) but at offset 2^31 or more, which is past
+  // num_records: they read nothing from memory and fill an unused stage with
+  // zeros.
   auto issue = [&](int kt) {
     const uint32_t st = lds0 + (uint32_t)(kt % NSTAGE) * STAGE;
-    const uint32_t ka = (uint32_t)kt * (BK * 2), kb = (uint32_t)kt * (BK / 2);
+    const bool live = kt < nk;
+    const uint32_t ka = live ? (uint32_t)kt * (BK * 2) : 0x80000000u;
+    const uint32_t kb = live ? (uint32_t)kt * (BK / 2) : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       dma16(ars, a_voff[i] + ka,
@@ -187,7 +200,6 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // l%32's partial over k half l/32.
   float rs[2] = {0.f, 0.f};
 
-  const int nk = (int)(p.k / BK);
   const int lr = lane & 31;   // operand row (A) / column (B) within a 32-block
   const int lh = lane >> 5;   // k half: chunks 4 lh .. 4 lh + 3 of every step
   const uint32_t magic_v = vconst(0x43004300u);
@@ -202,57 +214,83 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
   for (int j = 0; j < 4; ++j) b_rd[j] = A_STAGE + lh * (BN * 16) + (WN * 128 + j * 32 + lr) * 16;
 
-  issue(0);
-  if (nk > 1) issue(1);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // this step's loads are done once only the next step's remain in flight
-    if (kt + 1 < nk) wait_vmcnt<LOADS_PER_STAGE>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // every wave's share landed; stage (kt+2)%3 is free
-    if (kt + 2 < nk) issue(kt + 2);
-
+  auto read_b = [&](int kt, uint4 (&bw)[4]) {
     const uint8_t* st = smem + (kt % NSTAGE) * STAGE;
-    uint4 bw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bw[j] = *reinterpret_cast<const uint4*>(st + b_rd[j]);
+  };
+  auto read_a = [&](int kt, int ks, bf16x8 (&af)[4]) {
+    const uint8_t* st = smem + (kt % NSTAGE) * STAGE;
+    const int chunk = lh * 4 + ks;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int chunk = lh * 4 + ks;
-      bf16x8 af[4], bfr[4];
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(st + a_rd[i] + ((chunk ^ a_sw) << 4));
+  };
+  auto compute = [&](const bf16x8 (&af)[4], const uint4 (&bw)[4], int ks) {
+    bf16x8 bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(st + a_rd[i] + ((chunk ^ a_sw) << 4));
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
+      bfr[j] = unpack8(w, magic_v);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
-        bfr[j] = unpack8(w, magic_v);
-      }
+    for (int ii = 0; ii < 2; ++ii) {
+      const bf16x8 x = af[2 * WN + ii];
+      // (pairs taken with shufflevector: extracting lanes of a bit-cast
+      // u32x4 was folded onto the first dword by this compiler)
+      float t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, rs[ii], false);
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, t, false);
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, t, false);
+      rs[ii] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, t, false);
+    }
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const bf16x8 x = af[2 * WN + ii];
-        // (pairs taken with shufflevector: extracting lanes of a bit-cast
-        // u32x4 was folded onto the first dword by this compiler)
-        float t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, rs[ii], false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, t, false);
-        rs[ii] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, t, false);
-      }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
 #if WQ_G_SCHED
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
-        if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      }
-#endif
+    for (int t = 0; t < 16; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+      if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
+#endif
+  };
+
+  // ---- main loop.  Barrier b(t) publishes stage t (its loads landed) and
+  // frees stage t - 1 (every wave has read it), after which step t + 2 is
+  // issued into it.  b(t + 1) sits before the last 16-k group of step t, so
+  // that step t + 1's first operands are read while that group multiplies.
+  issue(0);
+  issue(1);
+  wait_vmcnt<LOADS_PER_STAGE>();
+  __syncthreads();
+  issue(2);
+  uint4 bw[4];
+  bf16x8 a0[4], a1[4];
+  read_b(0, bw);
+  read_a(0, 0, a0);
+  for (int kt = 0; kt < nk; ++kt) {
+    read_a(kt, 1, a1);
+    compute(a0, bw, 0);
+    read_a(kt, 2, a0);
+    compute(a1, bw, 1);
+    read_a(kt, 3, a1);
+    compute(a0, bw, 2);
+    // a1 holds the last operands read from stage kt (the barrier's release
+    // waits for them); stage kt + 1 landed once only step kt + 2 is in flight
+    wait_vmcnt<LOADS_PER_STAGE>();
+    __syncthreads();
+    issue(kt + 3);
+    uint4 bn[4];
+    read_b(kt + 1, bn);
+    read_a(kt + 1, 0, a0);
+    compute(a1, bw, 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bw[j] = bn[j];
   }
+  wait_vmcnt<0>();  // no load may still be writing LDS below
 
   // ---- row sums: complete the k halves, swap halves of the row blocks
   // with the other column half's wave through LDS.
@@ -261,32 +299,63 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     rs[ii] += __shfl_xor(rs[ii], 32);
     if (lh == 0) rsx[wm][2 * WN + ii][lr] = rs[ii];
   }
-  __syncthreads();
+  __syncthreads();  // also: every wave is done with the ring
 
-  // ---- epilogue: fold out the offset, scale per column, bf16 RNE, store.
+  // ---- epilogue: fold out the offset, scale per column, bf16 RNE; stage
+  // half the tile in LDS, then write it with coalesced 16-byte stores.
   // Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
   const float zb = 128.f + p.zero_const;
+  float sc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float rsum[16];
+  for (int j = 0; j < 4; ++j) {
+    const int64_t col = n0 + WN * 128 + j * 32 + lr;
+    sc[j] = col < p.n ? bf16_to_f32(p.scales[col]) : 0.f;
+  }
+  const bool vec_ok = (p.n & 7) == 0;  // rows 16-byte aligned
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const floatx4 v = *reinterpret_cast<const floatx4*>(&rsx[wm][i][8 * g + 4 * lh]);
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rsum[4 * g + e] = v[e];
-    }
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * half + ii;
+      float rsum[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + WN * 128 + j * 32 + lr;
-      const bool cok = col < p.n;
-      const float s = cok ? bf16_to_f32(p.scales[col]) : 0.f;
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 v = *reinterpret_cast<const floatx4*>(&rsx[wm][i][8 * g + 4 * lh]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
-        const float v = (acc[i][j][e] - zb * rsum[e]) * s;
-        if (cok && row < p.m) p.c[row * p.n + col] = (uint16_t)f32_to_bf16_rne(v);
+        for (int e = 0; e < 4; ++e) rsum[4 * g + e] = v[e];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = WN * 128 + j * 32 + lr;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          // staged row: 64 wm + 32 ii + local row
+          const int srow = wm * 64 + ii * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
+          const float v = (acc[i][j][e] - zb * rsum[e]) * sc[j];
+          *reinterpret_cast<uint16_t*>(smem + srow * C_PITCH + col * 2) =
+              (uint16_t)f32_to_bf16_rne(v);
+        }
       }
     }
+    __syncthreads();
+    // 128 staged rows x 32 chunks of 16 B; thread t takes chunks t + 256 u
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int q = tid + 256 * u;
+      const int srow = q >> 5, cch = q & 31;
+      const int64_t row = m0 + (srow >> 6) * 128 + half * 64 + (srow & 63);
+      const int64_t col = n0 + cch * 8;
+      if (row >= p.m || col >= p.n) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + srow * C_PITCH + cch * 16);
+      uint16_t* dst = p.c + row * p.n + col;
+      if (vec_ok && col + 8 <= p.n) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int t = 0; t < 8 && col + t < p.n; ++t) dst[t] = (uint16_t)(w[t / 2] >> (16 * (t % 2)));
+      }
+    }
+    if (half == 0) __syncthreads();  // staging is rewritten by the second half
   }
 }
 
