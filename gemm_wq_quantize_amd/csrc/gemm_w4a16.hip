@@ -93,9 +93,12 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_record
 // 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane
 // (lds_base wave-uniform).  Issued from asm so that the compiler does not
 // wait for these loads before every LDS read; completion is awaited with
-// explicit vmcnt waits below.
+// explicit vmcnt waits below.  The compiler's hazard checks do not look
+// inside asm, so the asm keeps its own: one wait state between the M0 write
+// and the LDS-DMA load that reads M0.  (No other code in these kernels uses
+// M0, so clobbering it is safe.)
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(lds_base)
                : "memory", "m0");
@@ -165,27 +168,50 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     const int row = s >> 3, chunk = (s & 7) ^ swz(row);
     a_voff[i] = (uint32_t)row * kbytes_a + (uint32_t)chunk * 16;
   }
-  const uint32_t b_voff = (uint32_t)(wave * 64 + lane) * kbytes_b;
+  // B load h of wave w fills slots 64 (4 h + w) + lane of the B stage laid
+  // out [row][half ^ ((row / 8) % 2)] (16 B each): row s / 2, stored half
+  // s % 2.  The half swap keeps the 16 rows one B read touches in distinct
+  // bank groups.
+  uint32_t b_voff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int s = (h * 4 + wave) * 64 + lane;
+    const int row = s >> 1, half = (s & 1) ^ ((row >> 3) & 1);
+    b_voff[h] = (uint32_t)row * kbytes_b + (uint32_t)half * 16;
+  }
   const int nk = (int)(p.k / BK);
 
   // Step kt's loads into stage kt % 3.  Steps past the end are issued too
   // (the loop then has no branch) but at offset 2^31 or more, which is past
   // num_records: they read nothing from memory and fill an unused stage with
   // zeros.
-  auto issue = [&](int kt) {
+  // loads [first, last) of step kt: 0..7 are A, 8 and 9 are B
+  auto issue_part = [&](int kt, int first, int last) {
     const uint32_t st = lds0 + (uint32_t)(kt % NSTAGE) * STAGE;
     const bool live = kt < nk;
     const uint32_t ka = live ? (uint32_t)kt * (BK * 2) : 0x80000000u;
     const uint32_t kb = live ? (uint32_t)kt * (BK / 2) : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      dma16(ars, a_voff[i] + ka,
-            __builtin_amdgcn_readfirstlane(st + (uint32_t)(i * 4 + wave) * 1024));
+      if (i >= first && i < last)
+        dma16(ars, a_voff[i] + ka,
+              __builtin_amdgcn_readfirstlane(st + (uint32_t)(i * 4 + wave) * 1024));
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      dma16(brs, b_voff + kb + (uint32_t)h * 16,
-            __builtin_amdgcn_readfirstlane(st + A_STAGE + (uint32_t)h * (BN * 16) +
-                                           (uint32_t)wave * 1024));
+      if (8 + h >= first && 8 + h < last)
+        dma16(brs, b_voff[h] + kb,
+              __builtin_amdgcn_readfirstlane(st + A_STAGE + (uint32_t)(h * 4 + wave) * 1024));
+  };
+  auto issue = [&](int kt) { issue_part(kt, 0, LOADS_PER_STAGE); };
+  // Every group of loads inside the loop sits between full scheduling
+  // barriers.  Without them, the scheduling-group ordering in compute()
+  // (sched_group_barrier) let this compiler move code across the asm loads
+  // such that some tiles came out wrong; with them the loads keep their
+  // place in program order.
+  auto issue_fenced = [&](int kt, int first, int last) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_part(kt, first, last);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   floatx16 acc[4][4];
@@ -198,7 +224,9 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // Row sums of A: this wave sums row blocks 2 WN and 2 WN + 1 only (the
   // wave of the other column half sums the other two); lane l holds row
   // l%32's partial over k half l/32.
-  float rs[2] = {0.f, 0.f};
+  // Four independent accumulators per block: a chain of dependent v_dot2
+  // would stall this wave's in-order issue, MFMAs included.
+  float rsq[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
   const int lr = lane & 31;   // operand row (A) / column (B) within a 32-block
   const int lh = lane >> 5;   // k half: chunks 4 lh .. 4 lh + 3 of every step
@@ -212,7 +240,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   const int a_sw = swz(lr);  // == swz(row) for all four rows
   int b_rd[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b_rd[j] = A_STAGE + lh * (BN * 16) + (WN * 128 + j * 32 + lr) * 16;
+  for (int j = 0; j < 4; ++j) {
+    const int n = WN * 128 + j * 32 + lr;
+    b_rd[j] = A_STAGE + (n * 2 + (lh ^ ((lr >> 3) & 1))) * 16;
+  }
 
   auto read_b = [&](int kt, uint4 (&bw)[4]) {
     const uint8_t* st = smem + (kt % NSTAGE) * STAGE;
@@ -238,10 +269,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
       const bf16x8 x = af[2 * WN + ii];
       // (pairs taken with shufflevector: extracting lanes of a bit-cast
       // u32x4 was folded onto the first dword by this compiler)
-      float t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, rs[ii], false);
-      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, t, false);
-      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, t, false);
-      rs[ii] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, t, false);
+      rsq[ii][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, rsq[ii][0], false);
+      rsq[ii][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, rsq[ii][1], false);
+      rsq[ii][2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, rsq[ii][2], false);
+      rsq[ii][3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, rsq[ii][3], false);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -262,11 +293,17 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // frees stage t - 1 (every wave has read it), after which step t + 2 is
   // issued into it.  b(t + 1) sits before the last 16-k group of step t, so
   // that step t + 1's first operands are read while that group multiplies.
+  // Step t's loads go out in three groups: 0-3 right after b(t - 2), 4-6
+  // and 7-9 between the 16-k groups of step t - 2 (a burst of ten would
+  // stall this wave's MFMA issue).  All ten loads of step t + 2 precede the
+  // wait before b(t + 1), so that wait (at most ten loads in flight) covers
+  // step t + 1.
+  asm volatile("s_nop 4");  // VALU-written SGPRs (descriptors) read by the first loads
   issue(0);
   issue(1);
   wait_vmcnt<LOADS_PER_STAGE>();
   __syncthreads();
-  issue(2);
+  issue_fenced(2, 0, 4);
   uint4 bw[4];
   bf16x8 a0[4], a1[4];
   read_b(0, bw);
@@ -274,15 +311,17 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   for (int kt = 0; kt < nk; ++kt) {
     read_a(kt, 1, a1);
     compute(a0, bw, 0);
+    issue_fenced(kt + 2, 4, 7);
     read_a(kt, 2, a0);
     compute(a1, bw, 1);
+    issue_fenced(kt + 2, 7, 10);
     read_a(kt, 3, a1);
     compute(a0, bw, 2);
     // a1 holds the last operands read from stage kt (the barrier's release
     // waits for them); stage kt + 1 landed once only step kt + 2 is in flight
     wait_vmcnt<LOADS_PER_STAGE>();
     __syncthreads();
-    issue(kt + 3);
+    issue_fenced(kt + 3, 0, 4);
     uint4 bn[4];
     read_b(kt + 1, bn);
     read_a(kt + 1, 0, a0);
@@ -296,8 +335,9 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // with the other column half's wave through LDS.
 #pragma unroll
   for (int ii = 0; ii < 2; ++ii) {
-    rs[ii] += __shfl_xor(rs[ii], 32);
-    if (lh == 0) rsx[wm][2 * WN + ii][lr] = rs[ii];
+    float r = (rsq[ii][0] + rsq[ii][1]) + (rsq[ii][2] + rsq[ii][3]);
+    r += __shfl_xor(r, 32);
+    if (lh == 0) rsx[wm][2 * WN + ii][lr] = r;
   }
   __syncthreads();  // also: every wave is done with the ring
 

@@ -36,7 +36,7 @@ def run(a_bits, codes, scale_bits, zc=8.0):
 
 
 @pytest.mark.parametrize("m,n,k", [(300, 520, 512), (256, 256, 64), (64, 8, 128), (1, 1000, 192),
-                                   (513, 257, 1088)])
+                                   (513, 257, 1088), (320, 640, 256), (200, 300, 704)])
 def test_gemm_ragged(m, n, k):
     say("gemm", m, n, k)
     p = wq_inputs.large_gemm(m, n, k, n_rows=m, seed=m + n)
