@@ -78,7 +78,8 @@ int wq_gemv_w4(const uint8_t* packed, int layout, const void* scales, int scale_
   if (out_dtype != WQ_F32 && out_dtype != WQ_BF16) return WQ_EINVAL;
   if (n == 0 || c == 0) return WQ_OK;
   if (!packed || !scales || !x || !out) return WQ_EINVAL;
-  if (k == 0 || k % 32 != 0 || !valid_group(group, k) || c > 32) return WQ_ESHAPE;
+  if (k == 0 || k % 32 != 0 || k > (int64_t(1) << 24) || !valid_group(group, k) || c > 32)
+    return WQ_ESHAPE;  // k bound: 32-bit buffer offsets in every kernel
   if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(scales, dtype_size(scale_dtype)) ||
       (zeros && !aligned(zeros, dtype_size(scale_dtype))) || !aligned(out, dtype_size(out_dtype)))
     return WQ_EALIGN;

@@ -706,6 +706,279 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
   }
 }
 
+// Wide-batch variant for bf16 activations (c = 5..32, in passes of at most
+// 16 columns).  The work per weight byte grows with c, so this path is bound
+// by the VALU (two MACs per v_dot2) rather than by HBM, and the kernel is laid
+// out to keep the dot2 issue rate up:
+//  * a wave owns 4 consecutive rows and a lane one chunk of 32 k of a 2048-k
+//    tile, so each x fragment a lane reads from LDS feeds 4 rows (1 byte of
+//    LDS per dot2) and 4 x 16 accumulators give plenty of independent work;
+//  * a workgroup (4 waves) covers 16 rows, which leaves >= 256 workgroups
+//    at the small-batch shapes;
+//  * x is double-buffered in LDS per tile and filled by buffer loads that
+//    write LDS directly; each lane then sums the chunks it loaded itself
+//    (the per-chunk sums of x), so one barrier per tile suffices;
+//  * weights and scales run two tiles ahead in a register ring, issued
+//    without branches (past-the-end offsets read zero);
+//  * after the last tile each wave sums its 64 lanes with DPP in a fixed
+//    order.
+// Load order per tile t: consume weights of t, x of t + 1 (to LDS), weights
+// of t + 2.  The compiler's own wait before consuming the weights of t + 1
+// then covers only the weights of t + 2 -- it cannot see the x loads, which
+// are explicit asm -- and the explicit wait for x of t + 1 leaves exactly the
+// weights of t + 2 in flight.
+constexpr int BT_CH = 64;   // chunks per batch tile
+constexpr int BT_RW = 4;    // rows per wave
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = halfwave_sum(v);  // half totals in lanes 16..31 and 48..63
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast 31
+  return v;  // total in lanes 48..63
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor in SGPRs (offsets at or past num_records read 0).
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane
+// (lds_base wave-uniform).  Explicit asm, so the compiler neither counts nor
+// waits for it; callers wait with wait_vmcnt.  One wait state separates the
+// M0 write from the load that reads M0 (the compiler's hazard checks do not
+// see inside asm); no other code in this file uses M0.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int C, int LAYOUT, bool HZ, bool SBF>
+__global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) {
+  static_assert(C % 4 == 0 && C <= 16, "columns per pass");
+  constexpr int XC = C / 4;                              // x columns per wave and tile
+  constexpr int WLOADS = BT_RW * (HZ ? 3 : 2);           // loads per lane per weight tile
+  constexpr int RG = 4 * BT_RW;                          // rows per row-group (workgroup item)
+  __shared__ __attribute__((aligned(16))) uint4 xs[2][C * 4 * BT_CH];  // [buf][col][piece][chunk]
+  __shared__ float sxs[2][C * BT_CH];                    // [buf][col][chunk]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nchunks = (int)(p.k / 32);
+  const int nt = (nchunks + BT_CH - 1) / BT_CH;
+  const int rowbytes = (int)(p.k / 2);
+  const int ngroups = p.gshift < 0 ? 1 : (nchunks >> p.gshift);
+  constexpr int ESZ = SBF ? 2 : 4;
+  // persistent: workgroup w takes row-groups w, w + G, w + 2G, ...; its items
+  // are (row-group, tile) in that order
+  const int G = gridDim.x, w = blockIdx.x;
+  const int nrg = (int)((p.n + RG - 1) / RG);
+  const int nitems = (nrg > w ? (nrg - w + G - 1) / G : 0) * nt;
+
+  const i32x4 xrs = sgpr_rsrc(p.x, (uint32_t)(p.c * p.k * 2));
+  const uint32_t lds_x = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)&xs[0][0];
+
+  // ---- weight ring: item i in slot i % 2.  Descriptors cover the wave's 4
+  // rows of the item's row-group (none for items past the end).
+  uint4 wv[2][BT_RW];
+  float sc[2][BT_RW], zb[2][BT_RW];
+  auto issue_w = [&](int slot, int i) {
+    const int t = i % nt, rg = w + (i / nt) * G;
+    const int64_t r0 = (int64_t)rg * RG + wave * BT_RW;
+    const int wrows = i < nitems ? (int)max<int64_t>(0, min<int64_t>(BT_RW, p.n - r0)) : 0;
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.packed + r0 * rowbytes), 0, wrows * rowbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)p.scales + r0 * ngroups * ESZ), 0, wrows * ngroups * ESZ, 0x00020000);
+    const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)(HZ ? p.zeros : p.scales) + r0 * ngroups * ESZ), 0,
+        HZ ? wrows * ngroups * ESZ : 0, 0x00020000);
+    const int ch = t * BT_CH + lane;
+    const bool ok = ch < nchunks;
+    const int g = p.gshift < 0 ? 0 : (ch >> p.gshift);
+#pragma unroll
+    for (int r = 0; r < BT_RW; ++r) {
+      const uint32_t wo = ok ? (uint32_t)(r * rowbytes + ch * 16) : OOB;
+      const uint32_t so = ok ? (uint32_t)((r * ngroups + g) * ESZ) : OOB;
+      wv[slot][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wo, 0, 0));
+      float sv, zv = p.zero_const;
+      if (SBF) {
+        sv = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(srs, (int)so, 0, 0));
+        if (HZ) zv = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(zrs, (int)so, 0, 0));
+      } else {
+        sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, (int)so, 0, 0));
+        if (HZ) zv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zrs, (int)so, 0, 0));
+      }
+      sc[slot][r] = sv;  // 0 past the end: the item contributes nothing
+      zb[slot][r] = 128.f + zv;
+    }
+  };
+
+  // ---- x of item i's tile into buffer b: this wave fills chunk `lane` of
+  // columns wave + 4 j, all four 16-byte pieces (a wave instruction writes
+  // 64 consecutive 16-byte slots: one [col][piece] row of the buffer)
+  auto dma_x = [&](int i, int b) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 4");  // VALU-written SGPRs (descriptor, LDS bases) read by the loads
+    const int ch = (i % nt) * BT_CH + lane;
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      const int col = wave + 4 * j;
+      const bool ok = i < nitems && ch < nchunks && col < p.c;
+      // (OOB + 48 is still past num_records, which is below 2^31)
+      const uint32_t base = ok ? (uint32_t)(((int64_t)col * p.k + (int64_t)ch * 32) * 2) : OOB;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dma16(xrs, base + q * 16,
+              __builtin_amdgcn_readfirstlane(lds_x + (uint32_t)(((b * C + col) * 4 + q) * BT_CH * 16)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // per-chunk sums of the x this lane loaded (its own loads have landed).
+  // Without per-group zeros the stored value is already the offset term
+  // -(128 + z) * sum x that starts every dot2 chain of the chunk.
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  const float xz = HZ ? 1.f : -(128.f + p.zero_const);
+  auto sum_x = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      const int col = wave + 4 * j;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = xs[b][(col * 4 + q) * BT_CH + lane];
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), ones, s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), ones, s1, false);
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), ones, s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), ones, s1, false);
+      }
+      sxs[b][col * BT_CH + lane] = (s0 + s1) * xz;
+    }
+  };
+
+  float acc[BT_RW][C];
+#pragma unroll
+  for (int r = 0; r < BT_RW; ++r)
+#pragma unroll
+    for (int j = 0; j < C; ++j) acc[r][j] = 0.f;
+  const uint32_t magic_v = vconst(0x43004300u);
+
+  // sum each accumulator over the wave's 64 chunks (fixed DPP order); lane
+  // r * C + col stores row r, column col of the row-group
+  auto finish_rowgroup = [&](int i) {
+    const int64_t r0 = (int64_t)(w + (i / nt) * G) * RG + wave * BT_RW;
+    float mine = 0.f;
+#pragma unroll
+    for (int r = 0; r < BT_RW; ++r)
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                            __builtin_bit_cast(int, wave_sum(acc[r][j])), 63));
+        if (lane == r * C + j) mine = v;
+        acc[r][j] = 0.f;
+      }
+    const int r = lane / C, j = lane % C;
+    const int64_t row = r0 + r;
+    if (lane < BT_RW * C && j < p.c && row < p.n) {
+      if (p.out_bf16)
+        reinterpret_cast<uint16_t*>(p.out)[j * p.n + row] = (uint16_t)f32_to_bf16_rne(mine);
+      else
+        reinterpret_cast<float*>(p.out)[j * p.n + row] = mine;
+    }
+  };
+
+  issue_w(0, 0);
+  issue_w(1, 1);
+  dma_x(0, 0);
+  wait_vmcnt<0>();
+  sum_x(0);
+  __syncthreads();
+
+  // item i uses ring slot and x buffer i % 2; the loop runs in pairs so that
+  // both are compile-time constants (register arrays cannot be indexed at run
+  // time)
+  auto item = [&](const int i, const int slot) {
+    const int b = slot;
+    // unpack this item's weights: 16 bf16 pairs (128 + q) per row
+    uint32_t wp[BT_RW][16];
+    float scr[BT_RW], zbr[BT_RW];
+#pragma unroll
+    for (int r = 0; r < BT_RW; ++r) {
+      const uint32_t w4[4] = {wv[slot][r].x, wv[slot][r].y, wv[slot][r].z, wv[slot][r].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          wp[r][4 * q + j] = LAYOUT == 1 ? pair_bf16_fast(w4[q], j, magic_v) : pair_bf16<0>(w4[q], j);
+      scr[r] = sc[slot][r];
+      zbr[r] = zb[slot][r];
+    }
+    dma_x(i + 1, b ^ 1);   // buffer b ^ 1 was last read in item i - 1
+    issue_w(slot, i + 2);  // reuses the slot just unpacked
+
+    // x fragments of two columns live at a time
+    uint32_t xa[16], xb[16];
+    float sa, sb;
+    auto read_x = [&](int col, uint32_t (&xv)[16], float& sx) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = xs[b][(col * 4 + q) * BT_CH + lane];
+        xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+      }
+      sx = sxs[b][col * BT_CH + lane];
+    };
+    auto mac = [&](int col, const uint32_t (&xv)[16], float sx) {
+      // four chains (one per row) interleaved in issue order, so
+      // consecutive dot2 never depend on each other
+      float d[BT_RW];
+#pragma unroll
+      for (int r = 0; r < BT_RW; ++r) d[r] = HZ ? -zbr[r] * sx : sx;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+#pragma unroll
+        for (int r = 0; r < BT_RW; ++r)
+          d[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e]),
+                                                 __builtin_bit_cast(bf16x2, xv[e]), d[r], false);
+#pragma unroll
+      for (int r = 0; r < BT_RW; ++r) acc[r][col] = fmaf(scr[r], d[r], acc[r][col]);
+    };
+    read_x(0, xa, sa);
+#pragma unroll
+    for (int col = 0; col < C; col += 2) {
+      read_x(col + 1, xb, sb);
+      mac(col, xa, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      if (col + 2 < C) read_x(col + 2, xa, sa);
+      mac(col + 1, xb, sb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // x of item i + 1 landed once only the weights of i + 2 are in flight
+    wait_vmcnt<WLOADS>();
+    sum_x(b ^ 1);
+    __syncthreads();
+    if (i % nt == nt - 1) finish_rowgroup(i);  // uniform
+  };
+  for (int i = 0; i < nitems; i += 2) {
+    item(i, 0);
+    if (i + 1 < nitems) item(i + 1, 1);
+  }
+  wait_vmcnt<0>();  // nothing may still be writing LDS when the wave ends
+}
+
 constexpr int STREAM_LDS_BUDGET = 48 * 1024;  // bytes of LDS per workgroup
 
 // D: weight tiles in flight per lane (4 for the decode batches; fewer for
@@ -847,6 +1120,26 @@ hipError_t launch_c(const KArgs& ka, int layout, hipStream_t s) {
   return launch_rc<1, C, XBF16>(ka, layout, s);
 }
 
+template <int C>
+hipError_t launch_batch(const KArgs& ka, int layout, hipStream_t s) {
+  // persistent grid: as many workgroups as fit at once (two per CU for 8
+  // columns, one for 16), or one per row-group if there are fewer
+  const int64_t nrg = (ka.n + 4 * BT_RW - 1) / (4 * BT_RW);
+  const unsigned blocks = (unsigned)std::min<int64_t>(nrg, (int64_t)cu_count() * (C <= 8 ? 2 : 1));
+  const bool hz = ka.zeros != nullptr, sb = ka.scale_bf16 != 0;
+#define WQ_BL(L, Z, S) \
+  hipLaunchKernelGGL((k_gemv_w4_batch<C, L, Z, S>), dim3(blocks), dim3(256), 0, s, ka)
+  if (layout == 1) {
+    if (hz) { if (sb) WQ_BL(1, true, true); else WQ_BL(1, true, false); }
+    else    { if (sb) WQ_BL(1, false, true); else WQ_BL(1, false, false); }
+  } else {
+    if (hz) { if (sb) WQ_BL(0, true, true); else WQ_BL(0, true, false); }
+    else    { if (sb) WQ_BL(0, false, true); else WQ_BL(0, false, false); }
+  }
+#undef WQ_BL
+  return hipGetLastError();
+}
+
 hipError_t launch_bf16(const KArgs& ka, int layout, hipStream_t s) {
   switch (ka.c) {
     case 1: return launch_stream_c<1>(ka, layout, s);
@@ -855,9 +1148,16 @@ hipError_t launch_bf16(const KArgs& ka, int layout, hipStream_t s) {
     case 4: return launch_stream_c<4>(ka, layout, s);
     default: break;
   }
-  if (ka.c <= 8) return launch_stream_c<8>(ka, layout, s);
-  if (ka.c <= 16) return launch_stream_c<16>(ka, layout, s);
-  return launch_c<32, true>(ka, layout, s);
+  // wide batches: passes of at most 16 columns over x[c0:c0+16] -> out[c0:c0+16]
+  for (int64_t c0 = 0; c0 < ka.c; c0 += 16) {
+    KArgs kp = ka;
+    kp.c = std::min<int64_t>(16, ka.c - c0);
+    kp.x = reinterpret_cast<const uint16_t*>(ka.x) + c0 * ka.k;
+    kp.out = reinterpret_cast<char*>(ka.out) + c0 * ka.n * (ka.out_bf16 ? 2 : 4);
+    const hipError_t e = kp.c <= 8 ? launch_batch<8>(kp, layout, s) : launch_batch<16>(kp, layout, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_f32(const KArgs& ka, int layout, hipStream_t s) {

@@ -122,8 +122,9 @@ int wq_quantize_pack_int4(const uint16_t* w, int64_t n, int64_t k, int64_t group
  *   out     [c][n], out_dtype WQ_F32 or WQ_BF16 (RNE).
  * Accumulates in float32; the result does not depend on the stream or on
  * timing (bitwise repeatable).  Requires 1 <= c <= 32 (0 is a no-op),
- * k % 32 == 0, packed and x 16-byte aligned, scales/zeros/out 4-byte aligned
- * (out 2-byte for bf16).
+ * k % 32 == 0, k <= 2^24 (32-bit buffer offsets), packed and x 16-byte
+ * aligned, scales/zeros/out 4-byte aligned (out 2-byte for bf16);
+ * otherwise WQ_ESHAPE / WQ_EALIGN before anything is launched.
  */
 int wq_gemv_w4(const uint8_t* packed, int layout, const void* scales, int scale_dtype,
                const void* zeros, float zero_const, int64_t n, int64_t k, int64_t group,

@@ -66,6 +66,10 @@ def test_validation_errors_without_gpu(lib):
     assert lib.wq_quantize_pack_int4(FAKE, 4, 48, 48, 1, FAKE, FAKE, 2, None) == g.WQ_ESHAPE
     assert lib.wq_gemv_w4(FAKE, 1, FAKE, 2, None, 8.0, 4, 256, 128, FAKE, 2, 33, FAKE, 2, None) == g.WQ_ESHAPE
     assert lib.wq_gemv_w4(FAKE, 1, FAKE, 2, None, 8.0, 4, 250, 250, FAKE, 2, 1, FAKE, 2, None) == g.WQ_ESHAPE
+    big = (1 << 24) + 32  # beyond the 32-bit offset bound
+    assert lib.wq_gemv_w4(FAKE, 1, FAKE, 2, None, 8.0, 4, big, big, FAKE, 2, 1, FAKE, 2, None) == g.WQ_ESHAPE
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, (1 << 22) + 64, 8.0, 64, 64, (1 << 22) + 64, FAKE,
+                             None) == g.WQ_ESHAPE
     assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 96, 8.0, 64, 64, 96, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 100, 1, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 128, 17, FAKE, None) == g.WQ_ESHAPE

@@ -176,6 +176,8 @@ RAGGED = [
     (260, 96, 32, 2, "f32", "bf16", False, torch.float32, 1),
     (1, 32, 32, 1, "f32", "f32", False, torch.float32, 1),
     (515, 2048, 2048, 12, "f32", "f32", True, torch.float32, 1),
+    (2050, 4160, 4160, 6, "bf16", "f32", True, torch.bfloat16, 1),
+    (33, 2080, 32, 9, "bf16", "f32", False, torch.float32, 0),
 ]
 
 
@@ -203,11 +205,11 @@ def test_gemv_ragged_and_dtypes(case):
         check_bf16_rows(got, ref)
 
 
-@pytest.mark.parametrize("xdt", ["bf16", "f32"])
-def test_gemv_integer_exact(xdt):
-    say("gemv integer exact", xdt)
+@pytest.mark.parametrize("xdt,c", [("bf16", 4), ("f32", 4), ("bf16", 16)])
+def test_gemv_integer_exact(xdt, c):
+    say("gemv integer exact", xdt, c)
     rng = np.random.default_rng(21)
-    n, k, c = 700, 5120, 4
+    n, k = 700, 5120
     codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
     x = rng.integers(-2, 3, (c, k)).astype(np.float32)
     exact = x.astype(np.int64) @ (codes.astype(np.int64) - 8).T
