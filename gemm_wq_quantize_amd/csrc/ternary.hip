@@ -14,6 +14,8 @@
 // the per-block sums of q taken from the int8 data, never from the fp16 s.
 #include "wq_internal.h"
 
+#include <algorithm>
+
 namespace wq {
 namespace {
 
@@ -247,6 +249,180 @@ __global__ __launch_bounds__(256) void k_gemv_ternary(const uint32_t* __restrict
   }
 }
 
+// Persistent variant: x (int8 q, per-32 d and sum q) is staged in LDS once
+// per workgroup, and every wave walks its own list of 8-row groups with the
+// weight loads D items (one item = 8 blocks of each of the wave's 8 rows)
+// ahead in a register ring -- no barrier inside the main loop.  Loads carry
+// no branch: items past the end read at an offset beyond the buffer, which
+// returns zeros (an all-zero block decodes to digits 0 and scale 0).
+constexpr uint32_t T_OOB = 0x80000000u;
+
+// LDS bank plan (64 banks, 4 bytes): the digit table is stored in 16 copies
+// interleaved by entry (word 16 e + l % 16 holds entry e for lane l), so the
+// four lanes that share a copy are the only ones that can collide; x blocks
+// of 128 int8 are padded to 144 bytes so that the 8 blocks a wave reads at
+// once start in 8 different bank quads.
+#ifndef WQ_T_LPR
+#define WQ_T_LPR 8  // lanes per row in the persistent ternary GEMV
+#endif
+#ifndef WQ_T_WAVES
+#define WQ_T_WAVES 4  // waves per SIMD the register budget is sized for
+#endif
+constexpr int TP_LPR = WQ_T_LPR;
+constexpr int LUT_COPIES = 16;
+constexpr int XB_WORDS = 36;  // words per padded 128-element x block
+
+// dynamic LDS: table [256][16], x [C][bpr][36 words], sum q [C][k/32], d [C][k/32]
+// LPR lanes per row (8 or 16): a wave holds 64 / LPR rows, a lane one block
+// of its row per item (an item = LPR consecutive blocks of each row).
+template <int C, int D, int LPR>
+__global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const uint32_t* __restrict__ w,
+                                                              const uint8_t* __restrict__ xq,
+                                                              float* __restrict__ out, int n, int k,
+                                                              int c) {
+  extern __shared__ uint32_t tsm[];
+  const int nsb = k / 32;
+  const int bpr = k / 128;                                // blocks per row
+  uint32_t* lut = tsm;                                    // [256][LUT_COPIES]
+  uint32_t* xs = tsm + 256 * LUT_COPIES;                  // [C][bpr][XB_WORDS]
+  int* xsum = reinterpret_cast<int*>(xs + C * bpr * XB_WORDS);  // [C][nsb]
+  float* xd = reinterpret_cast<float*>(xsum + C * nsb);   // [C][nsb]
+
+  constexpr int RPW = 64 / LPR;  // rows per wave (one row group)
+  const int tid = threadIdx.x, lane = tid & 63, sub = lane & (LPR - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntiles = (bpr + LPR - 1) / LPR;
+  const int nw = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
+  const int nrg = (n + RPW - 1) / RPW;
+  const int nitems = (nrg > gw ? (nrg - gw + nw - 1) / nw : 0) * ntiles;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)w, 0, (int)((int64_t)n * bpr * PT_BYTES), 0x00020000);
+
+  // ---- weight ring: item i = (row group gw + (i / ntiles) nw, tile i % ntiles)
+  uint32_t wd[D][7];
+  auto issue = [&](int slot, int i) {
+    const int t = i % ntiles, rg = gw + (i / ntiles) * nw;
+    const int row = rg * RPW + lane / LPR, blk = t * LPR + sub;
+    const bool ok = i < nitems && row < n && blk < bpr;
+    const uint32_t o = ok ? (uint32_t)((row * bpr + blk) * PT_BYTES) : T_OOB;
+#pragma unroll
+    for (int q = 0; q < 7; ++q)
+      wd[slot][q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * q), 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, d);
+
+  // ---- one-time staging: digit table and the activations
+  {
+    const uint32_t v = tid;
+    const uint32_t ent = (v % 3) | ((v / 3) % 3) << 8 | ((v / 9) % 3) << 16 | ((v / 27) % 3) << 24 |
+                         ((v / 81) % 3) << 4;  // entries >= 243 are never indexed by valid data
+#pragma unroll
+    for (int cpy = 0; cpy < LUT_COPIES; ++cpy) lut[tid * LUT_COPIES + cpy] = ent;
+  }
+  for (int idx = tid; idx < C * nsb; idx += 256) {
+    const int col = idx / nsb, sb = idx - col * nsb;
+    uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0}, hd = 0;
+    if (col < c) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(xq + ((int64_t)col * nsb + sb) * Q8_BYTES);
+      hd = src[0];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = src[1 + i];
+    }
+    uint32_t* dst = xs + (col * bpr + (sb >> 2)) * XB_WORDS + (sb & 3) * 8;
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      dst[i] = q[i];
+      sum = __builtin_amdgcn_sdot4((int)q[i], 0x01010101, sum, false);
+    }
+    xsum[col * nsb + sb] = sum;
+    xd[col * nsb + sb] = f16_to_f32(hd & 0xFFFFu);
+  }
+  __syncthreads();
+
+  float acc[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) acc[j] = 0.f;
+
+  // Items past nitems (the last group of D) copy out and refill their slot
+  // like any other -- the loads stay out of branches -- but skip the math.
+  auto item = [&](const int i, const int slot) {
+    const int t = i % ntiles;
+    const int blk = t * LPR + sub;
+    uint32_t v[7];
+#pragma unroll
+    for (int q = 0; q < 7; ++q) v[q] = wd[slot][q];
+    issue(slot, i + D);  // the slot is free once copied out
+    if (i >= nitems) return;  // uniform; no load below
+    // decode the 128 digits into 32 dwords in k order (dg[i] = elements 4i..4i+3)
+    const uint32_t* lt = lut + (lane & (LUT_COPIES - 1));
+    uint32_t dg[32];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {  // qs bytes 0..15: element 16 j + b
+      const uint32_t l0 = lt[(v[g] & 0xFF) * LUT_COPIES], l1 = lt[((v[g] >> 8) & 0xFF) * LUT_COPIES];
+      const uint32_t l2 = lt[((v[g] >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(v[g] >> 24) * LUT_COPIES];
+      uint32_t d0, d1, d2, d3, d4;
+      transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
+      dg[g] = d0; dg[4 + g] = d1; dg[8 + g] = d2; dg[12 + g] = d3; dg[16 + g] = d4;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {  // qs bytes 16..23: element 80 + 8 j + b
+      const uint32_t x = v[4 + g];
+      const uint32_t l0 = lt[(x & 0xFF) * LUT_COPIES], l1 = lt[((x >> 8) & 0xFF) * LUT_COPIES];
+      const uint32_t l2 = lt[((x >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(x >> 24) * LUT_COPIES];
+      uint32_t d0, d1, d2, d3, d4;
+      transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
+      dg[20 + g] = d0; dg[22 + g] = d1; dg[24 + g] = d2; dg[26 + g] = d3; dg[28 + g] = d4;
+    }
+    {
+      const uint32_t h = v[6] & 0xFFFFu;  // qh: elements 120..127
+      dg[30] = (h | (h << 14)) & 0x03030303u;
+      dg[31] = ((h >> 4) | (h << 10)) & 0x03030303u;
+    }
+    const float dw = f16_to_f32(v[6] >> 16);  // 0 for blocks past the end
+    const int bx = blk < bpr ? blk : 0;      // keeps x reads inside the staged range
+#pragma unroll
+    for (int col = 0; col < C; ++col) {
+      const uint4* xv = reinterpret_cast<const uint4*>(xs + (col * bpr + bx) * XB_WORDS);
+      float part = 0.f;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {  // activation block within the 128
+        const uint4 x0 = xv[2 * s4], x1 = xv[2 * s4 + 1];
+        int sacc = -xsum[col * nsb + bx * 4 + s4];
+        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 0], (int)x0.x, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 1], (int)x0.y, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 2], (int)x0.z, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 3], (int)x0.w, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 4], (int)x1.x, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 5], (int)x1.y, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 6], (int)x1.z, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 7], (int)x1.w, sacc, false);
+        part = fmaf(xd[col * nsb + bx * 4 + s4], (float)sacc, part);
+      }
+      acc[col] = fmaf(dw, part, acc[col]);
+    }
+    if (t == ntiles - 1) {  // uniform: the wave leaves its 8-row group
+      const int row = (gw + (i / ntiles) * nw) * RPW + lane / LPR;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        float s = acc[j];
+        if (LPR == 16) s += __shfl_xor(s, 8);  // the lanes of a row, fixed order
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 1);
+        if (sub == 0 && j < c && row < n) out[(int64_t)j * n + row] = s;
+        acc[j] = 0.f;
+      }
+    }
+  };
+  // groups of D items keep the ring slot a compile-time constant
+  for (int i = 0; i < nitems; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) item(i + d, d);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
@@ -264,8 +440,61 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x
   return hipGetLastError();
 }
 
+int cu_count_t() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+constexpr int TP_D = 4;  // items in flight per lane
+
+// Persistent launch when x fits in LDS; returns hipErrorInvalidValue (no
+// launch) otherwise.
+template <int C>
+hipError_t launch_ternary_persist(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k,
+                                  int64_t c, float* out, hipStream_t s) {
+  const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8;
+  if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
+    return hipErrorInvalidValue;
+  static bool attr_set = false;  // one per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t nrg = (n + 64 / TP_LPR - 1) / (64 / TP_LPR);
+  // workgroups resident at once: LDS and the waves per SIMD the register
+  // budget allows
+  const int per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(WQ_T_WAVES, (160 * 1024) / lds));
+  const int64_t grid = std::min<int64_t>((nrg + 3) / 4, (int64_t)cu_count_t() * per_cu);
+  hipLaunchKernelGGL((k_gemv_ternary_persist<C, TP_D, TP_LPR>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
+                     wp, xq, out, (int)n, (int)k, (int)c);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s) {
+  const uint32_t* wp0 = reinterpret_cast<const uint32_t*>(w);
+  {
+    // (a single column runs slightly faster on the tiled kernel below, whose
+    // per-tile staging is small at c = 1)
+    hipError_t e = hipErrorInvalidValue;
+    switch (c) {
+      case 1: break;
+      case 2: e = launch_ternary_persist<2>(wp0, xq, n, k, c, out, s); break;
+      case 3: case 4: e = launch_ternary_persist<4>(wp0, xq, n, k, c, out, s); break;
+      default: if (c <= 8) e = launch_ternary_persist<8>(wp0, xq, n, k, c, out, s); break;
+    }
+    if (e != hipErrorInvalidValue) return e;
+  }
   const unsigned blocks = (unsigned)((n + 31) / 32);
   const uint32_t* wp = reinterpret_cast<const uint32_t*>(w);
 #define WQ_TG(C) hipLaunchKernelGGL(k_gemv_ternary<C>, dim3(blocks), dim3(256), 0, s, wp, xq, out, n, k, (int)c)

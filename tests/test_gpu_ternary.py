@@ -66,7 +66,7 @@ def test_ternary_gemv(k, n):
     p = wq_inputs.ternary_gemv(k, n, cmax=16)
     wb = gpu_blocks(p.trits, p.d_bits)
     wref = ot.encode_ptq1_0(p.trits, p.d_bits)
-    cs = (1, 4, 8) if k == 5120 else (1, 3, 5, 16)
+    cs = (1, 2, 4, 8) if k == 5120 else (1, 3, 5, 16)
     for c in cs:
         say("ternary gemv", k, n, c)
         xq = gpu_q8(p.x[:c])
