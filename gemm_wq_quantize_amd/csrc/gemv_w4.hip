@@ -445,8 +445,10 @@ __device__ __forceinline__ float halfwave_sum(float v) {
 // (row-group of R rows, tile of 1024 k) in row-group-major order, cut into
 // NT/32 equal contiguous ranges, one per half-wave, so every half-wave
 // streams the same number of 16-byte loads and keeps D items in flight from
-// start to finish.  x, its per-chunk sums and the workgroup's scales (and
-// zeros) are staged in LDS once.  A half-wave reduces its partial for a
+// start to finish.  x and its per-chunk sums are staged in LDS once; the
+// scales (and zeros) travel with the weights in the load ring, so the
+// prologue waits only for x, which sits in cache after the first workgroup
+// asks for it.  A half-wave reduces its partial for a
 // row-group when it leaves it and parks it in an LDS slot; the slots of each
 // row-group are summed in half-wave order at the end (fixed order: bitwise
 // repeatable).
@@ -461,9 +463,8 @@ __device__ __forceinline__ float halfwave_sum(float v) {
 constexpr uint32_t OOB = 0x80000000u;
 
 template <int NT, int R, int C, int LAYOUT, int D, bool HZ, bool SBF>
-__global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int maxrows) {
+__global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
   constexpr int NHW = NT / 32;
-  using SType = typename std::conditional<SBF, uint16_t, float>::type;
   extern __shared__ uint4 smem[];
   const int nchunks = (int)(p.k / 32);
   const int nit = (nchunks + TILE_CHUNKS - 1) / TILE_CHUNKS;
@@ -473,8 +474,6 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
   float* sxs = reinterpret_cast<float*>(smem + C * 4 * nch);      // [C][nch]
   float* slots = sxs + C * nch;                                   // [NHW][sph][R][C]
   int* hwtab = reinterpret_cast<int*>(slots + NHW * sph * R * C); // [NHW][3]: i0, i1, rg_first
-  SType* sls = reinterpret_cast<SType*>(hwtab + NHW * 3);         // [maxrows][ngroups] scales
-  SType* zls = sls + maxrows * ngroups;                           // [maxrows][ngroups] zeros
 
   const int tid = threadIdx.x;
   const int lane = tid & 31;
@@ -498,30 +497,52 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
   const int rgbytes = R * rowbytes;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.packed + (int64_t)r0 * rowbytes), 0, count * rowbytes, 0x00020000);
+  // scales (and zeros) of this workgroup's rows: loaded with the weights in
+  // the ring (one per row and item), so the prologue waits for x only
+  constexpr int ESZ = SBF ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)p.scales + (int64_t)r0 * ngroups * ESZ), 0, count * ngroups * ESZ, 0x00020000);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)(HZ ? p.zeros : p.scales) + (int64_t)r0 * ngroups * ESZ), 0,
+      HZ ? count * ngroups * ESZ : 0, 0x00020000);
 
-  // issue position: byte offset of (row-group, tile) for this lane, tile,
-  // items left to issue
-  int itile = i0 - rg_first * nit, left = i1 - i0;
+  // issue position: byte offset of (row-group, tile) for this lane, its
+  // row-group and tile, items left to issue
+  int itile = i0 - rg_first * nit, left = i1 - i0, irg = rg_first;
   int ioff = rg_first * rgbytes + itile * (TILE_CHUNKS * 16) + lane * 16;
   uint4 wv[D][R];
-  auto issue = [&](uint4 (&w)[R]) {
-    const bool ok = left > 0 && itile * TILE_CHUNKS + lane < nchunks;
+  uint32_t sv[D][R], zv[D][R];  // raw scale / zero bits (converted when consumed)
+  auto issue = [&](const int slot) {
+    const int ch = itile * TILE_CHUNKS + lane;
+    const bool ok = left > 0 && ch < nchunks;
     const uint32_t wo = ok ? (uint32_t)ioff : OOB;
+    const int g = p.gshift < 0 ? 0 : (ch >> p.gshift);
+    const uint32_t so = ok ? (uint32_t)((irg * R * ngroups + g) * ESZ) : OOB;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                 wrs, wo + (uint32_t)(r * rowbytes), 0, 0));
+    for (int r = 0; r < R; ++r) {
+      wv[slot][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                        wrs, wo + (uint32_t)(r * rowbytes), 0, 0));
+      const uint32_t sro = so + (uint32_t)(r * ngroups * ESZ);
+      if (SBF) {
+        sv[slot][r] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)sro, 0, 0);
+        if (HZ) zv[slot][r] = __builtin_amdgcn_raw_buffer_load_b16(zrs, (int)sro, 0, 0);
+      } else {
+        sv[slot][r] = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)sro, 0, 0);
+        if (HZ) zv[slot][r] = __builtin_amdgcn_raw_buffer_load_b32(zrs, (int)sro, 0, 0);
+      }
+    }
     --left;
     ioff += TILE_CHUNKS * 16;
     if (++itile == nit) {
       itile = 0;
+      ++irg;
       ioff += rgbytes - nit * (TILE_CHUNKS * 16);
     }
   };
 
   // Staging loads are issued before the weight prologue: loads complete in
   // issue order, so waiting for them must not also wait for the weights.
-  constexpr int XU = 10, SU = 4;  // per-lane staging loads (launcher bounds both)
+  constexpr int XU = 10;  // per-lane x staging loads (the launcher bounds x)
   const int xunits = C * nch * 4;
   uint4 xr[XU];
 #pragma unroll
@@ -535,23 +556,9 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
         xr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) + col * p.k + kk);
     }
   }
-  const int nsc = count * ngroups;
-  const int64_t sbase = (int64_t)r0 * ngroups;
-  SType sr[SU], zr[SU];
-#pragma unroll
-  for (int i = 0; i < SU; ++i) {
-    const int idx = tid + i * NT;
-    sr[i] = SType(0);
-    zr[i] = SType(0);
-    if (idx < nsc) {
-      sr[i] = reinterpret_cast<const SType*>(p.scales)[sbase + idx];
-      if (HZ) zr[i] = reinterpret_cast<const SType*>(p.zeros)[sbase + idx];
-    }
-  }
-
   // weight prologue: D items in flight per half-wave
 #pragma unroll
-  for (int d = 0; d < D; ++d) issue(wv[d]);
+  for (int d = 0; d < D; ++d) issue(d);
 
   // x (zero beyond k and beyond c) and the per-chunk sums of x into LDS
 #pragma unroll
@@ -573,15 +580,6 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
       if (piece == 0) sxs[col * nch + ch] = ps;
     }
   }
-  // this workgroup's scales (and zeros); rows past count read 0
-#pragma unroll
-  for (int i = 0; i < SU; ++i) {
-    const int idx = tid + i * NT;
-    if (idx < maxrows * ngroups) {
-      sls[idx] = sr[i];
-      if (HZ) zls[idx] = zr[i];
-    }
-  }
   __syncthreads();
 
   const float zconst = 128.f + p.zero_const;
@@ -592,16 +590,14 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
 #pragma unroll
     for (int j = 0; j < C; ++j) acc[r][j] = 0.f;
 
-  // consume position: row-group cg (first scale of its rows: srow0), tile ct
+  // consume position: row-group cg, tile ct
   int cg = rg_first, ct = i0 - rg_first * nit;
-  int srow0 = cg * R * ngroups;
   const int nsteps = i1 - i0;
   for (int base = 0; base < nsteps; base += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const bool valid = base + d < nsteps;
       const int xo = ct * TILE_CHUNKS + lane;
-      const int g = p.gshift < 0 ? 0 : (xo >> p.gshift);
       uint32_t wp[R][16];
       float sc[R], zb[R];
 #pragma unroll
@@ -613,19 +609,17 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
           for (int j = 0; j < 4; ++j)
             wp[r][4 * qq + j] = LAYOUT == 1 ? pair_bf16_fast(w4[qq], j, magic_v)
                                             : pair_bf16<LAYOUT>(w4[qq], j);
-        const int si = srow0 + r * ngroups + g;
-        float sv, zv;
+        // items past the half-wave's range (or chunks past k) loaded a zero
+        // scale, so they contribute nothing
         if constexpr (SBF) {
-          sv = bf16_to_f32(sls[si]);
-          zv = HZ ? 128.f + bf16_to_f32(zls[si]) : zconst;
+          sc[r] = bf16_to_f32(sv[d][r]);
+          zb[r] = HZ ? 128.f + bf16_to_f32(zv[d][r]) : zconst;
         } else {
-          sv = sls[si];
-          zv = HZ ? 128.f + zls[si] : zconst;
+          sc[r] = __uint_as_float(sv[d][r]);
+          zb[r] = HZ ? 128.f + __uint_as_float(zv[d][r]) : zconst;
         }
-        sc[r] = valid ? sv : 0.f;  // past-the-range items contribute nothing
-        zb[r] = zv;
       }
-      issue(wv[d]);  // the ring slot is free once unpacked
+      issue(d);  // the ring slot is free once unpacked
 #pragma unroll
       for (int col = 0; col < C; ++col) {
         uint32_t xv[16];
@@ -667,7 +661,6 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph, int ma
           }
         ct = 0;
         ++cg;
-        srow0 += R * ngroups;
       }
     }
   }
@@ -1056,14 +1049,14 @@ hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
   const int64_t ngroups = ka.gshift < 0 ? 1 : (nchunks >> ka.gshift);
   int grid = cu_count();
   if ((int64_t)grid * R > ka.n) grid = (int)std::max<int64_t>(1, ka.n / R);
-  const int maxrows = (int)((ka.n + grid - 1) / grid);
+  const int64_t maxrows = (ka.n + grid - 1) / grid;
+  if (maxrows * ngroups * 4 >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // scale offsets
   const int sph = persist_slots(ka.n, grid, R, nit, NHW);
   const bool hz = ka.zeros != nullptr;
-  const int64_t lds = C * nch * (64 + 4) + (int64_t)NHW * sph * R * C * 4 + NHW * 3 * 4 +
-                      (int64_t)maxrows * ngroups * (ka.scale_bf16 ? 2 : 4) * (hz ? 2 : 1);
+  const int64_t lds = C * nch * (64 + 4) + (int64_t)NHW * sph * R * C * 4 + NHW * 3 * 4;
   if (lds > PERSIST_LDS_MAX) return hipErrorInvalidValue;
-  // per-lane staging registers of the kernel (x: 10 units, scales: 4)
-  if (C * nch * 4 > 10 * NT || (int64_t)maxrows * ngroups > 4 * NT) return hipErrorInvalidValue;
+  // per-lane staging registers of the kernel (x: 10 units)
+  if (C * nch * 4 > 10 * NT) return hipErrorInvalidValue;
   const int sb = ka.scale_bf16 ? 1 : 0;
 #define WQ_PFN(L, Z, S) reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, L, D, Z, S>)
   const void* fns[2][2][2] = {{{WQ_PFN(0, false, false), WQ_PFN(0, false, true)},
@@ -1077,8 +1070,8 @@ hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
     hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, PERSIST_LDS_MAX);
     attr_set[layout][hz][sb] = true;
   }
-  int sph_arg = sph, maxrows_arg = maxrows;
-  void* args[] = {const_cast<KArgs*>(&ka), &sph_arg, &maxrows_arg};
+  int sph_arg = sph;
+  void* args[] = {const_cast<KArgs*>(&ka), &sph_arg};
   return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, (size_t)lds, s);
 }
 
