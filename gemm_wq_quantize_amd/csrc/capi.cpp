@@ -110,11 +110,16 @@ int wq_gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_
   if (m == 0 || n == 0) return WQ_OK;
   if (!a || !b || !scales || !c_out) return WQ_EINVAL;
   if (k == 0 || k % 64 != 0 || k > (int64_t(1) << 22)) return WQ_ESHAPE;  // 32-bit tile offsets
-  if (layout != WQ_LAYOUT_GFX950 || group != k) return WQ_EUNSUPPORTED;
-  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c_out, 16) || !aligned(scales, 2))
+  // one scale per column, or per group of a power-of-two multiple of 64 k
+  if (!valid_group(group, k)) return WQ_ESHAPE;
+  const bool grouped = group != k;
+  if (grouped && group < 64) return WQ_EUNSUPPORTED;  // a 64-k step must lie in one group
+  if (layout != WQ_LAYOUT_GFX950) return WQ_EUNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c_out, 16) ||
+      !aligned(scales, grouped ? 4 : 2))
     return WQ_EALIGN;
   if (((m + 255) / 256) * ((n + 255) / 256) > kMaxGrid) return WQ_ESHAPE;
-  return hip_status(wq::launch_gemm_w4a16(a, b, scales, zero_const, m, n, k, c_out,
+  return hip_status(wq::launch_gemm_w4a16(a, b, scales, group, zero_const, m, n, k, c_out,
                                           as_stream(stream)));
 }
 

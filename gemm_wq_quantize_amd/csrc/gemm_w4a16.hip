@@ -1,11 +1,13 @@
 // W4A16 GEMM on the bf16 matrix cores (gfx950).
 //
-//   C[i][j] = s[j] * sum_k A[i][k] * (q[j][k] - z)
+//   C[i][j] = sum_k A[i][k] * (q[j][k] - z) * s[j][k / group]
 //
 // (Helion issue "int4 gemm kernel": C = A x unpack(B) with two codes per
 // byte along K; here B is stored output-major [N][K/2] in the gfx950 nibble
-// order, with a per-column bf16 scale applied in the epilogue and a float32
-// accumulator.)
+// order with bf16 scales and a float32 accumulator.  One scale per column
+// (group == K) is applied in the epilogue; scales per group of K (the
+// weight-only quantiser's group-128 output) are applied to B as it is
+// unpacked, see "Group scales" below.)
 //
 // Tiling.  A 256-lane workgroup computes a 256 x 256 tile of C with four
 // waves in a 2 x 2 grid; each wave owns 128 x 128 = 4 x 4 blocks of
@@ -31,6 +33,17 @@
 // Workgroups are renumbered so that each XCD (8 on MI355X, dispatched
 // round-robin) walks a compact band of output tiles, sharing A and B rows in
 // its own L2.
+//
+// Group scales (group a multiple of 64, so a 64-k step lies in one group).
+// Each step's stage also holds, for every column of the tile, the aligned
+// 4-byte word of the scale array that contains s[j][group of the step]
+// (one 4-byte buffer-to-LDS load per lane; which half holds the scale
+// follows from the parity of j * groups + group).  A lane unpacks each code
+// straight to float32 (128 + q, by OR-ing the nibble into the mantissa of
+// 128.0f), forms (128 + q) * s - (128 + z) * s = (q - z) * s with one FMA --
+// exact, the product needs at most 21 significant bits -- and rounds the
+// pair to bf16 (RNE) for the MFMA.  No row sums are needed; the only
+// rounding beyond the float32 accumulation is that of (q - z) * s to bf16.
 #include "wq_internal.h"
 
 namespace wq {
@@ -40,8 +53,11 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int NSTAGE = 3;
 constexpr int A_STAGE = BM * BK * 2;          // bytes: 256 rows x 128 B
 constexpr int B_STAGE = BN * BK / 2;          // bytes: 256 rows x 32 B
-constexpr int STAGE = A_STAGE + B_STAGE;      // 40 KiB
-constexpr int LOADS_PER_STAGE = (STAGE / 16) / 256;  // 16-byte loads per lane: 10
+constexpr int S_STAGE = BN * 4;               // bytes: one scale word per column
+// stage size and loads per lane per stage: 40 KiB and 10 (8 A + 2 B) with
+// one scale per column; 41 KiB and 11 (+1 scale word) with group scales
+template <bool GS> constexpr int stage_bytes() { return A_STAGE + B_STAGE + (GS ? S_STAGE : 0); }
+template <bool GS> constexpr int loads_per_stage() { return 10 + (GS ? 1 : 0); }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -53,6 +69,8 @@ struct GArgs {
   int64_t m, n, k;
   float zero_const;
   int tiles_m, tiles_n;
+  int ngroups;   // k / group
+  int gshift;    // log2(group / 64): step t lies in group t >> gshift
 };
 
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask_s, uint32_t bits_v) {
@@ -104,6 +122,33 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_ba
                : "memory", "m0");
 }
 
+// 4 bytes per lane from rsrc + voff into LDS at lds_base + 4 * lane
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// eight codes of one gfx950-layout word -> bf16x8 of (q - z) * s, k order:
+// c = -(128 + z) * s.  Element 2j sits in bits 4j..4j+3, element 2j+1 in bits
+// 16+4j..16+4j+3; moved to bits 16..19 under the exponent of 128.0f they
+// read as 128 + q.
+__device__ __forceinline__ bf16x8 unpack8_scaled(uint32_t w, float s, float c) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = __uint_as_float(((w << (16 - 4 * j)) & 0x000F0000u) | 0x43000000u);
+    const float hi = __uint_as_float(((w >> (4 * j)) & 0x000F0000u) | 0x43000000u);
+    const f2 v = {fmaf(lo, s, c), fmaf(hi, s, c)};
+    r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // A-tile swizzle: physical 16-byte column of k-chunk c in row r is c ^ swz(r)
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -123,12 +168,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // padded by 16 bytes so that the two rows one 2-byte LDS write touches (4
 // apart) fall in different banks.
 constexpr int C_PITCH = BN * 2 + 16;
-static_assert(128 * C_PITCH <= NSTAGE * STAGE, "epilogue staging fits the ring");
+static_assert(128 * C_PITCH <= NSTAGE * stage_bytes<false>(), "epilogue staging fits the ring");
 
 // One workgroup tile.  WN (the wave's column half) is a template argument so
-// that the row-sum split below indexes fragments at compile time.
-template <int WN>
+// that the row-sum split below indexes fragments at compile time; GS selects
+// group scales (applied while unpacking B) over one scale per column
+// (applied in the epilogue).
+template <int WN, bool GS>
 __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (*rsx)[4][32]) {
+  constexpr int STAGE = stage_bytes<GS>();
+  constexpr int LOADS_PER_STAGE = loads_per_stage<GS>();
   // ---- tile order: XCD-aware renumbering, then bands of 8 tile-rows
   const int nwg = p.tiles_m * p.tiles_n;
   int id = blockIdx.x;
@@ -153,6 +202,12 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // descriptors over this tile's rows; rows past M / N read as zero
   const i32x4 ars = make_rsrc(p.a + m0 * p.k, (uint32_t)rows_a * kbytes_a);
   const i32x4 brs = make_rsrc(p.b + n0 * (p.k / 2), (uint32_t)rows_b * kbytes_b);
+  // group scales of this tile's columns, [rows_b][ngroups] bf16.  The range
+  // is rounded up to whole 4-byte words: the base is 4-byte aligned, so the
+  // word holding the last scale is one the caller's array already touches
+  // (and cannot cross a page); the half past the array is never used.
+  const i32x4 srs = make_rsrc(GS ? (const void*)(p.scales + n0 * p.ngroups) : (const void*)p.scales,
+                              GS ? (((uint32_t)rows_b * (uint32_t)p.ngroups * 2u + 3u) & ~3u) : 0u);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   // ---- global -> LDS assignment.  Load i (0..7) of wave w fills A slots
@@ -179,13 +234,16 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     const int row = s >> 1, half = (s & 1) ^ ((row >> 3) & 1);
     b_voff[h] = (uint32_t)row * kbytes_b + (uint32_t)half * 16;
   }
+  // scale word of wave w, lane l: column 64 w + l
+  const uint32_t s_voff = (uint32_t)((wave * 64 + lane) * p.ngroups) * 2u;
   const int nk = (int)(p.k / BK);
 
   // Step kt's loads into stage kt % 3.  Steps past the end are issued too
   // (the loop then has no branch) but at offset 2^31 or more, which is past
   // num_records: they read nothing from memory and fill an unused stage with
   // zeros.
-  // loads [first, last) of step kt: 0..7 are A, 8 and 9 are B
+  // loads [first, last) of step kt: 0..7 are A, 8 and 9 are B, 10 the
+  // group scales
   auto issue_part = [&](int kt, int first, int last) {
     const uint32_t st = lds0 + (uint32_t)(kt % NSTAGE) * STAGE;
     const bool live = kt < nk;
@@ -201,6 +259,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
       if (8 + h >= first && 8 + h < last)
         dma16(brs, b_voff[h] + kb,
               __builtin_amdgcn_readfirstlane(st + A_STAGE + (uint32_t)(h * 4 + wave) * 1024));
+    if (GS && 10 >= first && 10 < last) {
+      const uint32_t so = live ? ((s_voff + (uint32_t)(kt >> p.gshift) * 2u) & ~3u) : 0x80000000u;
+      dma4(srs, so, __builtin_amdgcn_readfirstlane(st + A_STAGE + B_STAGE + (uint32_t)wave * 256));
+    }
   };
   auto issue = [&](int kt) { issue_part(kt, 0, LOADS_PER_STAGE); };
   // Every group of loads inside the loop sits between full scheduling
@@ -250,6 +312,25 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int j = 0; j < 4; ++j) bw[j] = *reinterpret_cast<const uint4*>(st + b_rd[j]);
   };
+  // group scales of this lane's four columns for step kt (raw words)
+  auto read_s = [&](int kt, uint32_t (&sw)[4]) {
+    const uint8_t* st = smem + (kt % NSTAGE) * STAGE + A_STAGE + B_STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sw[j] = *reinterpret_cast<const uint32_t*>(st + (WN * 128 + j * 32 + lr) * 4);
+  };
+  // word -> float scale and offset term: the scale of column n for group g
+  // is the high half when n * groups + g is odd (n and lr share parity)
+  const float zb = 128.f + p.zero_const;
+  float gsc[4] = {0.f, 0.f, 0.f, 0.f}, gof[4] = {0.f, 0.f, 0.f, 0.f};
+  auto set_s = [&](int kt, const uint32_t (&sw)[4]) {
+    const bool hi = (((lr & p.ngroups) ^ (kt >> p.gshift)) & 1) != 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      gsc[j] = __uint_as_float(hi ? (sw[j] & 0xFFFF0000u) : (sw[j] << 16));
+      gof[j] = -zb * gsc[j];
+    }
+  };
   auto read_a = [&](int kt, int ks, bf16x8 (&af)[4]) {
     const uint8_t* st = smem + (kt % NSTAGE) * STAGE;
     const int chunk = lh * 4 + ks;
@@ -262,10 +343,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
-      bfr[j] = unpack8(w, magic_v);
+      bfr[j] = GS ? unpack8_scaled(w, gsc[j], gof[j]) : unpack8(w, magic_v);
     }
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
+    for (int ii = 0; ii < 2 && !GS; ++ii) {
       const bf16x8 x = af[2 * WN + ii];
       // (pairs taken with shufflevector: extracting lanes of a bit-cast
       // u32x4 was folded onto the first dword by this compiler)
@@ -283,7 +364,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, GS ? 7 : 3, 0);  // VALU
       if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
 #endif
@@ -294,10 +375,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // issued into it.  b(t + 1) sits before the last 16-k group of step t, so
   // that step t + 1's first operands are read while that group multiplies.
   // Step t's loads go out in three groups: 0-3 right after b(t - 2), 4-6
-  // and 7-9 between the 16-k groups of step t - 2 (a burst of ten would
-  // stall this wave's MFMA issue).  All ten loads of step t + 2 precede the
-  // wait before b(t + 1), so that wait (at most ten loads in flight) covers
-  // step t + 1.
+  // and 7-9 (and the scale word) between the 16-k groups of step t - 2 (a
+  // burst of ten would stall this wave's MFMA issue).  All loads of step
+  // t + 2 precede the wait before b(t + 1), so that wait (at most one step
+  // of loads in flight) covers step t + 1.
   asm volatile("s_nop 4");  // VALU-written SGPRs (descriptors) read by the first loads
   issue(0);
   issue(1);
@@ -306,7 +387,12 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   issue_fenced(2, 0, 4);
   uint4 bw[4];
   bf16x8 a0[4], a1[4];
+  uint32_t sw[4];
   read_b(0, bw);
+  if (GS) {
+    read_s(0, sw);
+    set_s(0, sw);
+  }
   read_a(0, 0, a0);
   for (int kt = 0; kt < nk; ++kt) {
     read_a(kt, 1, a1);
@@ -314,7 +400,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     issue_fenced(kt + 2, 4, 7);
     read_a(kt, 2, a0);
     compute(a1, bw, 1);
-    issue_fenced(kt + 2, 7, 10);
+    issue_fenced(kt + 2, 7, LOADS_PER_STAGE);
     read_a(kt, 3, a1);
     compute(a0, bw, 2);
     // a1 holds the last operands read from stage kt (the barrier's release
@@ -324,32 +410,34 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     issue_fenced(kt + 3, 0, 4);
     uint4 bn[4];
     read_b(kt + 1, bn);
+    if (GS) read_s(kt + 1, sw);
     read_a(kt + 1, 0, a0);
     compute(a1, bw, 3);
 #pragma unroll
     for (int j = 0; j < 4; ++j) bw[j] = bn[j];
+    if (GS) set_s(kt + 1, sw);
   }
   wait_vmcnt<0>();  // no load may still be writing LDS below
 
   // ---- row sums: complete the k halves, swap halves of the row blocks
   // with the other column half's wave through LDS.
 #pragma unroll
-  for (int ii = 0; ii < 2; ++ii) {
+  for (int ii = 0; ii < 2 && !GS; ++ii) {
     float r = (rsq[ii][0] + rsq[ii][1]) + (rsq[ii][2] + rsq[ii][3]);
     r += __shfl_xor(r, 32);
     if (lh == 0) rsx[wm][2 * WN + ii][lr] = r;
   }
   __syncthreads();  // also: every wave is done with the ring
 
-  // ---- epilogue: fold out the offset, scale per column, bf16 RNE; stage
-  // half the tile in LDS, then write it with coalesced 16-byte stores.
+  // ---- epilogue: fold out the offset, scale per column (both already in
+  // the accumulator with group scales), bf16 RNE; stage half the tile in
+  // LDS, then write it with coalesced 16-byte stores.
   // Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  const float zb = 128.f + p.zero_const;
   float sc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t col = n0 + WN * 128 + j * 32 + lr;
-    sc[j] = col < p.n ? bf16_to_f32(p.scales[col]) : 0.f;
+    sc[j] = GS ? 1.f : (col < p.n ? bf16_to_f32(p.scales[col]) : 0.f);
   }
   const bool vec_ok = (p.n & 7) == 0;  // rows 16-byte aligned
 #pragma unroll
@@ -360,7 +448,8 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
       float rsum[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const floatx4 v = *reinterpret_cast<const floatx4*>(&rsx[wm][i][8 * g + 4 * lh]);
+        const floatx4 v = GS ? floatx4{0.f, 0.f, 0.f, 0.f}
+                             : *reinterpret_cast<const floatx4*>(&rsx[wm][i][8 * g + 4 * lh]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) rsum[4 * g + e] = v[e];
       }
@@ -371,7 +460,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
         for (int e = 0; e < 16; ++e) {
           // staged row: 64 wm + 32 ii + local row
           const int srow = wm * 64 + ii * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
-          const float v = (acc[i][j][e] - zb * rsum[e]) * sc[j];
+          const float v = GS ? acc[i][j][e] : (acc[i][j][e] - zb * rsum[e]) * sc[j];
           *reinterpret_cast<uint16_t*>(smem + srow * C_PITCH + col * 2) =
               (uint16_t)f32_to_bf16_rne(v);
         }
@@ -399,19 +488,20 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   }
 }
 
+template <bool GS>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * stage_bytes<GS>()];
   __shared__ __attribute__((aligned(16))) float rsx[2][4][32];  // row sums [wm][row block][row]
   // wave-uniform branch (the wave index is moved to a scalar register)
-  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1>(p, smem, rsx);
-  else gemm_tile<0>(p, smem, rsx);
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1, GS>(p, smem, rsx);
+  else gemm_tile<0, GS>(p, smem, rsx);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_w4a16(const uint16_t* a, const uint8_t* b, const uint16_t* scales,
-                             float zero_const, int64_t m, int64_t n, int64_t k, uint16_t* c,
-                             hipStream_t s) {
+                             int64_t group, float zero_const, int64_t m, int64_t n, int64_t k,
+                             uint16_t* c, hipStream_t s) {
   GArgs p;
   p.a = a;
   p.b = b;
@@ -423,8 +513,14 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint8_t* b, const uint16_t
   p.zero_const = zero_const;
   p.tiles_m = (int)((m + BM - 1) / BM);
   p.tiles_n = (int)((n + BN - 1) / BN);
+  p.ngroups = (int)(k / group);
+  p.gshift = 0;
+  while ((int64_t(BK) << p.gshift) < group) ++p.gshift;
   const unsigned nwg = (unsigned)(p.tiles_m * p.tiles_n);
-  hipLaunchKernelGGL(k_gemm_w4a16, dim3(nwg), dim3(256), 0, s, p);
+  if (group == k)
+    hipLaunchKernelGGL(k_gemm_w4a16<false>, dim3(nwg), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_gemm_w4a16<true>, dim3(nwg), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -132,17 +132,25 @@ int wq_gemv_w4(const uint8_t* packed, int layout, const void* scales, int scale_
                void* stream);
 
 /*
- * wq_gemm_w4a16 -- C[i][j] = sum_k A[i][k] * (q[j][k] - zero_const) * s[j]
+ * wq_gemm_w4a16 -- C[i][j] = sum_k A[i][k] * (q[j][k] - zero_const) * s[j][k / group]
  * (Helion issue [matmul_bf16_int4]; B is stored output-major [n][k/2], the
- * transpose of the issue's (K/2, N) int8 view, with a per-column scale).
+ * transpose of the issue's (K/2, N) int8 view; the group scales are the
+ * weight-only quantiser's output, as in the Vulkan shader's per-group
+ * scale).
  *   a       [m][k] bf16.
  *   b       [n][k/2] uint8 in `layout` (WQ_LAYOUT_GFX950 only).
- *   scales  [n] bf16 (group must equal k).
+ *   scales  bf16: [n] when group == k (one scale per column, applied to the
+ *           float32 sum), else [n][k/group] with group a power of two,
+ *           64 <= group < k (each weight becomes bf16((q - z) * s), RNE,
+ *           before the bf16 multiply; group 32 is WQ_EUNSUPPORTED).
  *   c_out   [m][n] bf16 (RNE of the float32 accumulator).
- * Requires k % 64 == 0 and k <= 2^22; a, b and c_out 16-byte aligned, scales 2-byte
- * aligned.  Any m and n (ragged tiles are masked).  Every zero_const is
- * exact for integer zero points (|q - z| <= 15 is a bf16 integer); other
- * values are rounded to bf16 per weight.
+ * Requires k % 64 == 0 and k <= 2^22; a, b and c_out 16-byte aligned, scales
+ * 2-byte aligned (4-byte with group scales; the kernel reads whole aligned
+ * 4-byte words of the scale array, so the 2 bytes after its last element
+ * may be read and are ignored).  Any m and n (ragged tiles are masked).
+ * With one scale per column the zero point folds out exactly through the
+ * row sums of A; integer zero points with group scales are exact up to the
+ * bf16 rounding of (q - z) * s.
  */
 int wq_gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* scales,
                   int64_t group, float zero_const, int64_t m, int64_t n, int64_t k,

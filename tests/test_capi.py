@@ -77,9 +77,14 @@ def test_validation_errors_without_gpu(lib):
     assert lib.wq_quantize_q8_1(FAKE, 2, 48, FAKE, None) == g.WQ_ESHAPE
     # unsupported combinations
     assert lib.wq_gemm_w4a16(FAKE, FAKE, 0, FAKE, 128, 8.0, 64, 64, 128, FAKE, None) == g.WQ_EUNSUPPORTED
-    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 128, 8.0, 64, 64, 256, FAKE, None) == g.WQ_EUNSUPPORTED
+    # group scales: a power of two >= 64 dividing k (k = 256 or 192 here)
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 32, 8.0, 64, 64, 256, FAKE, None) == g.WQ_EUNSUPPORTED
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 96, 8.0, 64, 64, 192, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 512, 8.0, 64, 64, 256, FAKE, None) == g.WQ_ESHAPE
     # alignment
     assert lib.wq_gemv_w4(ODD, 1, FAKE, 2, None, 8.0, 4, 128, 128, FAKE, 2, 1, FAKE, 2, None) == g.WQ_EALIGN
     assert lib.wq_quantize_pack_int4(FAKE, 4, 256, 128, 1, ODD, FAKE, 2, None) == g.WQ_EALIGN
     assert lib.wq_gemm_w4a16(ODD, FAKE, 1, FAKE, 128, 8.0, 64, 64, 128, FAKE, None) == g.WQ_EALIGN
+    # group scales are read as aligned 4-byte words
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, P(0x1002), 128, 8.0, 64, 64, 256, FAKE, None) == g.WQ_EALIGN
     assert lib.wq_gemv_ternary(ODD, FAKE, 4, 128, 1, FAKE, None) == g.WQ_EALIGN

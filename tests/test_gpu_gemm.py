@@ -5,7 +5,7 @@ import torch
 
 import wq_inputs
 from oracle import fpformat, int4 as o4
-from tolerances import check_bf16_rows
+from tolerances import check_bf16_rownorm, check_bf16_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -23,14 +23,14 @@ def bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
 
 
-def run(a_bits, codes, scale_bits, zc=8.0):
+def run(a_bits, codes, scale_bits, zc=8.0, group=None):
     g = G()
     m, k = a_bits.shape
     n = codes.shape[0]
     b = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda")
     g.wq_pack_int4(torch.from_numpy(codes).cuda(), 1, b)
     c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-    g.wq_gemm_w4a16(bf16_dev(a_bits), b, 1, bf16_dev(scale_bits), k, zc, c)
+    g.wq_gemm_w4a16(bf16_dev(a_bits), b, 1, bf16_dev(scale_bits), group or k, zc, c)
     torch.cuda.synchronize()
     return c
 
@@ -89,3 +89,62 @@ def test_gemm_8192_sampled_rows():
     rms = allc.pow(2).mean(dim=1).sqrt().cpu().numpy()
     expect = float(np.sqrt(np.mean(ref ** 2)))
     assert np.all(np.abs(rms / expect - 1) < 0.1)
+
+
+# ---- group scales ([N][K/group] bf16; each weight rounded to bf16 before the
+# multiply, as the oracle's ``gemm_w4a16_rows_bf16w`` states)
+@pytest.mark.parametrize("m,n,k,group", [(300, 520, 512, 128), (256, 256, 256, 64),
+                                         (129, 333, 1152, 128), (200, 300, 704, 64),
+                                         (513, 257, 2048, 256), (64, 1000, 1024, 512)])
+def test_gemm_group_scales(m, n, k, group):
+    # (129, 333, 1152): 9 groups and 333 columns, an odd number of scales,
+    # so the last scale sits in the low half of a word that ends past the array
+    say("gemm group scales", m, n, k, group)
+    p = wq_inputs.grouped_gemm(m, n, k, group, seed=m + n)
+    c = run(p.a_bits, p.codes, p.scale_bits, group=group).float().cpu().numpy()
+    a = fpformat.bf16_bits_to_f32(p.a_bits)
+    s = fpformat.bf16_bits_to_f32(p.scale_bits)
+    packed = o4.pack(p.codes, 1)
+    check_bf16_rows(c, o4.gemm_w4a16_rows_bf16w(a, packed, 1, s, 8.0, group))
+    check_bf16_rownorm(c, o4.gemm_w4a16_rows(a, packed, 1, s, 8.0, group))
+
+
+def test_gemm_group_scales_integer_exact():
+    # power-of-two scales that change per group: every weight is exact in
+    # bf16 and every partial sum a multiple of 1/4 below 2^22, so C must be
+    # the RNE bf16 of the exact sum; taking a scale from the wrong group or
+    # the wrong half of a scale word changes the result
+    say("gemm group scales, integer exact")
+    rng = np.random.default_rng(14)
+    m, n, k, group = 256, 264, 1408, 128
+    a = rng.integers(-4, 5, (m, k)).astype(np.float32)
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    e = rng.integers(-2, 3, (n, k // group))
+    s_bits = fpformat.f32_to_bf16_bits((2.0 ** e).astype(np.float32))
+    c = run(fpformat.f32_to_bf16_bits(a), codes, s_bits, group=group)
+    w = (codes.astype(np.float64) - 8) * np.repeat(2.0 ** e, group, axis=1)
+    exact = a.astype(np.float64) @ w.T
+    want = fpformat.f32_to_bf16_bits(exact.astype(np.float32))
+    assert np.array_equal(c.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+def test_gemm_on_quantiser_output():
+    # the quantiser's group-128 output (codes and bf16 scales) feeds the GEMM
+    # directly; the oracle quantises the same fp16 weights itself
+    say("gemm on wq_quantize_pack_int4 output, 64 x 4096 x 11008")
+    g = G()
+    m, n, k = 64, 4096, 11008
+    rng = np.random.default_rng(15)
+    w16 = wq_inputs.to_f16_bits(0.02 * rng.standard_normal((n, k), dtype=np.float32))
+    a_bits = wq_inputs.to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, k // 128), dtype=torch.bfloat16, device="cuda")
+    g.wq_quantize_pack_int4(torch.from_numpy(w16).view(torch.float16).cuda(), 128, 1, packed, scales)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    g.wq_gemm_w4a16(bf16_dev(a_bits), packed, 1, scales, 128, 8.0, c)
+    torch.cuda.synchronize()
+    codes, s, _ = o4.quantize_int4(w16, 128, "bf16")
+    assert np.array_equal(packed.cpu().numpy(), o4.pack(codes, 1))
+    a = fpformat.bf16_bits_to_f32(a_bits)
+    got = c.float().cpu().numpy()
+    check_bf16_rows(got, o4.gemm_w4a16_rows_bf16w(a, o4.pack(codes, 1), 1, s, 8.0, 128))

@@ -272,3 +272,37 @@ def test_gemm_rows_closed_forms():
     ai = rng.integers(-4, 5, (m, k))
     c = int4.gemm_w4a16_rows(ai.astype(np.float64), p, 1, np.ones((n, 1)), 8.0, k)
     assert np.array_equal(c, (ai @ (codes.astype(np.int64) - 8).T).astype(np.float64))
+
+
+def test_gemm_bf16_weights_handworked():
+    # one column, group 64, scale bf16 0x3C24 = 1.28125 * 2^-7: (q - 8) = 7
+    # gives 8.96875 * 2^-7 = (1 + 15.5/128) * 2^-4, a tie that rounds to even
+    # (16/128) -> 0.0703125; q - 8 = 3 gives 3.84375 * 2^-7, exact in bf16;
+    # q - 8 = -7 mirrors the tie.  One-hot rows of A read single weights.
+    s = fpformat.bf16_bits_to_f32(np.array([[0x3C24]], np.uint16)).astype(np.float64)
+    assert s[0, 0] == 0.010009765625
+    codes = np.full((1, 64), 8, np.uint8)
+    codes[0, 0], codes[0, 1], codes[0, 2] = 15, 11, 1
+    a = np.eye(64)[:3]
+    c = int4.gemm_w4a16_rows_bf16w(a, int4.pack(codes, 1), 1, s, 8.0, 64)
+    assert c[:, 0].tolist() == [0.0703125, 0.030029296875, -0.0703125]
+    exact = int4.gemm_w4a16_rows(a, int4.pack(codes, 1), 1, s, 8.0, 64)
+    assert exact[:, 0].tolist() == [7 * 0.010009765625, 3 * 0.010009765625, -7 * 0.010009765625]
+
+
+def test_gemm_bf16_weights_equal_exact_for_power_of_two_scales():
+    # (q - 8) * 2^e is exact in bf16, so rounding the weights changes nothing;
+    # a wrong group index (scale taken from another group) would still differ
+    # from the exact oracle because the exponents vary per group.
+    rng = np.random.default_rng(12)
+    m, n, k, group = 5, 12, 512, 128
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = 2.0 ** rng.integers(-3, 3, (n, k // group))
+    a = rng.standard_normal((m, k))
+    p = int4.pack(codes, 1)
+    got = int4.gemm_w4a16_rows_bf16w(a, p, 1, s, 8.0, group)
+    ref = int4.gemm_w4a16_rows(a, p, 1, s, 8.0, group)
+    assert np.array_equal(got, ref)
+    # and against a per-element brute force of the group lookup
+    w = np.array([[(int(codes[r, kk]) - 8) * s[r, kk // group] for kk in range(k)] for r in range(n)])
+    assert np.allclose(ref, a @ w.T, rtol=0, atol=1e-12)

@@ -50,3 +50,16 @@ def check_bf16_rows(got, ref, rel=REL_BF16_ROW):
     assert not badel.any(), (f"{int(badel.sum())} of {badel.size} elements beyond "
                              f"2^-8|y*| + {ACC_BUDGET} rms; worst excess "
                              f"{float((np.abs(diff) / np.maximum(bound, 1e-300)).max()):.3g}x")
+
+
+def check_bf16_rownorm(got, ref, rel=REL_BF16_ROW):
+    """The normwise half of ``check_bf16_rows`` alone: ||y - y*|| <= rel ||y*||
+    per row, for a reference that is not the kernel's own rounding chain."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    err = np.sqrt(np.sum((got - ref) ** 2, axis=-1))
+    nrm = np.sqrt(np.sum(ref * ref, axis=-1))
+    bad = err > rel * nrm
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} rows beyond {rel} normwise; worst "
+                           f"{float((err / np.maximum(nrm, 1e-300)).max()):.3g}")

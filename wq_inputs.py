@@ -28,7 +28,7 @@ import torch
 
 __all__ = [
     "to_bf16_bits", "to_f16_bits", "bf16_bits_to_f32", "f16_bits_to_f32",
-    "tiny_int4", "decode_int4", "small_batch_int4", "large_gemm",
+    "tiny_int4", "decode_int4", "small_batch_int4", "large_gemm", "grouped_gemm",
     "ternary_gemv", "DECODE_SHAPES", "SMALL_BATCH_SHAPES",
 ]
 
@@ -144,6 +144,17 @@ def large_gemm(m: int = 8192, n: int = 8192, k: int = 8192, n_rows: int = 256,
     scale_bits = to_bf16_bits(np.full(n, 0.01, dtype=np.float32))
     rows = np.sort(rng.choice(m, min(n_rows, m), replace=False))
     return GemmProblem(m, n, k, a_bits, codes, scale_bits, 8.0, rows)
+
+
+def grouped_gemm(m: int, n: int, k: int, group: int = 128, seed: int = 0) -> GemmProblem:
+    """W4A16 GEMM with group scales, shaped like the decode workload's weights:
+    A bf16 ~ N(0,1); int4 codes U{0..15}; bf16 scales U(0.002, 0.02) per
+    (column, group of ``group`` k) as [N][K/group]; zero 8; every row."""
+    rng = np.random.default_rng(seed)
+    a_bits = to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    scale_bits = to_bf16_bits(rng.uniform(0.002, 0.02, (n, k // group)).astype(np.float32))
+    return GemmProblem(m, n, k, a_bits, codes, scale_bits, 8.0, np.arange(m))
 
 
 @dataclass
