@@ -132,17 +132,18 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds_bas
 
 // eight codes of one gfx950-layout word -> bf16x8 of (q - z) * s, k order:
 // c = -(128 + z) * s.  Element 2j sits in bits 4j..4j+3, element 2j+1 in bits
-// 16+4j..16+4j+3; moved to bits 16..19 under the exponent of 128.0f they
-// read as 128 + q.
-__device__ __forceinline__ bf16x8 unpack8_scaled(uint32_t w, float s, float c) {
+// 16+4j..16+4j+3; moved to bits 16..19 under the exponent of 128.0f
+// (magic_v = 0x43000000) they read as 128 + q.  VOP3 takes no literal, so the
+// mask is a scalar operand of v_and_or_b32.
+__device__ __forceinline__ bf16x8 unpack8_scaled(uint32_t w, float s, float c, uint32_t magic_v) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   typedef float f2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   u32x4 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float lo = __uint_as_float(((w << (16 - 4 * j)) & 0x000F0000u) | 0x43000000u);
-    const float hi = __uint_as_float(((w >> (4 * j)) & 0x000F0000u) | 0x43000000u);
+    const float lo = __uint_as_float(and_or(w << (16 - 4 * j), 0x000F0000u, magic_v));
+    const float hi = __uint_as_float(and_or(j == 0 ? w : w >> (4 * j), 0x000F0000u, magic_v));
     const f2 v = {fmaf(lo, s, c), fmaf(hi, s, c)};
     r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
   }
@@ -162,6 +163,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 #ifndef WQ_G_SCHED
 #define WQ_G_SCHED 1  // 1: interleave MFMA / VALU / LDS reads with scheduling-group barriers
+#endif
+#ifndef WQ_G_VPM
+#define WQ_G_VPM 4    // VALU instructions placed after each MFMA with group scales
 #endif
 
 // Epilogue staging: half the tile (128 rows x 256 bf16) at a time, rows
@@ -293,6 +297,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   const int lr = lane & 31;   // operand row (A) / column (B) within a 32-block
   const int lh = lane >> 5;   // k half: chunks 4 lh .. 4 lh + 3 of every step
   const uint32_t magic_v = vconst(0x43004300u);
+  const uint32_t magic_m = vconst(0x43000000u);
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 
   // LDS byte offsets (within a stage) of this lane's operands
@@ -343,10 +348,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
-      bfr[j] = GS ? unpack8_scaled(w, gsc[j], gof[j]) : unpack8(w, magic_v);
+      bfr[j] = unpack8(w, magic_v);
     }
 #pragma unroll
-    for (int ii = 0; ii < 2 && !GS; ++ii) {
+    for (int ii = 0; ii < 2; ++ii) {
       const bf16x8 x = af[2 * WN + ii];
       // (pairs taken with shufflevector: extracting lanes of a bit-cast
       // u32x4 was folded onto the first dword by this compiler)
@@ -364,7 +369,31 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, GS ? 7 : 3, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+      if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+#endif
+  };
+  // Group scales: slice ks of the step's B words dequantised ahead of use
+  // (dq), so the 16 MFMAs of one slice (mm) overlap the VALU work of the next.
+  auto dq = [&](const uint4 (&bw)[4], int ks, bf16x8 (&bfr)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
+      bfr[j] = unpack8_scaled(w, gsc[j], gof[j], magic_m);
+    }
+  };
+  auto mm = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+#if WQ_G_SCHED
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, WQ_G_VPM, 0);  // VALU
       if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
 #endif
@@ -387,35 +416,59 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   issue_fenced(2, 0, 4);
   uint4 bw[4];
   bf16x8 a0[4], a1[4];
-  uint32_t sw[4];
   read_b(0, bw);
-  if (GS) {
+  if constexpr (GS) {
+    uint32_t sw[4];
+    bf16x8 b0[4], b1[4];
     read_s(0, sw);
     set_s(0, sw);
-  }
-  read_a(0, 0, a0);
-  for (int kt = 0; kt < nk; ++kt) {
-    read_a(kt, 1, a1);
-    compute(a0, bw, 0);
-    issue_fenced(kt + 2, 4, 7);
-    read_a(kt, 2, a0);
-    compute(a1, bw, 1);
-    issue_fenced(kt + 2, 7, LOADS_PER_STAGE);
-    read_a(kt, 3, a1);
-    compute(a0, bw, 2);
-    // a1 holds the last operands read from stage kt (the barrier's release
-    // waits for them); stage kt + 1 landed once only step kt + 2 is in flight
-    wait_vmcnt<LOADS_PER_STAGE>();
-    __syncthreads();
-    issue_fenced(kt + 3, 0, 4);
-    uint4 bn[4];
-    read_b(kt + 1, bn);
-    if (GS) read_s(kt + 1, sw);
-    read_a(kt + 1, 0, a0);
-    compute(a1, bw, 3);
+    read_a(0, 0, a0);
+    dq(bw, 0, b0);
+    for (int kt = 0; kt < nk; ++kt) {
+      read_a(kt, 1, a1);
+      dq(bw, 1, b1);
+      mm(a0, b0);
+      issue_fenced(kt + 2, 4, 7);
+      read_a(kt, 2, a0);
+      dq(bw, 2, b0);
+      mm(a1, b1);
+      issue_fenced(kt + 2, 7, LOADS_PER_STAGE);
+      read_a(kt, 3, a1);
+      dq(bw, 3, b1);
+      mm(a0, b0);
+      wait_vmcnt<LOADS_PER_STAGE>();
+      __syncthreads();
+      issue_fenced(kt + 3, 0, 4);
+      read_b(kt + 1, bw);  // bw's slices are all dequantised by now
+      read_s(kt + 1, sw);
+      read_a(kt + 1, 0, a0);
+      set_s(kt + 1, sw);
+      dq(bw, 0, b0);
+      mm(a1, b1);
+    }
+  } else {
+    read_a(0, 0, a0);
+    for (int kt = 0; kt < nk; ++kt) {
+      read_a(kt, 1, a1);
+      compute(a0, bw, 0);
+      issue_fenced(kt + 2, 4, 7);
+      read_a(kt, 2, a0);
+      compute(a1, bw, 1);
+      issue_fenced(kt + 2, 7, LOADS_PER_STAGE);
+      read_a(kt, 3, a1);
+      compute(a0, bw, 2);
+      // a1 holds the last operands read from stage kt (the barrier's release
+      // waits for them); stage kt + 1 landed once only step kt + 2 is in flight
+      wait_vmcnt<LOADS_PER_STAGE>();
+      __syncthreads();
+      issue_fenced(kt + 3, 0, 4);
+      uint4 bn[4];
+      read_b(kt + 1, bn);
+      read_a(kt + 1, 0, a0);
+      compute(a1, bw, 3);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bw[j] = bn[j];
-    if (GS) set_s(kt + 1, sw);
+      for (int j = 0; j < 4; ++j) bw[j] = bn[j];
+    }
   }
   wait_vmcnt<0>();  // no load may still be writing LDS below
 

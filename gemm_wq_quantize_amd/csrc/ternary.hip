@@ -272,6 +272,102 @@ constexpr int TP_LPR = WQ_T_LPR;
 constexpr int LUT_COPIES = 16;
 constexpr int XB_WORDS = 36;  // words per padded 128-element x block
 
+// One-time staging of a workgroup's LDS: the digit table in LUT_COPIES
+// interleaved copies and the activations (x blocks padded to XB_WORDS words,
+// per-32 sum of q and d).  Columns c..C-1 stage zeros.
+template <int C>
+__device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsum, float* xd,
+                                           const uint8_t* __restrict__ xq, int bpr, int nsb, int c) {
+  const int tid = threadIdx.x;
+  {
+    // Thread t owns entry t (words 16 t .. 16 t + 15) and writes its copies
+    // as four 16-byte quads in the order (m + t / 4) % 4: the 16 lanes one
+    // ds_write_b128 cycle serves then cover all 64 banks (writing the copies
+    // in order would put every lane of a cycle in 4 banks).
+    static_assert(LUT_COPIES == 16, "copy quads");
+    const uint32_t v = tid;
+    const uint32_t ent = (v % 3) | ((v / 3) % 3) << 8 | ((v / 9) % 3) << 16 | ((v / 27) % 3) << 24 |
+                         ((v / 81) % 3) << 4;  // entries >= 243 are never indexed by valid data
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<uint4*>(lut + tid * LUT_COPIES + 4 * ((m + (tid >> 2)) & 3)) =
+          make_uint4(ent, ent, ent, ent);
+  }
+  for (int idx = tid; idx < C * nsb; idx += 256) {
+    const int col = idx / nsb, sb = idx - col * nsb;
+    uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0}, hd = 0;
+    if (col < c) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(xq + ((int64_t)col * nsb + sb) * Q8_BYTES);
+      hd = src[0];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = src[1 + i];
+    }
+    uint32_t* dst = xs + (col * bpr + (sb >> 2)) * XB_WORDS + (sb & 3) * 8;
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      dst[i] = q[i];
+      sum = __builtin_amdgcn_sdot4((int)q[i], 0x01010101, sum, false);
+    }
+    xsum[col * nsb + sb] = sum;
+    xd[col * nsb + sb] = f16_to_f32(hd & 0xFFFFu);
+  }
+}
+
+// One PTQ1_0 block (its 7 words in v) against the staged activations of
+// block bx of the row: acc[col] += d_w * sum_s4 d_x * (sum u q - sum q).
+// lt is this lane's copy of the digit table.
+template <int C>
+__device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_t* lt,
+                                           const uint32_t* xs, const int* xsum, const float* xd,
+                                           int bx, int bpr, int nsb, float (&acc)[C]) {
+  // decode the 128 digits into 32 dwords in k order (dg[i] = elements 4i..4i+3)
+  uint32_t dg[32];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {  // qs bytes 0..15: element 16 j + b
+    const uint32_t l0 = lt[(v[g] & 0xFF) * LUT_COPIES], l1 = lt[((v[g] >> 8) & 0xFF) * LUT_COPIES];
+    const uint32_t l2 = lt[((v[g] >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(v[g] >> 24) * LUT_COPIES];
+    uint32_t d0, d1, d2, d3, d4;
+    transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
+    dg[g] = d0; dg[4 + g] = d1; dg[8 + g] = d2; dg[12 + g] = d3; dg[16 + g] = d4;
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {  // qs bytes 16..23: element 80 + 8 j + b
+    const uint32_t x = v[4 + g];
+    const uint32_t l0 = lt[(x & 0xFF) * LUT_COPIES], l1 = lt[((x >> 8) & 0xFF) * LUT_COPIES];
+    const uint32_t l2 = lt[((x >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(x >> 24) * LUT_COPIES];
+    uint32_t d0, d1, d2, d3, d4;
+    transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
+    dg[20 + g] = d0; dg[22 + g] = d1; dg[24 + g] = d2; dg[26 + g] = d3; dg[28 + g] = d4;
+  }
+  {
+    const uint32_t h = v[6] & 0xFFFFu;  // qh: elements 120..127
+    dg[30] = (h | (h << 14)) & 0x03030303u;
+    dg[31] = ((h >> 4) | (h << 10)) & 0x03030303u;
+  }
+  const float dw = f16_to_f32(v[6] >> 16);  // 0 for blocks past the end
+#pragma unroll
+  for (int col = 0; col < C; ++col) {
+    const uint4* xv = reinterpret_cast<const uint4*>(xs + (col * bpr + bx) * XB_WORDS);
+    float part = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {  // activation block within the 128
+      const uint4 x0 = xv[2 * s4], x1 = xv[2 * s4 + 1];
+      int sacc = -xsum[col * nsb + bx * 4 + s4];
+      sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 0], (int)x0.x, sacc, false);
+      sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 1], (int)x0.y, sacc, false);
+      sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 2], (int)x0.z, sacc, false);
+      sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 3], (int)x0.w, sacc, false);
+      sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 4], (int)x1.x, sacc, false);
+      sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 5], (int)x1.y, sacc, false);
+      sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 6], (int)x1.z, sacc, false);
+      sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 7], (int)x1.w, sacc, false);
+      part = fmaf(xd[col * nsb + bx * 4 + s4], (float)sacc, part);
+    }
+    acc[col] = fmaf(dw, part, acc[col]);
+  }
+}
+
 // dynamic LDS: table [256][16], x [C][bpr][36 words], sum q [C][k/32], d [C][k/32]
 // LPR lanes per row (8 or 16): a wave holds 64 / LPR rows, a lane one block
 // of its row per item (an item = LPR consecutive blocks of each row).
@@ -313,32 +409,7 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
   for (int d = 0; d < D; ++d) issue(d, d);
 
   // ---- one-time staging: digit table and the activations
-  {
-    const uint32_t v = tid;
-    const uint32_t ent = (v % 3) | ((v / 3) % 3) << 8 | ((v / 9) % 3) << 16 | ((v / 27) % 3) << 24 |
-                         ((v / 81) % 3) << 4;  // entries >= 243 are never indexed by valid data
-#pragma unroll
-    for (int cpy = 0; cpy < LUT_COPIES; ++cpy) lut[tid * LUT_COPIES + cpy] = ent;
-  }
-  for (int idx = tid; idx < C * nsb; idx += 256) {
-    const int col = idx / nsb, sb = idx - col * nsb;
-    uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0}, hd = 0;
-    if (col < c) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(xq + ((int64_t)col * nsb + sb) * Q8_BYTES);
-      hd = src[0];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = src[1 + i];
-    }
-    uint32_t* dst = xs + (col * bpr + (sb >> 2)) * XB_WORDS + (sb & 3) * 8;
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      dst[i] = q[i];
-      sum = __builtin_amdgcn_sdot4((int)q[i], 0x01010101, sum, false);
-    }
-    xsum[col * nsb + sb] = sum;
-    xd[col * nsb + sb] = f16_to_f32(hd & 0xFFFFu);
-  }
+  tern_stage<C>(lut, xs, xsum, xd, xq, bpr, nsb, c);
   __syncthreads();
 
   float acc[C];
@@ -355,53 +426,8 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
     for (int q = 0; q < 7; ++q) v[q] = wd[slot][q];
     issue(slot, i + D);  // the slot is free once copied out
     if (i >= nitems) return;  // uniform; no load below
-    // decode the 128 digits into 32 dwords in k order (dg[i] = elements 4i..4i+3)
-    const uint32_t* lt = lut + (lane & (LUT_COPIES - 1));
-    uint32_t dg[32];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {  // qs bytes 0..15: element 16 j + b
-      const uint32_t l0 = lt[(v[g] & 0xFF) * LUT_COPIES], l1 = lt[((v[g] >> 8) & 0xFF) * LUT_COPIES];
-      const uint32_t l2 = lt[((v[g] >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(v[g] >> 24) * LUT_COPIES];
-      uint32_t d0, d1, d2, d3, d4;
-      transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
-      dg[g] = d0; dg[4 + g] = d1; dg[8 + g] = d2; dg[12 + g] = d3; dg[16 + g] = d4;
-    }
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {  // qs bytes 16..23: element 80 + 8 j + b
-      const uint32_t x = v[4 + g];
-      const uint32_t l0 = lt[(x & 0xFF) * LUT_COPIES], l1 = lt[((x >> 8) & 0xFF) * LUT_COPIES];
-      const uint32_t l2 = lt[((x >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(x >> 24) * LUT_COPIES];
-      uint32_t d0, d1, d2, d3, d4;
-      transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
-      dg[20 + g] = d0; dg[22 + g] = d1; dg[24 + g] = d2; dg[26 + g] = d3; dg[28 + g] = d4;
-    }
-    {
-      const uint32_t h = v[6] & 0xFFFFu;  // qh: elements 120..127
-      dg[30] = (h | (h << 14)) & 0x03030303u;
-      dg[31] = ((h >> 4) | (h << 10)) & 0x03030303u;
-    }
-    const float dw = f16_to_f32(v[6] >> 16);  // 0 for blocks past the end
-    const int bx = blk < bpr ? blk : 0;      // keeps x reads inside the staged range
-#pragma unroll
-    for (int col = 0; col < C; ++col) {
-      const uint4* xv = reinterpret_cast<const uint4*>(xs + (col * bpr + bx) * XB_WORDS);
-      float part = 0.f;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {  // activation block within the 128
-        const uint4 x0 = xv[2 * s4], x1 = xv[2 * s4 + 1];
-        int sacc = -xsum[col * nsb + bx * 4 + s4];
-        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 0], (int)x0.x, sacc, false);
-        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 1], (int)x0.y, sacc, false);
-        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 2], (int)x0.z, sacc, false);
-        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 3], (int)x0.w, sacc, false);
-        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 4], (int)x1.x, sacc, false);
-        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 5], (int)x1.y, sacc, false);
-        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 6], (int)x1.z, sacc, false);
-        sacc = __builtin_amdgcn_sdot4((int)dg[8 * s4 + 7], (int)x1.w, sacc, false);
-        part = fmaf(xd[col * nsb + bx * 4 + s4], (float)sacc, part);
-      }
-      acc[col] = fmaf(dw, part, acc[col]);
-    }
+    // blocks past the end loaded zeros (scale 0); x reads stay in the staged range
+    tern_block<C>(v, lut + (lane & (LUT_COPIES - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
     if (t == ntiles - 1) {  // uniform: the wave leaves its 8-row group
       const int row = (gw + (i / ntiles) * nw) * RPW + lane / LPR;
 #pragma unroll
@@ -420,6 +446,96 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
   for (int i = 0; i < nitems; i += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) item(i + d, d);
+  }
+}
+
+// K-split variant for the narrowest batches.  With one 8-row group per wave,
+// a single column leaves about two waves per SIMD (N = 17280 gives 2160
+// groups), too few to hide the latencies of the digit-table reads and the
+// permutes.  Here the tiles of each row group are split between S waves of
+// one workgroup (4 / S row groups per 256-lane workgroup, not persistent), so
+// S times more waves run, and the S partial sums of a row are added in LDS in
+// part order.
+template <int C, int D, int S>
+__global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_ksplit(const uint32_t* __restrict__ w,
+                                                             const uint8_t* __restrict__ xq,
+                                                             float* __restrict__ out, int n, int k,
+                                                             int c) {
+  constexpr int LPR = 8, RPW = 64 / LPR;
+  extern __shared__ uint32_t tsm[];
+  const int nsb = k / 32;
+  const int bpr = k / 128;
+  uint32_t* lut = tsm;                                    // [256][LUT_COPIES]
+  uint32_t* xs = tsm + 256 * LUT_COPIES;                  // [C][bpr][XB_WORDS]
+  int* xsum = reinterpret_cast<int*>(xs + C * bpr * XB_WORDS);  // [C][nsb]
+  float* xd = reinterpret_cast<float*>(xsum + C * nsb);   // [C][nsb]
+  float* psum = xd + C * nsb;                             // [4 waves][RPW rows][C]
+
+  const int tid = threadIdx.x, lane = tid & 63, sub = lane & (LPR - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int part = wave % S;
+  const int rg = (int)blockIdx.x * (4 / S) + wave / S;
+  const int row = rg * RPW + lane / LPR;
+  const int ntiles = (bpr + LPR - 1) / LPR;
+  const int tps = (ntiles + S - 1) / S;                   // tiles per part
+  const int t0 = part * tps;
+  const int nitems = max(0, min(ntiles, t0 + tps) - t0);  // this wave's tiles
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)w, 0, (int)((int64_t)n * bpr * PT_BYTES), 0x00020000);
+
+  // weight ring: item i = tile t0 + i of the row group
+  uint32_t wd[D][7];
+  auto issue = [&](int slot, int i) {
+    const int blk = (t0 + i) * LPR + sub;
+    const bool ok = i < nitems && row < n && blk < bpr;
+    const uint32_t o = ok ? (uint32_t)((row * bpr + blk) * PT_BYTES) : T_OOB;
+#pragma unroll
+    for (int q = 0; q < 7; ++q)
+      wd[slot][q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * q), 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, d);
+
+  tern_stage<C>(lut, xs, xsum, xd, xq, bpr, nsb, c);
+  __syncthreads();
+
+  float acc[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) acc[j] = 0.f;
+  auto item = [&](const int i, const int slot) {
+    uint32_t v[7];
+#pragma unroll
+    for (int q = 0; q < 7; ++q) v[q] = wd[slot][q];
+    issue(slot, i + D);       // the slot is free once copied out
+    if (i >= nitems) return;  // uniform; no load below
+    const int blk = (t0 + i) * LPR + sub;
+    tern_block<C>(v, lut + (lane & (LUT_COPIES - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
+  };
+  for (int i = 0; i < nitems; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) item(i + d, d);
+  }
+
+  // this part's row sums (the lanes of a row, fixed order) -> LDS; part 0
+  // adds the parts in order
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    float v = acc[j];
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    if (sub == 0) psum[(wave * RPW + lane / LPR) * C + j] = v;
+  }
+  __syncthreads();
+  if (part == 0 && sub == 0 && row < n) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if (j >= c) break;
+      float v = psum[(wave * RPW + lane / LPR) * C + j];
+#pragma unroll
+      for (int p2 = 1; p2 < S; ++p2) v += psum[((wave + p2) * RPW + lane / LPR) * C + j];
+      out[(int64_t)j * n + row] = v;
+    }
   }
 }
 
@@ -455,6 +571,34 @@ int cu_count_t() {
 
 constexpr int TP_D = 4;  // items in flight per lane
 
+#ifndef WQ_T_KSPLIT_CMAX
+#define WQ_T_KSPLIT_CMAX 1  // widest batch routed to the K-split kernel
+#endif
+
+// K-split launch (S = 2) when x fits in LDS; returns hipErrorInvalidValue (no
+// launch) otherwise.
+template <int C>
+hipError_t launch_ternary_ksplit(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k,
+                                 int64_t c, float* out, hipStream_t s) {
+  constexpr int S = 2;
+  const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8 +
+                      4 * 8 * C * 4;
+  if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
+    return hipErrorInvalidValue;
+  static bool attr_set = false;  // one per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t nrg = (n + 7) / 8;
+  const int64_t grid = (nrg + (4 / S) - 1) / (4 / S);
+  hipLaunchKernelGGL((k_gemv_ternary_ksplit<C, TP_D, S>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
+                     wp, xq, out, (int)n, (int)k, (int)c);
+  return hipGetLastError();
+}
+
 // Persistent launch when x fits in LDS; returns hipErrorInvalidValue (no
 // launch) otherwise.
 template <int C>
@@ -487,6 +631,20 @@ hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, i
     // (a single column runs slightly faster on the tiled kernel below, whose
     // per-tile staging is small at c = 1)
     hipError_t e = hipErrorInvalidValue;
+    if (c <= WQ_T_KSPLIT_CMAX) {
+      switch (c) {
+        case 1: e = launch_ternary_ksplit<1>(wp0, xq, n, k, c, out, s); break;
+#if WQ_T_KSPLIT_CMAX >= 2
+        case 2: e = launch_ternary_ksplit<2>(wp0, xq, n, k, c, out, s); break;
+#endif
+#if WQ_T_KSPLIT_CMAX >= 3
+        default: e = launch_ternary_ksplit<4>(wp0, xq, n, k, c, out, s); break;
+#else
+        default: break;
+#endif
+      }
+      if (e != hipErrorInvalidValue) return e;
+    }
     switch (c) {
       case 1: break;
       case 2: e = launch_ternary_persist<2>(wp0, xq, n, k, c, out, s); break;

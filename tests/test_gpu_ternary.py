@@ -75,14 +75,17 @@ def test_ternary_gemv(k, n):
         check_f32(gpu_gemv(wb, xq, k), ot.gemv_ternary(wref, xref))
 
 
-@pytest.mark.parametrize("k,n", [(5120, 4000), (17280, 300)])
-def test_ternary_unit_scale_exact(k, n):
-    say("ternary unit scale", k, n)
+@pytest.mark.parametrize("k,n,c", [(5120, 4000, 8), (17280, 300, 8), (5120, 4000, 1), (384, 77, 1),
+                                   (17280, 300, 1)])
+def test_ternary_unit_scale_exact(k, n, c):
+    # c = 1 runs the kernel that splits each row's blocks between two waves
+    # (k = 384: three blocks, so the second wave of a row has none)
+    say("ternary unit scale", k, n, c)
     p = wq_inputs.ternary_gemv(k, n, cmax=8, unit_scale=True)
     wb = gpu_blocks(p.trits, p.d_bits)
-    xq = gpu_q8(p.x)
+    xq = gpu_q8(p.x[:c])
     got = gpu_gemv(wb, xq, k)
-    exact = p.x.astype(np.int64) @ p.trits.astype(np.int64).T
+    exact = p.x[:c].astype(np.int64) @ p.trits.astype(np.int64).T
     assert np.array_equal(got, exact.astype(np.float64))
 
 
