@@ -12,6 +12,7 @@
 namespace wq {
 namespace {
 
+
 // Eight codes c[0..7] (k order, one per byte of lo/hi) -> one packed word.
 __device__ __forceinline__ uint32_t pack_word(uint32_t lo, uint32_t hi, int layout) {
   uint32_t c0 = lo & 15u, c1 = (lo >> 8) & 15u, c2 = (lo >> 16) & 15u, c3 = (lo >> 24) & 15u;
@@ -99,6 +100,108 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const uint16_t* __restric
   }
 }
 
+// Single-pass quantiser: one team of TEAM lanes per (row, group), each lane
+// holding WPL 16-byte words (8 fp16 weights each) of the group in registers.
+//
+// code = clamp(rint(RN(w / s)), -8, 7) + 8 needs the correctly rounded
+// float32 quotient only where rounding to an integer can tell it apart from
+// a nearby value.  The quotient is formed from r = RN(1 / s) with one
+// residual correction (Markstein's FMA division step: y = w r,
+// e = w - s y exactly by FMA, q = y + e r), which is RN(w / s) or one ulp
+// from it.  rint(q) can differ from rint(RN(w / s)) only when one of them
+// lies on a half-integer or they straddle one, so any lane whose q is within
+// 2^-19 (two ulps below 8) of a half-integer sends its wave through the exact
+// IEEE divide instead.  |w / s| < 7.1 and s is a normal number, so nothing
+// over- or underflows.
+__device__ __forceinline__ uint32_t pack8(const int (&c)[8], int layout) {
+  if (layout == 0)
+    return c[0] | c[1] << 4 | c[2] << 8 | c[3] << 12 | c[4] << 16 | c[5] << 20 | c[6] << 24 | c[7] << 28;
+  return c[0] | c[2] << 4 | c[4] << 8 | c[6] << 12 | c[1] << 16 | c[3] << 20 | c[5] << 24 | c[7] << 28;
+}
+
+template <int TEAM, int WPL>
+__global__ __launch_bounds__(256) void k_quantize_pack_r(const uint16_t* __restrict__ w,
+                                                         uint32_t* __restrict__ packed,
+                                                         void* __restrict__ scales, int n,
+                                                         int ngroups, int64_t k, int group,
+                                                         int layout, int scale_bf16) {
+  constexpr int TPW = 256 / TEAM;  // teams per workgroup
+  const int tid = threadIdx.x, lane = tid % TEAM;
+  const int unit = (int)blockIdx.x * TPW + tid / TEAM;  // (row, group); n * ngroups < 2^31
+  const bool active = unit < n * ngroups;
+  const int u = active ? unit : 0;
+  const int row = u / ngroups, g = u - row * ngroups;
+  const int gw = group / 8;  // words per group
+  const uint16_t* src = w + (int64_t)row * k + (int64_t)g * group;
+
+  uint4 v[WPL];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < WPL; ++i) {
+    const int j = lane + TEAM * i;
+    v[i] = j < gw ? *reinterpret_cast<const uint4*>(src + 8 * j) : make_uint4(0, 0, 0, 0);
+    const uint32_t h[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, fabsf(f16_to_f32(h[e] & 0xFFFFu)));
+      amax = fmaxf(amax, fabsf(f16_to_f32(h[e] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = TEAM / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, TEAM));
+
+  const float s32 = amax / 7.0f;  // IEEE divide
+  uint32_t sbits = 0;
+  float s = s32;
+  if (scale_bf16) {
+    sbits = f32_to_bf16_rne(s32);
+    s = bf16_to_f32(sbits);
+  }
+  if (active && lane == 0) {
+    if (scale_bf16)
+      reinterpret_cast<uint16_t*>(scales)[u] = (uint16_t)sbits;
+    else
+      reinterpret_cast<float*>(scales)[u] = s;
+  }
+  const float r = 1.0f / s;  // IEEE; +inf when s == 0 (codes are then 8)
+  uint32_t word[WPL];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < WPL; ++i) {
+    const uint32_t h[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    int c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = f16_to_f32(e & 1 ? h[e >> 1] >> 16 : h[e >> 1] & 0xFFFFu);
+      const float y = x * r;
+      const float q = fmaf(fmaf(-y, s, x), r, y);
+      near |= fabsf(__builtin_amdgcn_fractf(q) - 0.5f) <= 0x1p-19f;
+      c[e] = (int)__builtin_amdgcn_fmed3f(rintf(q), -8.f, 7.f) + 8;
+    }
+    word[i] = pack8(c, layout);
+  }
+  if (__builtin_amdgcn_ballot_w64(near) != 0) {  // uniform: exact quotients
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+      const uint32_t h[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      int c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = f16_to_f32(e & 1 ? h[e >> 1] >> 16 : h[e >> 1] & 0xFFFFu);
+        c[e] = (int)fminf(fmaxf(rintf(x / s), -8.f), 7.f) + 8;
+      }
+      word[i] = pack8(c, layout);
+    }
+  }
+  if (!active) return;
+  uint32_t* dst = packed + ((int64_t)row * k + (int64_t)g * group) / 8;
+#pragma unroll
+  for (int i = 0; i < WPL; ++i) {
+    const int j = lane + TEAM * i;
+    if (j < gw) dst[j] = s == 0.f ? 0x88888888u : word[i];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pack_int4(const uint8_t* codes, int64_t n, int64_t k, int layout,
@@ -118,6 +221,30 @@ hipError_t launch_quantize_pack_int4(const uint16_t* w, int64_t n, int64_t k, in
   int64_t units = n * (k / group);
   uint32_t* out = reinterpret_cast<uint32_t*>(packed);
   int sb = scale_bf16 ? 1 : 0;
+  // single pass with the group in registers: 8 lanes per group of up to 64
+  // words (4 lanes for 4 words), 64 lanes per group of up to 512 words;
+  // larger groups take the two-pass kernel below
+  if (units < (int64_t(1) << 30) && group < (int64_t(1) << 30) && gw <= 8 * 64) {
+    const int team = gw <= 4 ? 4 : gw <= 64 ? 8 : 64;
+    const int64_t wpl = (gw + team - 1) / team;  // 1..8
+    const int wsel = wpl <= 1 ? 1 : wpl <= 2 ? 2 : wpl <= 4 ? 4 : 8;
+    const unsigned blocks = (unsigned)((units * team + 255) / 256);
+#define WQ_QR(T, W)                                                                         \
+  hipLaunchKernelGGL((k_quantize_pack_r<T, W>), dim3(blocks), dim3(256), 0, s, w, out, scales, \
+                     (int)n, (int)(k / group), k, (int)group, layout, sb)
+    bool launched = true;
+    if (team == 4) WQ_QR(4, 1);
+    else if (team == 8 && wsel == 1) WQ_QR(8, 1);
+    else if (team == 8 && wsel == 2) WQ_QR(8, 2);
+    else if (team == 8 && wsel == 4) WQ_QR(8, 4);
+    else if (team == 8 && wsel == 8) WQ_QR(8, 8);
+    else if (team == 64 && wsel == 2) WQ_QR(64, 2);
+    else if (team == 64 && wsel == 4) WQ_QR(64, 4);
+    else if (team == 64 && wsel == 8) WQ_QR(64, 8);
+    else launched = false;
+#undef WQ_QR
+    if (launched) return hipGetLastError();
+  }
 #define WQ_QP(T)                                                                         \
   do {                                                                                   \
     int64_t blocks = (units * T + 255) / 256;                                            \

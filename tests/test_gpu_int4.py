@@ -116,6 +116,24 @@ def test_quantize_edge_cases(group, sdt):
     _quant_case(wq_inputs.to_f16_bits(w), group, sdt, 1)
 
 
+@pytest.mark.parametrize("group,k", [(32, 256), (64, 512), (256, 1024), (512, 2048), (96, 96),
+                                     (1024, 1024), (2048, 2048), (4096, 4096), (4352, 4352)])
+def test_quantize_every_team_shape(group, k):
+    # one case per register layout of the single-pass quantiser (4, 8 or 64
+    # lanes per group holding 1..8 words each; 96 = a per-row group of 12
+    # words, not a multiple of the lanes) and the two-pass kernel past 512
+    # words; exact ties and a zero group in every case
+    rng = np.random.default_rng(group + k)
+    n = 37
+    w = 0.02 * rng.standard_normal((n, k))
+    w[0, :min(group, k)] = 0.0
+    w[1, :8] = [7.0, 0.5, 1.5, 2.5, -0.5, -2.5, 3.25, -6.75]
+    w[2, -8:] = [-7.0, 3.5, -4.5, 5.5, 6.5, -1.5, 0.0, 2.0]
+    say("quantize team shape", group, k)
+    for sdt in ("bf16", "f32"):
+        _quant_case(wq_inputs.to_f16_bits(w), group, sdt, 1)
+
+
 # ---------------------------------------------------------------- GEMV
 def test_gemv_tiny_per_row_fp32():
     p = wq_inputs.tiny_int4()
