@@ -332,7 +332,16 @@ def secondary_rows(g, torch, np, wq_inputs, dev, log):
     rows["gemm_w4a16_8192"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
                                "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)}
     log("gemm 8192^3:", json.dumps(rows["gemm_w4a16_8192"]))
-    del a, b, c
+    # the same product with group-128 bf16 scales (the quantiser's output
+    # layout), drawn like the decode workload's scales
+    qg = wq_inputs.grouped_gemm(8, q.n, q.k, 128)
+    sg = torch.from_numpy(qg.scale_bits).view(torch.bfloat16).to(dev)
+    ms = timed(torch, lambda i: g.wq_gemm_w4a16(a, b, 1, sg, 128, 8.0, c), 10)
+    tf = 2.0 * q.m * q.n * q.k / (ms * 1e-3) / 1e12
+    rows["gemm_w4a16_8192_group128"] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                                        "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)}
+    log("gemm 8192^3, group 128:", json.dumps(rows["gemm_w4a16_8192_group128"]))
+    del a, b, c, sg
     torch.cuda.empty_cache()
 
     # ternary GEMV, K=5120 N=17280
