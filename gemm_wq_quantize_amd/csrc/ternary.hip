@@ -272,12 +272,8 @@ constexpr int TP_LPR = WQ_T_LPR;
 constexpr int LUT_COPIES = 16;
 constexpr int XB_WORDS = 36;  // words per padded 128-element x block
 
-// One-time staging of a workgroup's LDS: the digit table in LUT_COPIES
-// interleaved copies and the activations (x blocks padded to XB_WORDS words,
-// per-32 sum of q and d).  Columns c..C-1 stage zeros.
-template <int C>
-__device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsum, float* xd,
-                                           const uint8_t* __restrict__ xq, int bpr, int nsb, int c) {
+// The digit table in LUT_COPIES interleaved copies (256 threads).
+__device__ __forceinline__ void tern_lut_init(uint32_t* lut) {
   const int tid = threadIdx.x;
   {
     // Thread t owns entry t (words 16 t .. 16 t + 15) and writes its copies
@@ -293,6 +289,16 @@ __device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsu
       *reinterpret_cast<uint4*>(lut + tid * LUT_COPIES + 4 * ((m + (tid >> 2)) & 3)) =
           make_uint4(ent, ent, ent, ent);
   }
+}
+
+// One-time staging of a workgroup's LDS: the digit table in LUT_COPIES
+// interleaved copies and the activations (x blocks padded to XB_WORDS words,
+// per-32 sum of q and d).  Columns c..C-1 stage zeros.
+template <int C>
+__device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsum, float* xd,
+                                           const uint8_t* __restrict__ xq, int bpr, int nsb, int c) {
+  tern_lut_init(lut);
+  const int tid = threadIdx.x;
   for (int idx = tid; idx < C * nsb; idx += 256) {
     const int col = idx / nsb, sb = idx - col * nsb;
     uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0}, hd = 0;
@@ -317,12 +323,11 @@ __device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsu
 // One PTQ1_0 block (its 7 words in v) against the staged activations of
 // block bx of the row: acc[col] += d_w * sum_s4 d_x * (sum u q - sum q).
 // lt is this lane's copy of the digit table.
-template <int C>
-__device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_t* lt,
-                                           const uint32_t* xs, const int* xsum, const float* xd,
-                                           int bx, int bpr, int nsb, float (&acc)[C]) {
-  // decode the 128 digits into 32 dwords in k order (dg[i] = elements 4i..4i+3)
-  uint32_t dg[32];
+// The 128 digits u = t + 1 of one block (its 7 words in v) in k order:
+// dg[i] holds elements 4i..4i+3, one per byte.  lt is this lane's copy of
+// the digit table.
+__device__ __forceinline__ void tern_decode(const uint32_t (&v)[7], const uint32_t* lt,
+                                            uint32_t (&dg)[32]) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {  // qs bytes 0..15: element 16 j + b
     const uint32_t l0 = lt[(v[g] & 0xFF) * LUT_COPIES], l1 = lt[((v[g] >> 8) & 0xFF) * LUT_COPIES];
@@ -345,6 +350,14 @@ __device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_
     dg[30] = (h | (h << 14)) & 0x03030303u;
     dg[31] = ((h >> 4) | (h << 10)) & 0x03030303u;
   }
+}
+
+template <int C>
+__device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_t* lt,
+                                           const uint32_t* xs, const int* xsum, const float* xd,
+                                           int bx, int bpr, int nsb, float (&acc)[C]) {
+  uint32_t dg[32];
+  tern_decode(v, lt, dg);
   const float dw = f16_to_f32(v[6] >> 16);  // 0 for blocks past the end
 #pragma unroll
   for (int col = 0; col < C; ++col) {
@@ -539,6 +552,187 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_ksplit(const u
   }
 }
 
+// ---- ternary x q8_1 GEMM on the int8 matrix cores (64 or more columns)
+//
+// y[c][r] = sum_b d_w[r][b] sum_j d_x[c][4b + j] S[c][r][b][j] with the
+// exact sub-block sums S = sum_i t q over 32 k.  One v_mfma_i32_32x32x32_i8
+// covers exactly one 32-k q8_1 block, so it yields S for a 32 x 32 tile in
+// int32; the weights are the A operand (rows r) and x the B operand (columns
+// c), so the x scale of a result is the same for a whole lane (its column)
+// and is applied right after each product, the weight scale once per 128-k
+// block.  A 256-lane workgroup computes a 128 (r) x 128 (c) tile, a wave
+// 64 x 64 (2 x 2 products per 32 k); per 128-k step half the lanes decode one
+// weight block each into int8 trits (the GEMV's table decode, then u - 1)
+// and the other half copy four q8_1 blocks of one x row, into LDS rows padded
+// to 144 bytes (the 16 rows a ds_read_b128 cycle serves fall in distinct bank
+// quads).  The next step's global words are loaded into registers while this
+// step multiplies.
+constexpr int TG_B = 128;      // tile rows (weights) and columns (x)
+constexpr int TG_PITCH = 144;  // LDS bytes per operand row: 128 k + 16
+
+__global__ __launch_bounds__(256, 1) void k_gemm_ternary(const uint32_t* __restrict__ w,
+                                                         const uint8_t* __restrict__ xq,
+                                                         float* __restrict__ out, int n, int k,
+                                                         int m, int tiles_m) {
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * LUT_COPIES];
+  __shared__ __attribute__((aligned(16))) uint8_t wt[TG_B * TG_PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t xt[TG_B * TG_PITCH];
+  __shared__ __attribute__((aligned(16))) float dws[TG_B];
+  __shared__ __attribute__((aligned(16))) float dxs[TG_B * 4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave >> 1, wm = wave & 1;   // the wave's 64-row / 64-column quarter
+  const int bpr = k / 128, nsb = k / 32;
+  const int tm = (int)blockIdx.x % tiles_m, tn = (int)blockIdx.x / tiles_m;
+  const int n0 = tn * TG_B, m0 = tm * TG_B;
+
+  // load roles: lanes 0..127 fetch weight row n0 + t (one 28-byte block per
+  // step), lanes 128..255 x row m0 + t - 128 (four 36-byte blocks per step,
+  // 144 contiguous 16-byte-aligned bytes: a row is k / 32 * 36 bytes, a
+  // multiple of 144)
+  const bool wl = tid < TG_B;
+  const int lr = wl ? tid : tid - TG_B;
+  const int grow = (wl ? n0 : m0) + lr;
+  const bool rowok = grow < (wl ? n : m);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)w, 0, (int)((int64_t)n * bpr * PT_BYTES), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)xq, 0, (int)((int64_t)m * nsb * Q8_BYTES), 0x00020000);
+  uint32_t pre[36];
+  auto fetch = [&](int kb) {  // words of step kb into pre
+    if (wl) {
+      const uint32_t o = rowok ? (uint32_t)((grow * bpr + kb) * PT_BYTES) : T_OOB;
+#pragma unroll
+      for (int q = 0; q < 7; ++q) pre[q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * q), 0, 0);
+    } else {
+      const uint32_t o = rowok ? (uint32_t)((grow * nsb + 4 * kb) * Q8_BYTES) : T_OOB;
+#pragma unroll
+      for (int q = 0; q < 9; ++q) {
+        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(o + 16 * q), 0, 0));
+        pre[4 * q] = v.x; pre[4 * q + 1] = v.y; pre[4 * q + 2] = v.z; pre[4 * q + 3] = v.w;
+      }
+    }
+  };
+  auto put = [&]() {  // pre -> LDS operands of the step
+    if (wl) {
+      uint32_t v[7];
+#pragma unroll
+      for (int q = 0; q < 7; ++q) v[q] = pre[q];
+      uint32_t dg[32];
+      tern_decode(v, lut + (lane & (LUT_COPIES - 1)), dg);
+      uint4* dst = reinterpret_cast<uint4*>(wt + lr * TG_PITCH);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // digits u in {0,1,2} per byte -> trits u - 1 (no byte carries: u + 0x7F <= 0x81)
+        uint32_t t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = (dg[4 * i + e] + 0x7F7F7F7Fu) ^ 0x80808080u;
+        dst[i] = make_uint4(t[0], t[1], t[2], t[3]);
+      }
+      dws[lr] = f16_to_f32(v[6] >> 16);  // 0 for rows past n (zero block)
+    } else {
+      uint4* dst = reinterpret_cast<uint4*>(xt + lr * TG_PITCH);
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        dst[2 * sb] = make_uint4(pre[9 * sb + 1], pre[9 * sb + 2], pre[9 * sb + 3], pre[9 * sb + 4]);
+        dst[2 * sb + 1] = make_uint4(pre[9 * sb + 5], pre[9 * sb + 6], pre[9 * sb + 7], pre[9 * sb + 8]);
+        dxs[lr * 4 + sb] = f16_to_f32(pre[9 * sb] & 0xFFFFu);
+      }
+    }
+  };
+
+  fetch(0);
+  tern_lut_init(lut);
+  __syncthreads();
+
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  typedef int i32x16 __attribute__((ext_vector_type(16)));
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+  const int l32 = lane & 31, lh = lane >> 5;
+
+  for (int kb = 0; kb < bpr; ++kb) {
+    put();
+    __syncthreads();
+    if (kb + 1 < bpr) fetch(kb + 1);
+    f32x16 tacc[2][2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tacc[bi][bj][e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // 32-k sub-block: one q8_1 block of every column
+      i32x4 af[2], bf[2];
+      float dx[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+        af[bi] = *reinterpret_cast<const i32x4*>(wt + (wn * 64 + bi * 32 + l32) * TG_PITCH + 32 * j + 16 * lh);
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) {
+        const int col = wm * 64 + bj * 32 + l32;
+        bf[bj] = *reinterpret_cast<const i32x4*>(xt + col * TG_PITCH + 32 * j + 16 * lh);
+        dx[bj] = dxs[col * 4 + j];
+      }
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+          const i32x16 z = {};
+          const i32x16 sacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[bi], bf[bj], z, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) tacc[bi][bj][e] = fmaf(dx[bj], (float)sacc[e], tacc[bi][bj][e]);
+        }
+    }
+    // weight scales of this lane's 16 result rows (8 (e / 4) + 4 lh + e % 4)
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      float dw[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 v = *reinterpret_cast<const float4*>(dws + wn * 64 + bi * 32 + 8 * g + 4 * lh);
+        dw[4 * g] = v.x; dw[4 * g + 1] = v.y; dw[4 * g + 2] = v.z; dw[4 * g + 3] = v.w;
+      }
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[bi][bj][e] = fmaf(dw[e], tacc[bi][bj][e], acc[bi][bj][e]);
+    }
+    __syncthreads();  // operands of this step are no longer read
+  }
+
+  // y[c][r]: lane column c, rows r = 8 (e / 4) + 4 lh + e % 4 (four consecutive)
+  const bool vec_ok = (n & 3) == 0;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int col = m0 + wm * 64 + bj * 32 + l32;
+      if (col >= m) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = n0 + wn * 64 + bi * 32 + 8 * g + 4 * lh;
+        float* dst = out + (int64_t)col * n + r;
+        const f32x16& a = acc[bi][bj];
+        if (vec_ok && r + 3 < n) {
+          *reinterpret_cast<float4*>(dst) = make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r + e < n) dst[e] = a[4 * g + e];
+        }
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
@@ -627,6 +821,12 @@ hipError_t launch_ternary_persist(const uint32_t* wp, const uint8_t* xq, int64_t
 hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s) {
   const uint32_t* wp0 = reinterpret_cast<const uint32_t*>(w);
+  if (c >= 64) {  // a batch wide enough for the int8 matrix cores
+    const int tiles_m = (int)((c + TG_B - 1) / TG_B), tiles_n = (int)((n + TG_B - 1) / TG_B);
+    hipLaunchKernelGGL(k_gemm_ternary, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, wp0, xq,
+                       out, (int)n, (int)k, (int)c, tiles_m);
+    return hipGetLastError();
+  }
   {
     // (a single column runs slightly faster on the tiled kernel below, whose
     // per-tile staging is small at c = 1)

@@ -73,6 +73,11 @@ def test_validation_errors_without_gpu(lib):
     assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 96, 8.0, 64, 64, 96, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 100, 1, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 128, 17, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 128, 63, FAKE, None) == g.WQ_ESHAPE
+    # 32-bit offsets of the matrix-core path: 2^22 rows of 32 blocks is 3.8 GB
+    # of weights; 2^20 columns of 128 q8_1 blocks is 4.8 GB of activations
+    assert lib.wq_gemv_ternary(FAKE, FAKE, 1 << 22, 4096, 64, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary(FAKE, FAKE, 64, 4096, 1 << 20, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_pack_ptq1_0(FAKE, FAKE, 2, 64, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_quantize_q8_1(FAKE, 2, 48, FAKE, None) == g.WQ_ESHAPE
     # unsupported combinations
@@ -88,3 +93,4 @@ def test_validation_errors_without_gpu(lib):
     # group scales are read as aligned 4-byte words
     assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, P(0x1002), 128, 8.0, 64, 64, 256, FAKE, None) == g.WQ_EALIGN
     assert lib.wq_gemv_ternary(ODD, FAKE, 4, 128, 1, FAKE, None) == g.WQ_EALIGN
+    assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 128, 64, P(0x1004), None) == g.WQ_EALIGN

@@ -104,3 +104,29 @@ def test_ternary_special_cases():
             assert np.all(got == 0)
         else:
             check_f32(got, ref)
+
+
+# ---- 64 or more columns: the int8 matrix-core kernel
+@pytest.mark.parametrize("k,n,c", [(1024, 256, 64), (640, 333, 200), (5120, 2048, 128),
+                                   (384, 77, 130)])
+def test_ternary_gemm(k, n, c):
+    # ragged tiles in both directions; n = 333 and 77 take the scalar stores
+    say("ternary gemm", k, n, c)
+    p = wq_inputs.ternary_gemv(k, n, cmax=c, seed=c + n)
+    wb = gpu_blocks(p.trits, p.d_bits)
+    xq = gpu_q8(p.x)
+    xref = ot.quantize_q8_1(p.x)
+    assert np.array_equal(xq.cpu().numpy(), xref)
+    check_f32(gpu_gemv(wb, xq, k), ot.gemv_ternary(ot.encode_ptq1_0(p.trits, p.d_bits), xref))
+
+
+@pytest.mark.parametrize("k,n,c", [(1024, 300, 64), (5120, 200, 129)])
+def test_ternary_gemm_unit_scale_exact(k, n, c):
+    # unit scales and integer x: the int32 products and the float32 sums are
+    # exact, so the result is the integer product bit for bit
+    say("ternary gemm unit scale", k, n, c)
+    p = wq_inputs.ternary_gemv(k, n, cmax=c, unit_scale=True)
+    wb = gpu_blocks(p.trits, p.d_bits)
+    got = gpu_gemv(wb, gpu_q8(p.x), k)
+    exact = p.x.astype(np.int64) @ p.trits.astype(np.int64).T
+    assert np.array_equal(got, exact.astype(np.float64))
