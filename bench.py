@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4 GEMV weight GB/s (% of HBM peak); W4A16 GEMM TFLOP/s (% of MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
 
@@ -362,6 +363,18 @@ def secondary_rows(g, torch, np, wq_inputs, dev, log):
             "frac_hbm": round(wb.numel() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     rows["gemv_ternary"] = trow
     log("ternary:", json.dumps(trow))
+    # 4096 activation columns: the int8 matrix-core path (2 int8 ops per MAC)
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    mg = 4096
+    xg = torch.empty((mg, 160, 36), dtype=torch.uint8, device=dev)
+    g.wq_quantize_q8_1(torch.randn(mg, 5120, generator=gen).to(dev), xg)
+    yg = torch.empty((mg, 17280), dtype=torch.float32, device=dev)
+    ms = timed(torch, lambda i: g.wq_gemv_ternary(wcs[i % nc], xg, 5120, yg), 5)
+    tops = 2.0 * mg * 17280 * 5120 / (ms * 1e-3) / 1e12
+    rows["gemm_ternary_4096"] = {"ms": round(ms, 4), "TOPs": round(tops, 1),
+                                 "frac_mfma_int8": round(tops / INT8_PEAK_TOPS, 4)}
+    log("ternary gemm 4096 x 17280 x 5120:", json.dumps(rows["gemm_ternary_4096"]))
+    del xg, yg
     return rows
 
 

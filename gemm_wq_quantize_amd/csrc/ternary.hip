@@ -559,92 +559,96 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_ksplit(const u
 // covers exactly one 32-k q8_1 block, so it yields S for a 32 x 32 tile in
 // int32; the weights are the A operand (rows r) and x the B operand (columns
 // c), so the x scale of a result is the same for a whole lane (its column)
-// and is applied right after each product, the weight scale once per 128-k
-// block.  A 256-lane workgroup computes a 128 (r) x 128 (c) tile, a wave
-// 64 x 64 (2 x 2 products per 32 k); per 128-k step half the lanes decode one
-// weight block each into int8 trits (the GEMV's table decode, then u - 1)
-// and the other half copy four q8_1 blocks of one x row, into LDS rows padded
-// to 144 bytes (the 16 rows a ds_read_b128 cycle serves fall in distinct bank
-// quads).  The next step's global words are loaded into registers while this
-// step multiplies.
-constexpr int TG_B = 128;      // tile rows (weights) and columns (x)
+// and is applied right after each product (a convert and an FMA per result:
+// the per-32 activation scales keep this path VALU-heavy), the weight scale
+// once per 128-k block.
+//
+// A 512-lane workgroup computes a 256 (r) x 128 (c) tile, a wave 64 x 64 (2 x
+// 2 products per 32 k; two waves per SIMD keep a wave within the 256 VGPRs
+// the VALU can address).  Per 128-k step lanes 0..255 each decode the block
+// of one weight row into int8 trits (the GEMV's table decode, then u - 1)
+// and lanes 256..383 each copy the four q8_1 blocks of one x row, into LDS
+// rows padded to 144 bytes (the 16 rows a ds_read_b128 cycle serves fall in
+// distinct bank quads); waves w and w + 4 share a SIMD, so every SIMD holds
+// one decoding wave.  Two LDS stages: step t + 1 is decoded and stored while step t
+// multiplies, with one barrier per step, and the global words of step t + 2
+// are loaded into registers meanwhile.
+constexpr int TG_BN = 256;     // weight rows per tile
+constexpr int TG_BM = 128;     // x rows per tile
 constexpr int TG_PITCH = 144;  // LDS bytes per operand row: 128 k + 16
+constexpr int TG_WST = TG_BN * TG_PITCH;  // bytes per weight stage
+constexpr int TG_XST = TG_BM * TG_PITCH;  // bytes per x stage
 
-__global__ __launch_bounds__(256, 1) void k_gemm_ternary(const uint32_t* __restrict__ w,
+__global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restrict__ w,
                                                          const uint8_t* __restrict__ xq,
                                                          float* __restrict__ out, int n, int k,
                                                          int m, int tiles_m) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * LUT_COPIES];
-  __shared__ __attribute__((aligned(16))) uint8_t wt[TG_B * TG_PITCH];
-  __shared__ __attribute__((aligned(16))) uint8_t xt[TG_B * TG_PITCH];
-  __shared__ __attribute__((aligned(16))) float dws[TG_B];
-  __shared__ __attribute__((aligned(16))) float dxs[TG_B * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t wt[2 * TG_WST];
+  __shared__ __attribute__((aligned(16))) uint8_t xt[2 * TG_XST];
+  __shared__ __attribute__((aligned(16))) float dws[2 * TG_BN];
+  __shared__ __attribute__((aligned(16))) float dxs[2 * TG_BM * 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave >> 1, wm = wave & 1;   // the wave's 64-row / 64-column quarter
+  const int wn = wave >> 1, wm = wave & 1;  // the wave's 64 weight rows, 64 x rows
   const int bpr = k / 128, nsb = k / 32;
   const int tm = (int)blockIdx.x % tiles_m, tn = (int)blockIdx.x / tiles_m;
-  const int n0 = tn * TG_B, m0 = tm * TG_B;
+  const int n0 = tn * TG_BN, m0 = tm * TG_BM;
 
-  // load roles: lanes 0..127 fetch weight row n0 + t (one 28-byte block per
-  // step), lanes 128..255 x row m0 + t - 128 (four 36-byte blocks per step,
-  // 144 contiguous 16-byte-aligned bytes: a row is k / 32 * 36 bytes, a
+  // lanes 0..255: weight row n0 + t (one 28-byte block per step); lanes
+  // 256..383: x row m0 + t - 256 (four 36-byte blocks per step: 144
+  // contiguous bytes, 16-byte aligned since a row is k / 32 * 36 bytes, a
   // multiple of 144)
-  const bool wl = tid < TG_B;
-  const int lr = wl ? tid : tid - TG_B;
-  const int grow = (wl ? n0 : m0) + lr;
-  const bool rowok = grow < (wl ? n : m);
+  const bool wl = tid < TG_BN;
+  const bool xl = tid >= TG_BN && tid < TG_BN + TG_BM;
+  const int wrow = n0 + tid, xrow = m0 + tid - TG_BN;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)w, 0, (int)((int64_t)n * bpr * PT_BYTES), 0x00020000);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)xq, 0, (int)((int64_t)m * nsb * Q8_BYTES), 0x00020000);
-  uint32_t pre[36];
-  auto fetch = [&](int kb) {  // words of step kb into pre
+  uint32_t pw[7], px[36];
+  auto fetch = [&](int kb) {  // global words of step kb
     if (wl) {
-      const uint32_t o = rowok ? (uint32_t)((grow * bpr + kb) * PT_BYTES) : T_OOB;
+      const uint32_t ow = wrow < n ? (uint32_t)((wrow * bpr + kb) * PT_BYTES) : T_OOB;
 #pragma unroll
-      for (int q = 0; q < 7; ++q) pre[q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * q), 0, 0);
-    } else {
-      const uint32_t o = rowok ? (uint32_t)((grow * nsb + 4 * kb) * Q8_BYTES) : T_OOB;
+      for (int q = 0; q < 7; ++q) pw[q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(ow + 4 * q), 0, 0);
+    }
+    if (xl) {
+      const uint32_t ox = xrow < m ? (uint32_t)((xrow * nsb + 4 * kb) * Q8_BYTES) : T_OOB;
 #pragma unroll
       for (int q = 0; q < 9; ++q) {
-        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(o + 16 * q), 0, 0));
-        pre[4 * q] = v.x; pre[4 * q + 1] = v.y; pre[4 * q + 2] = v.z; pre[4 * q + 3] = v.w;
+        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(ox + 16 * q), 0, 0));
+        px[4 * q] = v.x; px[4 * q + 1] = v.y; px[4 * q + 2] = v.z; px[4 * q + 3] = v.w;
       }
     }
   };
-  auto put = [&]() {  // pre -> LDS operands of the step
+  auto put = [&](int st) {  // registers -> LDS stage st
     if (wl) {
-      uint32_t v[7];
-#pragma unroll
-      for (int q = 0; q < 7; ++q) v[q] = pre[q];
       uint32_t dg[32];
-      tern_decode(v, lut + (lane & (LUT_COPIES - 1)), dg);
-      uint4* dst = reinterpret_cast<uint4*>(wt + lr * TG_PITCH);
+      tern_decode(pw, lut + (lane & (LUT_COPIES - 1)), dg);
+      uint4* dst = reinterpret_cast<uint4*>(wt + st * TG_WST + tid * TG_PITCH);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        // digits u in {0,1,2} per byte -> trits u - 1 (no byte carries: u + 0x7F <= 0x81)
+        // digits u in {0,1,2} per byte -> trits u - 1 (no carries: u + 0x7F <= 0x81)
         uint32_t t[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) t[e] = (dg[4 * i + e] + 0x7F7F7F7Fu) ^ 0x80808080u;
         dst[i] = make_uint4(t[0], t[1], t[2], t[3]);
       }
-      dws[lr] = f16_to_f32(v[6] >> 16);  // 0 for rows past n (zero block)
-    } else {
-      uint4* dst = reinterpret_cast<uint4*>(xt + lr * TG_PITCH);
+      dws[st * TG_BN + tid] = f16_to_f32(pw[6] >> 16);  // 0 for rows past n (zero block)
+    }
+    if (xl) {
+      const int xr = tid - TG_BN;
+      uint4* xd = reinterpret_cast<uint4*>(xt + st * TG_XST + xr * TG_PITCH);
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
-        dst[2 * sb] = make_uint4(pre[9 * sb + 1], pre[9 * sb + 2], pre[9 * sb + 3], pre[9 * sb + 4]);
-        dst[2 * sb + 1] = make_uint4(pre[9 * sb + 5], pre[9 * sb + 6], pre[9 * sb + 7], pre[9 * sb + 8]);
-        dxs[lr * 4 + sb] = f16_to_f32(pre[9 * sb] & 0xFFFFu);
+        xd[2 * sb] = make_uint4(px[9 * sb + 1], px[9 * sb + 2], px[9 * sb + 3], px[9 * sb + 4]);
+        xd[2 * sb + 1] = make_uint4(px[9 * sb + 5], px[9 * sb + 6], px[9 * sb + 7], px[9 * sb + 8]);
+        dxs[st * TG_BM * 4 + xr * 4 + sb] = f16_to_f32(px[9 * sb] & 0xFFFFu);
       }
     }
   };
-
-  fetch(0);
-  tern_lut_init(lut);
-  __syncthreads();
 
   typedef float f32x16 __attribute__((ext_vector_type(16)));
   typedef int i32x16 __attribute__((ext_vector_type(16)));
@@ -658,55 +662,64 @@ __global__ __launch_bounds__(256, 1) void k_gemm_ternary(const uint32_t* __restr
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int l32 = lane & 31, lh = lane >> 5;
 
-  for (int kb = 0; kb < bpr; ++kb) {
-    put();
-    __syncthreads();
-    if (kb + 1 < bpr) fetch(kb + 1);
-    f32x16 tacc[2][2];
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) tacc[bi][bj][e] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {  // 32-k sub-block: one q8_1 block of every column
-      i32x4 af[2], bf[2];
-      float dx[2];
-#pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
-        af[bi] = *reinterpret_cast<const i32x4*>(wt + (wn * 64 + bi * 32 + l32) * TG_PITCH + 32 * j + 16 * lh);
-#pragma unroll
-      for (int bj = 0; bj < 2; ++bj) {
-        const int col = wm * 64 + bj * 32 + l32;
-        bf[bj] = *reinterpret_cast<const i32x4*>(xt + col * TG_PITCH + 32 * j + 16 * lh);
-        dx[bj] = dxs[col * 4 + j];
-      }
-#pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj) {
-          const i32x16 z = {};
-          const i32x16 sacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[bi], bf[bj], z, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) tacc[bi][bj][e] = fmaf(dx[bj], (float)sacc[e], tacc[bi][bj][e]);
-        }
-    }
-    // weight scales of this lane's 16 result rows (8 (e / 4) + 4 lh + e % 4)
+  // Per row block bi: its 8 products (sub-block j, column block bj) with
+  // the x scale applied to each product's int32 sums, then the weight scales
+  // of its rows.  The j loop is not unrolled, so at most two products' sums
+  // are live (unrolled, the compiler issued all 16 products of a step at
+  // once and spilled their results).
+  auto compute = [&](int st) {
+    const uint8_t* ws = wt + st * TG_WST;
+    const uint8_t* xs = xt + st * TG_XST;
+    const uint8_t* wrow0 = ws + (wn * 64 + l32) * TG_PITCH + 16 * lh;
+    const uint8_t* xcol0 = xs + (wm * 64 + l32) * TG_PITCH + 16 * lh;
+    const float* dxc = dxs + st * TG_BM * 4 + (wm * 64 + l32) * 4;
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
+      f32x16 t0, t1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t0[e] = t1[e] = 0.f;
+#pragma unroll 1
+      for (int j = 0; j < 4; ++j) {  // 32-k sub-block: one q8_1 block of every column
+        const i32x4 af = *reinterpret_cast<const i32x4*>(wrow0 + bi * 32 * TG_PITCH + 32 * j);
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(xcol0 + 32 * j);
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(xcol0 + 32 * TG_PITCH + 32 * j);
+        const float dx0 = dxc[j], dx1 = dxc[32 * 4 + j];
+        const i32x16 z = {};
+        const i32x16 s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b0, z, 0, 0, 0);
+        const i32x16 s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b1, z, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t0[e] = fmaf(dx0, (float)s0[e], t0[e]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t1[e] = fmaf(dx1, (float)s1[e], t1[e]);
+      }
+      // weight scales of this lane's 16 result rows (8 (e / 4) + 4 lh + e % 4)
       float dw[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 v = *reinterpret_cast<const float4*>(dws + wn * 64 + bi * 32 + 8 * g + 4 * lh);
+        const float4 v = *reinterpret_cast<const float4*>(dws + st * TG_BN + wn * 64 + bi * 32 + 8 * g + 4 * lh);
         dw[4 * g] = v.x; dw[4 * g + 1] = v.y; dw[4 * g + 2] = v.z; dw[4 * g + 3] = v.w;
       }
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[bi][bj][e] = fmaf(dw[e], tacc[bi][bj][e], acc[bi][bj][e]);
+      for (int e = 0; e < 16; ++e) {
+        acc[bi][0][e] = fmaf(dw[e], t0[e], acc[bi][0][e]);
+        acc[bi][1][e] = fmaf(dw[e], t1[e], acc[bi][1][e]);
+      }
     }
-    __syncthreads();  // operands of this step are no longer read
+  };
+
+  fetch(0);
+  if (tid < 256) tern_lut_init(lut);
+  __syncthreads();
+  put(0);
+  if (bpr > 1) fetch(1);
+  __syncthreads();
+  for (int kb = 0; kb < bpr; ++kb) {
+    compute(kb & 1);
+    if (kb + 1 < bpr) {
+      put((kb + 1) & 1);  // the other stage: every wave finished step kb - 1 at the last barrier
+      if (kb + 2 < bpr) fetch(kb + 2);
+    }
+    __syncthreads();
   }
 
   // y[c][r]: lane column c, rows r = 8 (e / 4) + 4 lh + e % 4 (four consecutive)
@@ -822,8 +835,8 @@ hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, i
                                int64_t c, float* out, hipStream_t s) {
   const uint32_t* wp0 = reinterpret_cast<const uint32_t*>(w);
   if (c >= 64) {  // a batch wide enough for the int8 matrix cores
-    const int tiles_m = (int)((c + TG_B - 1) / TG_B), tiles_n = (int)((n + TG_B - 1) / TG_B);
-    hipLaunchKernelGGL(k_gemm_ternary, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, wp0, xq,
+    const int tiles_m = (int)((c + TG_BM - 1) / TG_BM), tiles_n = (int)((n + TG_BN - 1) / TG_BN);
+    hipLaunchKernelGGL(k_gemm_ternary, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s, wp0, xq,
                        out, (int)n, (int)k, (int)c, tiles_m);
     return hipGetLastError();
   }
