@@ -29,6 +29,7 @@ _SIGS = {
     "wq_quantize_pack_int4": ([_p, _i64, _i64, _i64, _i, _p, _p, _i, _p], _i),
     "wq_gemv_w4": ([_p, _i, _p, _i, _p, _f, _i64, _i64, _i64, _p, _i, _i64, _p, _i, _p], _i),
     "wq_gemm_w4a16": ([_p, _p, _i, _p, _i64, _f, _i64, _i64, _i64, _p, _p], _i),
+    "wq_gemm_w4a16_zp": ([_p, _p, _i, _p, _p, _i64, _i64, _i64, _i64, _p, _p], _i),
     "wq_pack_ptq1_0": ([_p, _p, _i64, _i64, _p, _p], _i),
     "wq_quantize_q8_1": ([_p, _i64, _i64, _p, _p], _i),
     "wq_gemv_ternary": ([_p, _p, _i64, _i64, _i64, _p, _p], _i),
@@ -145,6 +146,20 @@ def wq_gemm_w4a16(a, b, layout, scales, group, zero_const, c_out, stream=None):
     _check("wq_gemm_w4a16",
            lib.wq_gemm_w4a16(_ptr(a), _ptr(b), layout, _ptr(scales), group, float(zero_const),
                              m, n, k, _ptr(c_out), _stream(stream)))
+
+
+def wq_gemm_w4a16_zp(a, b, layout, scales, zeros, group, c_out, stream=None):
+    """C[m][n] = sum_k A[m][k] (q[n][k] - z[n][k/group]) s[n][k/group] with stored
+    bf16 zeros of the scales' shape."""
+    m, k = a.shape
+    n = b.shape[0]
+    assert a.dtype == torch.bfloat16 and c_out.dtype == torch.bfloat16 and b.dtype == torch.uint8
+    assert b.numel() == n * k // 2 and c_out.numel() == m * n
+    assert scales.dtype == torch.bfloat16 and zeros.dtype == torch.bfloat16
+    assert zeros.numel() == scales.numel() == n * (k // group)
+    _check("wq_gemm_w4a16_zp",
+           lib.wq_gemm_w4a16_zp(_ptr(a), _ptr(b), layout, _ptr(scales), _ptr(zeros), group,
+                                m, n, k, _ptr(c_out), _stream(stream)))
 
 
 def wq_pack_ptq1_0(trits, d, blocks, stream=None):

@@ -24,6 +24,28 @@ int hip_status(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_EHIP; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+
+// shared validation and launch of the two GEMM entry points (zeros nullable)
+int gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* scales,
+               const uint16_t* zeros, int64_t group, float zero_const, int64_t m, int64_t n,
+               int64_t k, uint16_t* c_out, void* stream) {
+  if (m < 0 || n < 0 || k < 0 || group < 0) return WQ_EINVAL;
+  if (layout != WQ_LAYOUT_PLAIN && layout != WQ_LAYOUT_GFX950) return WQ_EINVAL;
+  if (m == 0 || n == 0) return WQ_OK;
+  if (!a || !b || !scales || !c_out) return WQ_EINVAL;
+  if (k == 0 || k % 64 != 0 || k > (int64_t(1) << 22)) return WQ_ESHAPE;  // 32-bit tile offsets
+  // one scale per column, or per group of a power-of-two multiple of 64 k
+  if (!valid_group(group, k)) return WQ_ESHAPE;
+  const bool grouped = group != k;
+  if (grouped && group < 64) return WQ_EUNSUPPORTED;  // a 64-k step must lie in one group
+  if (layout != WQ_LAYOUT_GFX950) return WQ_EUNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c_out, 16) ||
+      !aligned(scales, grouped ? 4 : 2) || (zeros && !aligned(zeros, grouped ? 4 : 2)))
+    return WQ_EALIGN;
+  if (((m + 255) / 256) * ((n + 255) / 256) > kMaxGrid) return WQ_ESHAPE;
+  return hip_status(wq::launch_gemm_w4a16(a, b, scales, zeros, group, zero_const, m, n, k, c_out,
+                                          as_stream(stream)));
+}
 }  // namespace
 
 extern "C" {
@@ -102,25 +124,18 @@ int wq_gemv_w4(const uint8_t* packed, int layout, const void* scales, int scale_
   return hip_status(wq::launch_gemv_w4(a, as_stream(stream)));
 }
 
+
 int wq_gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* scales,
                   int64_t group, float zero_const, int64_t m, int64_t n, int64_t k,
                   uint16_t* c_out, void* stream) {
-  if (m < 0 || n < 0 || k < 0 || group < 0) return WQ_EINVAL;
-  if (layout != WQ_LAYOUT_PLAIN && layout != WQ_LAYOUT_GFX950) return WQ_EINVAL;
-  if (m == 0 || n == 0) return WQ_OK;
-  if (!a || !b || !scales || !c_out) return WQ_EINVAL;
-  if (k == 0 || k % 64 != 0 || k > (int64_t(1) << 22)) return WQ_ESHAPE;  // 32-bit tile offsets
-  // one scale per column, or per group of a power-of-two multiple of 64 k
-  if (!valid_group(group, k)) return WQ_ESHAPE;
-  const bool grouped = group != k;
-  if (grouped && group < 64) return WQ_EUNSUPPORTED;  // a 64-k step must lie in one group
-  if (layout != WQ_LAYOUT_GFX950) return WQ_EUNSUPPORTED;
-  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c_out, 16) ||
-      !aligned(scales, grouped ? 4 : 2))
-    return WQ_EALIGN;
-  if (((m + 255) / 256) * ((n + 255) / 256) > kMaxGrid) return WQ_ESHAPE;
-  return hip_status(wq::launch_gemm_w4a16(a, b, scales, group, zero_const, m, n, k, c_out,
-                                          as_stream(stream)));
+  return gemm_w4a16(a, b, layout, scales, nullptr, group, zero_const, m, n, k, c_out, stream);
+}
+
+int wq_gemm_w4a16_zp(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* scales,
+                     const uint16_t* zeros, int64_t group, int64_t m, int64_t n, int64_t k,
+                     uint16_t* c_out, void* stream) {
+  if (!zeros && m > 0 && n > 0) return WQ_EINVAL;
+  return gemm_w4a16(a, b, layout, scales, zeros, group, 0.f, m, n, k, c_out, stream);
 }
 
 int wq_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k, uint8_t* blocks,

@@ -56,8 +56,11 @@ constexpr int B_STAGE = BN * BK / 2;          // bytes: 256 rows x 32 B
 constexpr int S_STAGE = BN * 4;               // bytes: one scale word per column
 // stage size and loads per lane per stage: 40 KiB and 10 (8 A + 2 B) with
 // one scale per column; 41 KiB and 11 (+1 scale word) with group scales
-template <bool GS> constexpr int stage_bytes() { return A_STAGE + B_STAGE + (GS ? S_STAGE : 0); }
-template <bool GS> constexpr int loads_per_stage() { return 10 + (GS ? 1 : 0); }
+// (stored zeros with group scales, GZ: one more word per column and load)
+template <bool GS, bool GZ> constexpr int stage_bytes() {
+  return A_STAGE + B_STAGE + (GS ? S_STAGE : 0) + (GZ ? S_STAGE : 0);
+}
+template <bool GS, bool GZ> constexpr int loads_per_stage() { return 10 + (GS ? 1 : 0) + (GZ ? 1 : 0); }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -65,6 +68,7 @@ struct GArgs {
   const uint16_t* a;
   const uint8_t* b;
   const uint16_t* scales;
+  const uint16_t* zeros;  // nullable: [n] or [n][k/group] bf16 zero points
   uint16_t* c;
   int64_t m, n, k;
   float zero_const;
@@ -172,16 +176,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // padded by 16 bytes so that the two rows one 2-byte LDS write touches (4
 // apart) fall in different banks.
 constexpr int C_PITCH = BN * 2 + 16;
-static_assert(128 * C_PITCH <= NSTAGE * stage_bytes<false>(), "epilogue staging fits the ring");
+static_assert(128 * C_PITCH <= NSTAGE * stage_bytes<false, false>(), "epilogue staging fits the ring");
 
 // One workgroup tile.  WN (the wave's column half) is a template argument so
 // that the row-sum split below indexes fragments at compile time; GS selects
 // group scales (applied while unpacking B) over one scale per column
 // (applied in the epilogue).
-template <int WN, bool GS>
+template <int WN, bool GS, bool GZ>
 __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (*rsx)[4][32]) {
-  constexpr int STAGE = stage_bytes<GS>();
-  constexpr int LOADS_PER_STAGE = loads_per_stage<GS>();
+  static_assert(GS || !GZ, "stored zeros of groups come with group scales");
+  constexpr int STAGE = stage_bytes<GS, GZ>();
+  constexpr int LOADS_PER_STAGE = loads_per_stage<GS, GZ>();
   // ---- tile order: XCD-aware renumbering, then bands of 8 tile-rows
   const int nwg = p.tiles_m * p.tiles_n;
   int id = blockIdx.x;
@@ -212,6 +217,9 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // (and cannot cross a page); the half past the array is never used.
   const i32x4 srs = make_rsrc(GS ? (const void*)(p.scales + n0 * p.ngroups) : (const void*)p.scales,
                               GS ? (((uint32_t)rows_b * (uint32_t)p.ngroups * 2u + 3u) & ~3u) : 0u);
+  // stored zeros of the groups: the same layout, read the same way
+  const i32x4 zrs = make_rsrc(GZ ? (const void*)(p.zeros + n0 * p.ngroups) : (const void*)p.scales,
+                              GZ ? (((uint32_t)rows_b * (uint32_t)p.ngroups * 2u + 3u) & ~3u) : 0u);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   // ---- global -> LDS assignment.  Load i (0..7) of wave w fills A slots
@@ -247,7 +255,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // num_records: they read nothing from memory and fill an unused stage with
   // zeros.
   // loads [first, last) of step kt: 0..7 are A, 8 and 9 are B, 10 the
-  // group scales
+  // group scales, 11 the group zeros
   auto issue_part = [&](int kt, int first, int last) {
     const uint32_t st = lds0 + (uint32_t)(kt % NSTAGE) * STAGE;
     const bool live = kt < nk;
@@ -266,6 +274,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     if (GS && 10 >= first && 10 < last) {
       const uint32_t so = live ? ((s_voff + (uint32_t)(kt >> p.gshift) * 2u) & ~3u) : 0x80000000u;
       dma4(srs, so, __builtin_amdgcn_readfirstlane(st + A_STAGE + B_STAGE + (uint32_t)wave * 256));
+    }
+    if (GZ && 11 >= first && 11 < last) {
+      const uint32_t so = live ? ((s_voff + (uint32_t)(kt >> p.gshift) * 2u) & ~3u) : 0x80000000u;
+      dma4(zrs, so, __builtin_amdgcn_readfirstlane(st + A_STAGE + B_STAGE + S_STAGE + (uint32_t)wave * 256));
     }
   };
   auto issue = [&](int kt) { issue_part(kt, 0, LOADS_PER_STAGE); };
@@ -317,23 +329,26 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int j = 0; j < 4; ++j) bw[j] = *reinterpret_cast<const uint4*>(st + b_rd[j]);
   };
-  // group scales of this lane's four columns for step kt (raw words)
-  auto read_s = [&](int kt, uint32_t (&sw)[4]) {
+  // group scales (and zeros) of this lane's four columns for step kt (raw words)
+  auto read_s = [&](int kt, uint32_t (&sw)[4], uint32_t (&zw)[4]) {
     const uint8_t* st = smem + (kt % NSTAGE) * STAGE + A_STAGE + B_STAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
       sw[j] = *reinterpret_cast<const uint32_t*>(st + (WN * 128 + j * 32 + lr) * 4);
+      zw[j] = GZ ? *reinterpret_cast<const uint32_t*>(st + S_STAGE + (WN * 128 + j * 32 + lr) * 4) : 0u;
+    }
   };
   // word -> float scale and offset term: the scale of column n for group g
   // is the high half when n * groups + g is odd (n and lr share parity)
   const float zb = 128.f + p.zero_const;
   float gsc[4] = {0.f, 0.f, 0.f, 0.f}, gof[4] = {0.f, 0.f, 0.f, 0.f};
-  auto set_s = [&](int kt, const uint32_t (&sw)[4]) {
+  auto set_s = [&](int kt, const uint32_t (&sw)[4], const uint32_t (&zw)[4]) {
     const bool hi = (((lr & p.ngroups) ^ (kt >> p.gshift)) & 1) != 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       gsc[j] = __uint_as_float(hi ? (sw[j] & 0xFFFF0000u) : (sw[j] << 16));
-      gof[j] = -zb * gsc[j];
+      const float z = GZ ? 128.f + __uint_as_float(hi ? (zw[j] & 0xFFFF0000u) : (zw[j] << 16)) : zb;
+      gof[j] = -z * gsc[j];
     }
   };
   auto read_a = [&](int kt, int ks, bf16x8 (&af)[4]) {
@@ -418,10 +433,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   bf16x8 a0[4], a1[4];
   read_b(0, bw);
   if constexpr (GS) {
-    uint32_t sw[4];
+    uint32_t sw[4], zw[4];
     bf16x8 b0[4], b1[4];
-    read_s(0, sw);
-    set_s(0, sw);
+    read_s(0, sw, zw);
+    set_s(0, sw, zw);
     read_a(0, 0, a0);
     dq(bw, 0, b0);
     for (int kt = 0; kt < nk; ++kt) {
@@ -440,9 +455,9 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
       __syncthreads();
       issue_fenced(kt + 3, 0, 4);
       read_b(kt + 1, bw);  // bw's slices are all dequantised by now
-      read_s(kt + 1, sw);
+      read_s(kt + 1, sw, zw);
       read_a(kt + 1, 0, a0);
-      set_s(kt + 1, sw);
+      set_s(kt + 1, sw, zw);
       dq(bw, 0, b0);
       mm(a1, b1);
     }
@@ -486,11 +501,12 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // the accumulator with group scales), bf16 RNE; stage half the tile in
   // LDS, then write it with coalesced 16-byte stores.
   // Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  float sc[4];
+  float sc[4], zc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t col = n0 + WN * 128 + j * 32 + lr;
     sc[j] = GS ? 1.f : (col < p.n ? bf16_to_f32(p.scales[col]) : 0.f);
+    zc[j] = (!GS && p.zeros && col < p.n) ? 128.f + bf16_to_f32(p.zeros[col]) : zb;
   }
   const bool vec_ok = (p.n & 7) == 0;  // rows 16-byte aligned
 #pragma unroll
@@ -513,7 +529,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
         for (int e = 0; e < 16; ++e) {
           // staged row: 64 wm + 32 ii + local row
           const int srow = wm * 64 + ii * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
-          const float v = GS ? acc[i][j][e] : (acc[i][j][e] - zb * rsum[e]) * sc[j];
+          const float v = GS ? acc[i][j][e] : (acc[i][j][e] - zc[j] * rsum[e]) * sc[j];
           *reinterpret_cast<uint16_t*>(smem + srow * C_PITCH + col * 2) =
               (uint16_t)f32_to_bf16_rne(v);
         }
@@ -541,24 +557,25 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   }
 }
 
-template <bool GS>
+template <bool GS, bool GZ>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * stage_bytes<GS>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * stage_bytes<GS, GZ>()];
   __shared__ __attribute__((aligned(16))) float rsx[2][4][32];  // row sums [wm][row block][row]
   // wave-uniform branch (the wave index is moved to a scalar register)
-  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1, GS>(p, smem, rsx);
-  else gemm_tile<0, GS>(p, smem, rsx);
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1, GS, GZ>(p, smem, rsx);
+  else gemm_tile<0, GS, GZ>(p, smem, rsx);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_w4a16(const uint16_t* a, const uint8_t* b, const uint16_t* scales,
-                             int64_t group, float zero_const, int64_t m, int64_t n, int64_t k,
-                             uint16_t* c, hipStream_t s) {
+                             const uint16_t* zeros, int64_t group, float zero_const, int64_t m,
+                             int64_t n, int64_t k, uint16_t* c, hipStream_t s) {
   GArgs p;
   p.a = a;
   p.b = b;
   p.scales = scales;
+  p.zeros = zeros;
   p.c = c;
   p.m = m;
   p.n = n;
@@ -571,9 +588,11 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint8_t* b, const uint16_t
   while ((int64_t(BK) << p.gshift) < group) ++p.gshift;
   const unsigned nwg = (unsigned)(p.tiles_m * p.tiles_n);
   if (group == k)
-    hipLaunchKernelGGL(k_gemm_w4a16<false>, dim3(nwg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_w4a16<false, false>), dim3(nwg), dim3(256), 0, s, p);
+  else if (zeros)
+    hipLaunchKernelGGL((k_gemm_w4a16<true, true>), dim3(nwg), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(k_gemm_w4a16<true>, dim3(nwg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_w4a16<true, false>), dim3(nwg), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

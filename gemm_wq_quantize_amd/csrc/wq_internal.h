@@ -52,8 +52,8 @@ struct GemvArgs {
 hipError_t launch_gemv_w4(const GemvArgs& a, hipStream_t s);
 
 hipError_t launch_gemm_w4a16(const uint16_t* a, const uint8_t* b, const uint16_t* scales,
-                             int64_t group, float zero_const, int64_t m, int64_t n, int64_t k,
-                             uint16_t* c, hipStream_t s);
+                             const uint16_t* zeros, int64_t group, float zero_const, int64_t m,
+                             int64_t n, int64_t k, uint16_t* c, hipStream_t s);
 
 hipError_t launch_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
                               uint8_t* blocks, hipStream_t s);

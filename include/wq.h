@@ -157,6 +157,25 @@ int wq_gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_
                   uint16_t* c_out, void* stream);
 
 /*
+ * wq_gemm_w4a16_zp -- C[i][j] = sum_k A[i][k] * (q[j][k] - z[j][k / group]) * s[j][k / group]:
+ * wq_gemm_w4a16 with stored zero points instead of zero_const (the Vulkan
+ * post's dequantisation (q - zero) * scale with a zero per group; the same
+ * weights wq_gemv_w4 accepts with its zeros argument, for the prefill
+ * product).
+ *   zeros   bf16, the shape of scales ([n] when group == k, else
+ *           [n][k/group]); required (null is WQ_EINVAL), same alignment as
+ *           scales (4-byte with group scales, whose last word may be read
+ *           past the array as for scales).
+ * Everything else as wq_gemm_w4a16.  With one scale per column the zero
+ * folds out through A's row sums; with group scales each weight is rounded
+ * once, bf16_rne((q - z) * s), exact in float32 before the rounding for bf16 s
+ * and z.
+ */
+int wq_gemm_w4a16_zp(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* scales,
+                     const uint16_t* zeros, int64_t group, int64_t m, int64_t n, int64_t k,
+                     uint16_t* c_out, void* stream);
+
+/*
  * wq_pack_ptq1_0 -- trits and block scales to PTQ1_0 blocks.
  *   trits   [n][k] int8 in {-1, 0, 1} (other values: outside the contract).
  *   d       [n][k/128] fp16 bit patterns.

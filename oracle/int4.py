@@ -171,16 +171,20 @@ def gemv_w4(packed: np.ndarray, layout: int, scales: np.ndarray, zeros,
 
 
 def gemm_w4a16_rows(a_rows: np.ndarray, packed: np.ndarray, layout: int,
-                    scales: np.ndarray, zero_const: float, group: int) -> np.ndarray:
+                    scales: np.ndarray, zero_const: float, group: int,
+                    zeros=None) -> np.ndarray:
     """Selected rows of C = A * dequant(B)^T in fp64: C[m, n] = sum_k A[m, k] *
-    (q[n, k] - z) * s[n, k // group].  B is stored output-major [N][K/2]."""
+    (q[n, k] - z) * s[n, k // group], z the stored zero of the group when
+    ``zeros`` is given, else ``zero_const``.  B is stored output-major
+    [N][K/2]."""
     codes = unpack(packed, layout)
-    w = dequantize(codes, scales, None, zero_const, group)
+    w = dequantize(codes, scales, zeros, zero_const, group)
     return np.asarray(a_rows, dtype=np.float64) @ w.T
 
 
 def gemm_w4a16_rows_bf16w(a_rows: np.ndarray, packed: np.ndarray, layout: int,
-                          scales: np.ndarray, zero_const: float, group: int) -> np.ndarray:
+                          scales: np.ndarray, zero_const: float, group: int,
+                          zeros=None) -> np.ndarray:
     """Selected rows of C = A * W^T in fp64 where every weight is first
     rounded to bf16: W[n, k] = bf16_rne((q[n, k] - z) * s[n, k // group]).
 
@@ -188,9 +192,11 @@ def gemm_w4a16_rows_bf16w(a_rows: np.ndarray, packed: np.ndarray, layout: int,
     bf16 operands (Helion issue, ``matmul_bf16_int4``: B is converted to
     bf16 before the dot), so a group scale that varies along K is applied to
     the weight before the multiply, and the weight is rounded once.  (q - z)
-    * s is exact in float32 for bf16 s and integer z, so the rounding here is
-    the one bf16 rounding of the exact product."""
+    * s is exact in float32 for bf16 s and an integer or bf16 z (at most
+    about 17 significant bits), so the rounding here is the one bf16 rounding
+    of the exact product.  ``zeros``: stored zeros per group (Vulkan post,
+    section 2: (q - zero) * scale), else ``zero_const``."""
     codes = unpack(packed, layout)
-    w = dequantize(codes, scales, None, zero_const, group)
+    w = dequantize(codes, scales, zeros, zero_const, group)
     w16 = fpformat.bf16_bits_to_f32(fpformat.f32_to_bf16_bits(w.astype(np.float32)))
     return np.asarray(a_rows, dtype=np.float64) @ w16.astype(np.float64).T

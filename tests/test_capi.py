@@ -90,6 +90,9 @@ def test_validation_errors_without_gpu(lib):
     assert lib.wq_gemv_w4(ODD, 1, FAKE, 2, None, 8.0, 4, 128, 128, FAKE, 2, 1, FAKE, 2, None) == g.WQ_EALIGN
     assert lib.wq_quantize_pack_int4(FAKE, 4, 256, 128, 1, ODD, FAKE, 2, None) == g.WQ_EALIGN
     assert lib.wq_gemm_w4a16(ODD, FAKE, 1, FAKE, 128, 8.0, 64, 64, 128, FAKE, None) == g.WQ_EALIGN
+    # stored zeros are required by the _zp entry point, aligned like the scales
+    assert lib.wq_gemm_w4a16_zp(FAKE, FAKE, 1, FAKE, None, 128, 64, 64, 256, FAKE, None) == g.WQ_EINVAL
+    assert lib.wq_gemm_w4a16_zp(FAKE, FAKE, 1, FAKE, P(0x1002), 128, 64, 64, 256, FAKE, None) == g.WQ_EALIGN
     # group scales are read as aligned 4-byte words
     assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, P(0x1002), 128, 8.0, 64, 64, 256, FAKE, None) == g.WQ_EALIGN
     assert lib.wq_gemv_ternary(ODD, FAKE, 4, 128, 1, FAKE, None) == g.WQ_EALIGN

@@ -148,3 +148,57 @@ def test_gemm_on_quantiser_output():
     a = fpformat.bf16_bits_to_f32(a_bits)
     got = c.float().cpu().numpy()
     check_bf16_rows(got, o4.gemm_w4a16_rows_bf16w(a, o4.pack(codes, 1), 1, s, 8.0, 128))
+
+
+# ---- stored zero points (wq_gemm_w4a16_zp)
+def run_zp(a_bits, codes, scale_bits, zero_bits, group):
+    g = G()
+    m, k = a_bits.shape
+    n = codes.shape[0]
+    b = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda")
+    g.wq_pack_int4(torch.from_numpy(codes).cuda(), 1, b)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    g.wq_gemm_w4a16_zp(bf16_dev(a_bits), b, 1, bf16_dev(scale_bits), bf16_dev(zero_bits), group, c)
+    torch.cuda.synchronize()
+    return c
+
+
+@pytest.mark.parametrize("m,n,k,group", [(300, 520, 512, 128), (129, 333, 1152, 128),
+                                         (256, 200, 704, 704), (64, 1000, 2048, 2048)])
+def test_gemm_stored_zeros(m, n, k, group):
+    # zeros bf16 U(6, 9) of the scales' shape: group scales (weights rounded
+    # once to bf16) and one scale and zero per column (folded exactly)
+    say("gemm stored zeros", m, n, k, group)
+    p = wq_inputs.grouped_gemm(m, n, k, group, seed=m + n + 1)
+    rng = np.random.default_rng(m + k)
+    z_bits = fpformat.f32_to_bf16_bits(rng.uniform(6, 9, p.scale_bits.shape).astype(np.float32))
+    c = run_zp(p.a_bits, p.codes, p.scale_bits, z_bits, group).float().cpu().numpy()
+    a = fpformat.bf16_bits_to_f32(p.a_bits)
+    s = fpformat.bf16_bits_to_f32(p.scale_bits).reshape(n, k // group)
+    z = fpformat.bf16_bits_to_f32(z_bits).reshape(n, k // group)
+    packed = o4.pack(p.codes, 1)
+    exact = o4.gemm_w4a16_rows(a, packed, 1, s, 8.0, group, zeros=z)
+    if group == k:
+        check_bf16_rows(c, exact)
+    else:
+        check_bf16_rows(c, o4.gemm_w4a16_rows_bf16w(a, packed, 1, s, 8.0, group, zeros=z))
+        check_bf16_rownorm(c, exact)
+
+
+@pytest.mark.parametrize("group", [128, 1024])
+def test_gemm_stored_zeros_integer_exact(group):
+    # integer zeros 3..12 and power-of-two scales per group (or per column):
+    # exact weights and sums, so C is the RNE bf16 of the exact product
+    say("gemm stored zeros, integer exact", group)
+    rng = np.random.default_rng(17 + group)
+    m, n, k = 192, 264, 1024
+    a = rng.integers(-4, 5, (m, k)).astype(np.float32)
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    e = rng.integers(-2, 3, (n, k // group))
+    zi = rng.integers(3, 13, (n, k // group))
+    c = run_zp(fpformat.f32_to_bf16_bits(a), codes,
+               fpformat.f32_to_bf16_bits((2.0 ** e).astype(np.float32)),
+               fpformat.f32_to_bf16_bits(zi.astype(np.float32)), group)
+    w = (codes.astype(np.float64) - np.repeat(zi, group, axis=1)) * np.repeat(2.0 ** e, group, axis=1)
+    want = fpformat.f32_to_bf16_bits((a.astype(np.float64) @ w.T).astype(np.float32))
+    assert np.array_equal(c.view(torch.int16).cpu().numpy().view(np.uint16), want)

@@ -306,3 +306,25 @@ def test_gemm_bf16_weights_equal_exact_for_power_of_two_scales():
     # and against a per-element brute force of the group lookup
     w = np.array([[(int(codes[r, kk]) - 8) * s[r, kk // group] for kk in range(k)] for r in range(n)])
     assert np.allclose(ref, a @ w.T, rtol=0, atol=1e-12)
+
+
+def test_gemm_stored_zeros_brute_force():
+    # stored zeros per group (bf16-like fractional values): per-element brute
+    # force of (q - z[n, g]) * s[n, g]; and the bf16-weight variant rounds
+    # exactly those products
+    rng = np.random.default_rng(13)
+    m, n, k, group = 4, 9, 256, 64
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = fpformat.bf16_bits_to_f32(fpformat.f32_to_bf16_bits(rng.uniform(0.002, 0.02, (n, k // group)).astype(np.float32))).astype(np.float64)
+    z = fpformat.bf16_bits_to_f32(fpformat.f32_to_bf16_bits(rng.uniform(6, 9, (n, k // group)).astype(np.float32))).astype(np.float64)
+    a = rng.standard_normal((m, k))
+    p = int4.pack(codes, 1)
+    got = int4.gemm_w4a16_rows(a, p, 1, s, 8.0, group, zeros=z)
+    w = np.array([[(int(codes[r, kk]) - z[r, kk // group]) * s[r, kk // group] for kk in range(k)]
+                  for r in range(n)])
+    assert np.allclose(got, a @ w.T, rtol=0, atol=1e-12)
+    # the product is exact in float32, so the bf16 variant is the RNE of it
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+    w16 = fpformat.bf16_bits_to_f32(fpformat.f32_to_bf16_bits(w.astype(np.float32))).astype(np.float64)
+    assert np.allclose(int4.gemm_w4a16_rows_bf16w(a, p, 1, s, 8.0, group, zeros=z), a @ w16.T,
+                       rtol=0, atol=1e-12)
