@@ -760,10 +760,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int C, int LAYOUT, bool HZ, bool SBF>
-__global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) {
-  static_assert(C % 4 == 0 && C <= 16, "columns per pass");
-  constexpr int XC = C / 4;                              // x columns per wave and tile
+// CS (1 or 2): column sets per workgroup.  With CS = 2 the workgroup has 8
+// waves; waves w and w + 4 take the same 4 rows and the two halves of the
+// columns, so each SIMD runs two waves on one x tile (the two load the same
+// weights, which the CU's cache serves once).
+template <int C, int CS, int LAYOUT, bool HZ, bool SBF>
+__global__ __launch_bounds__(256 * CS, (C <= 8 && CS == 1) ? 2 : 1) void k_gemv_w4_batch(KArgs p) {
+  static_assert(C % (4 * CS) == 0 && C <= 16, "columns per pass");
+  constexpr int XC = C / (4 * CS);                       // x columns per wave and tile (loads)
+  constexpr int CW = C / CS;                             // columns per wave (products)
   constexpr int WLOADS = BT_RW * (HZ ? 3 : 2);           // loads per lane per weight tile
   constexpr int RG = 4 * BT_RW;                          // rows per row-group (workgroup item)
   __shared__ __attribute__((aligned(16))) uint4 xs[2][C * 4 * BT_CH];  // [buf][col][piece][chunk]
@@ -771,6 +776,7 @@ __global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave & 3, wc = wave >> 2;  // row slot, column set
   const int nchunks = (int)(p.k / 32);
   const int nt = (nchunks + BT_CH - 1) / BT_CH;
   const int rowbytes = (int)(p.k / 2);
@@ -791,7 +797,7 @@ __global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) 
   float sc[2][BT_RW], zb[2][BT_RW];
   auto issue_w = [&](int slot, int i) {
     const int t = i % nt, rg = w + (i / nt) * G;
-    const int64_t r0 = (int64_t)rg * RG + wave * BT_RW;
+    const int64_t r0 = (int64_t)rg * RG + wr * BT_RW;
     const int wrows = i < nitems ? (int)max<int64_t>(0, min<int64_t>(BT_RW, p.n - r0)) : 0;
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.packed + r0 * rowbytes), 0, wrows * rowbytes, 0x00020000);
@@ -822,15 +828,15 @@ __global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) 
   };
 
   // ---- x of item i's tile into buffer b: this wave fills chunk `lane` of
-  // columns wave + 4 j, all four 16-byte pieces (a wave instruction writes
-  // 64 consecutive 16-byte slots: one [col][piece] row of the buffer)
+  // columns wave + 4 CS j, all four 16-byte pieces (a wave instruction
+  // writes 64 consecutive 16-byte slots: one [col][piece] row of the buffer)
   auto dma_x = [&](int i, int b) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 4");  // VALU-written SGPRs (descriptor, LDS bases) read by the loads
     const int ch = (i % nt) * BT_CH + lane;
 #pragma unroll
     for (int j = 0; j < XC; ++j) {
-      const int col = wave + 4 * j;
+      const int col = wave + 4 * CS * j;
       const bool ok = i < nitems && ch < nchunks && col < p.c;
       // (OOB + 48 is still past num_records, which is below 2^31)
       const uint32_t base = ok ? (uint32_t)(((int64_t)col * p.k + (int64_t)ch * 32) * 2) : OOB;
@@ -849,7 +855,7 @@ __global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) 
   auto sum_x = [&](int b) {
 #pragma unroll
     for (int j = 0; j < XC; ++j) {
-      const int col = wave + 4 * j;
+      const int col = wave + 4 * CS * j;
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -863,30 +869,30 @@ __global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) 
     }
   };
 
-  float acc[BT_RW][C];
+  float acc[BT_RW][CW];
 #pragma unroll
   for (int r = 0; r < BT_RW; ++r)
 #pragma unroll
-    for (int j = 0; j < C; ++j) acc[r][j] = 0.f;
+    for (int j = 0; j < CW; ++j) acc[r][j] = 0.f;
   const uint32_t magic_v = vconst(0x43004300u);
 
   // sum each accumulator over the wave's 64 chunks (fixed DPP order); lane
-  // r * C + col stores row r, column col of the row-group
+  // r * CW + cc stores row r, column wc * CW + cc of the row-group
   auto finish_rowgroup = [&](int i) {
-    const int64_t r0 = (int64_t)(w + (i / nt) * G) * RG + wave * BT_RW;
+    const int64_t r0 = (int64_t)(w + (i / nt) * G) * RG + wr * BT_RW;
     float mine = 0.f;
 #pragma unroll
     for (int r = 0; r < BT_RW; ++r)
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
+      for (int jj = 0; jj < CW; ++jj) {
         const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                            __builtin_bit_cast(int, wave_sum(acc[r][j])), 63));
-        if (lane == r * C + j) mine = v;
-        acc[r][j] = 0.f;
+                            __builtin_bit_cast(int, wave_sum(acc[r][jj])), 63));
+        if (lane == r * CW + jj) mine = v;
+        acc[r][jj] = 0.f;
       }
-    const int r = lane / C, j = lane % C;
+    const int r = lane / CW, j = wc * CW + lane % CW;
     const int64_t row = r0 + r;
-    if (lane < BT_RW * C && j < p.c && row < p.n) {
+    if (lane < BT_RW * CW && j < p.c && row < p.n) {
       if (p.out_bf16)
         reinterpret_cast<uint16_t*>(p.out)[j * p.n + row] = (uint16_t)f32_to_bf16_rne(mine);
       else
@@ -934,7 +940,7 @@ __global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) 
       }
       sx = sxs[b][col * BT_CH + lane];
     };
-    auto mac = [&](int col, const uint32_t (&xv)[16], float sx) {
+    auto mac = [&](int cc, const uint32_t (&xv)[16], float sx) {  // cc: column within the set
       // four chains (one per row) interleaved in issue order, so
       // consecutive dot2 never depend on each other
       float d[BT_RW];
@@ -947,16 +953,17 @@ __global__ __launch_bounds__(256, C <= 8 ? 2 : 1) void k_gemv_w4_batch(KArgs p) 
           d[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[r][e]),
                                                  __builtin_bit_cast(bf16x2, xv[e]), d[r], false);
 #pragma unroll
-      for (int r = 0; r < BT_RW; ++r) acc[r][col] = fmaf(scr[r], d[r], acc[r][col]);
+      for (int r = 0; r < BT_RW; ++r) acc[r][cc] = fmaf(scr[r], d[r], acc[r][cc]);
     };
-    read_x(0, xa, sa);
+    const int c0 = wc * CW;
+    read_x(c0, xa, sa);
 #pragma unroll
-    for (int col = 0; col < C; col += 2) {
-      read_x(col + 1, xb, sb);
-      mac(col, xa, sa);
+    for (int cc = 0; cc < CW; cc += 2) {
+      read_x(c0 + cc + 1, xb, sb);
+      mac(cc, xa, sa);
       __builtin_amdgcn_sched_barrier(0);
-      if (col + 2 < C) read_x(col + 2, xa, sa);
-      mac(col + 1, xb, sb);
+      if (cc + 2 < CW) read_x(c0 + cc + 2, xa, sa);
+      mac(cc + 1, xb, sb);
       __builtin_amdgcn_sched_barrier(0);
     }
     // x of item i + 1 landed once only the weights of i + 2 are in flight
@@ -1113,15 +1120,23 @@ hipError_t launch_c(const KArgs& ka, int layout, hipStream_t s) {
   return launch_rc<1, C, XBF16>(ka, layout, s);
 }
 
+#ifndef WQ_B_CS16
+#define WQ_B_CS16 2  // column sets per workgroup for 16-column passes
+#endif
+#ifndef WQ_B_CS8
+#define WQ_B_CS8 1   // ... and for 8-column passes
+#endif
+
 template <int C>
 hipError_t launch_batch(const KArgs& ka, int layout, hipStream_t s) {
   // persistent grid: as many workgroups as fit at once (two per CU for 8
   // columns, one for 16), or one per row-group if there are fewer
+  constexpr int CS = C <= 8 ? WQ_B_CS8 : WQ_B_CS16;
   const int64_t nrg = (ka.n + 4 * BT_RW - 1) / (4 * BT_RW);
   const unsigned blocks = (unsigned)std::min<int64_t>(nrg, (int64_t)cu_count() * (C <= 8 ? 2 : 1));
   const bool hz = ka.zeros != nullptr, sb = ka.scale_bf16 != 0;
 #define WQ_BL(L, Z, S) \
-  hipLaunchKernelGGL((k_gemv_w4_batch<C, L, Z, S>), dim3(blocks), dim3(256), 0, s, ka)
+  hipLaunchKernelGGL((k_gemv_w4_batch<C, CS, L, Z, S>), dim3(blocks), dim3(256 * CS), 0, s, ka)
   if (layout == 1) {
     if (hz) { if (sb) WQ_BL(1, true, true); else WQ_BL(1, true, false); }
     else    { if (sb) WQ_BL(1, false, true); else WQ_BL(1, false, false); }
