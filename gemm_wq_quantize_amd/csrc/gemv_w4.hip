@@ -594,6 +594,19 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
   int cg = rg_first, ct = i0 - rg_first * nit;
   const int nsteps = i1 - i0;
   for (int base = 0; base < nsteps; base += D) {
+#if WQ_P_PRIO
+    {
+      // issue priority from the share of items still to do: waves that
+      // are behind (the youngest, which oldest-first arbitration serves last)
+      // win the SIMD's issue slots
+      const int left4 = __builtin_amdgcn_readfirstlane(4 * (nsteps - base));
+      const int tot = __builtin_amdgcn_readfirstlane(nsteps);
+      if (left4 > 3 * tot) __builtin_amdgcn_s_setprio(3);
+      else if (left4 > 2 * tot) __builtin_amdgcn_s_setprio(2);
+      else if (left4 > tot) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
+#endif
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const bool valid = base + d < nsteps;
@@ -1015,6 +1028,9 @@ constexpr int PERSIST_LDS_MAX = 160 * 1024;  // all of a gfx950 CU's LDS
 #endif
 #ifndef WQ_P_D
 #define WQ_P_D 2
+#endif
+#ifndef WQ_P_PRIO
+#define WQ_P_PRIO 1  // progress-based issue priority in the decode loop
 #endif
 
 int cu_count() {
