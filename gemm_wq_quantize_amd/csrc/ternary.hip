@@ -265,6 +265,9 @@ constexpr uint32_t T_OOB = 0x80000000u;
 #ifndef WQ_T_LPR
 #define WQ_T_LPR 8  // lanes per row in the persistent ternary GEMV
 #endif
+#ifndef WQ_T_PRIO
+#define WQ_T_PRIO 1  // progress-based issue priority in the persistent loop
+#endif
 #ifndef WQ_T_WAVES
 #define WQ_T_WAVES 4  // waves per SIMD the register budget is sized for
 #endif
@@ -457,6 +460,14 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
   };
   // groups of D items keep the ring slot a compile-time constant
   for (int i = 0; i < nitems; i += D) {
+    if constexpr (WQ_T_PRIO && C <= 4) {
+      // issue priority from the share of items still to do (waves that fall
+      // behind are served first; 4-5% at 2 and 4 columns, a loss at 8)
+      if (4 * (nitems - i) > 3 * nitems) __builtin_amdgcn_s_setprio(3);
+      else if (4 * (nitems - i) > 2 * nitems) __builtin_amdgcn_s_setprio(2);
+      else if (4 * (nitems - i) > nitems) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) item(i + d, d);
   }
