@@ -1088,10 +1088,14 @@ hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
                                {WQ_PFN(1, true, false), WQ_PFN(1, true, true)}}};
 #undef WQ_PFN
   const void* fn = fns[layout][hz][sb];
-  static bool attr_set[2][2][2] = {};
-  if (!attr_set[layout][hz][sb]) {
-    hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, PERSIST_LDS_MAX);
-    attr_set[layout][hz][sb] = true;
+  // the attribute is per device: set it once on each
+  static bool attr_set[64][2][2][2] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev][layout][hz][sb]) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, PERSIST_LDS_MAX);
+    if (e != hipSuccess) return e;
+    attr_set[dev][layout][hz][sb] = true;
   }
   int sph_arg = sph;
   void* args[] = {const_cast<KArgs*>(&ka), &sph_arg};

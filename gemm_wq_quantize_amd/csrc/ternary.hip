@@ -803,12 +803,14 @@ hipError_t launch_ternary_ksplit(const uint32_t* wp, const uint8_t* xq, int64_t 
                       4 * 8 * C * 4;
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
-  static bool attr_set = false;  // one per instantiation
-  if (!attr_set) {
+  static bool attr_set[64] = {};  // per instantiation and device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev]) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev] = true;
   }
   const int64_t nrg = (n + 7) / 8;
   const int64_t grid = (nrg + (4 / S) - 1) / (4 / S);
@@ -825,12 +827,14 @@ hipError_t launch_ternary_persist(const uint32_t* wp, const uint8_t* xq, int64_t
   const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8;
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
-  static bool attr_set = false;  // one per instantiation
-  if (!attr_set) {
+  static bool attr_set[64] = {};  // per instantiation and device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev]) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev] = true;
   }
   const int64_t nrg = (n + 64 / TP_LPR - 1) / (64 / TP_LPR);
   // workgroups resident at once: LDS and the waves per SIMD the register
