@@ -202,3 +202,14 @@ def test_gemm_stored_zeros_integer_exact(group):
     w = (codes.astype(np.float64) - np.repeat(zi, group, axis=1)) * np.repeat(2.0 ** e, group, axis=1)
     want = fpformat.f32_to_bf16_bits((a.astype(np.float64) @ w.T).astype(np.float32))
     assert np.array_equal(c.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+def test_gemm_repeatable():
+    # every output is summed by one wave in a fixed order: bitwise repeatable,
+    # with one scale per column and with group scales
+    say("gemm bitwise repeatable")
+    p = wq_inputs.grouped_gemm(512, 768, 2048, 128, seed=21)
+    for group, sbits in ((2048, p.scale_bits[:, :1].copy()), (128, p.scale_bits)):
+        outs = [run(p.a_bits, p.codes, sbits, group=group).view(torch.int16).cpu().numpy()
+                for _ in range(3)]
+        assert all(np.array_equal(outs[0], o) for o in outs[1:]), group

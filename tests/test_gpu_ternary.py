@@ -130,3 +130,15 @@ def test_ternary_gemm_unit_scale_exact(k, n, c):
     got = gpu_gemv(wb, gpu_q8(p.x), k)
     exact = p.x.astype(np.int64) @ p.trits.astype(np.int64).T
     assert np.array_equal(got, exact.astype(np.float64))
+
+
+@pytest.mark.parametrize("c", [1, 4, 8, 96])
+def test_ternary_repeatable(c):
+    # fixed-order sums in every path (the split row groups of one column, the
+    # persistent kernel, the matrix-core kernel): bitwise repeatable
+    say("ternary bitwise repeatable", c)
+    p = wq_inputs.ternary_gemv(5120, 2000, cmax=c, seed=5)
+    wb = gpu_blocks(p.trits, p.d_bits)
+    xq = gpu_q8(p.x)
+    outs = [gpu_gemv(wb, xq, 5120) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
