@@ -72,8 +72,8 @@ def main():
                     help="also run one plain device copy of this size (PMC scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by output rows with no collective, see the design notes",
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
+              "across GPUs each would take a slice of the output rows (no collective needed)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -58,7 +58,7 @@ const char* wq_status_string(int status) {
     case WQ_EINVAL: return "WQ_EINVAL: null pointer, bad enum or negative size";
     case WQ_EALIGN: return "WQ_EALIGN: pointer misaligned for this call";
     case WQ_ESHAPE: return "WQ_ESHAPE: sizes violate this call's divisibility or limits";
-    case WQ_EUNSUPPORTED: return "WQ_EUNSUPPORTED: request not implemented by this build";
+    case WQ_EUNSUPPORTED: return "WQ_EUNSUPPORTED: valid request the library does not implement";
     case WQ_EHIP: return "WQ_EHIP: HIP runtime error at launch";
     default: return "unknown wq_status";
   }

@@ -67,7 +67,7 @@ typedef enum {
   WQ_EINVAL = -1,       /* null pointer, bad enum, negative size            */
   WQ_EALIGN = -2,       /* a pointer is not aligned as the call requires    */
   WQ_ESHAPE = -3,       /* sizes violate the call's divisibility/limits     */
-  WQ_EUNSUPPORTED = -4, /* valid request this build does not implement      */
+  WQ_EUNSUPPORTED = -4, /* valid request the library does not implement     */
   WQ_EHIP = -5          /* the HIP runtime reported an error at launch      */
 } wq_status;
 
