@@ -105,14 +105,19 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const uint16_t* __restric
 //
 // code = clamp(rint(RN(w / s)), -8, 7) + 8 needs the correctly rounded
 // float32 quotient only where rounding to an integer can tell it apart from
-// a nearby value.  The quotient is formed from r = RN(1 / s) with one
-// residual correction (Markstein's FMA division step: y = w r,
-// e = w - s y exactly by FMA, q = y + e r), which is RN(w / s) or one ulp
-// from it.  rint(q) can differ from rint(RN(w / s)) only when one of them
-// lies on a half-integer or they straddle one, so any lane whose q is within
-// 2^-19 (two ulps below 8) of a half-integer sends its wave through the exact
-// IEEE divide instead.  |w / s| < 7.1 and s is a normal number, so nothing
-// over- or underflows.
+// a nearby value.  With r = RN(1 / s), one FMA (the fp16 weight converted
+// inside it) gives t = RN(w r + 8.5 + 2^-18).  |w / s| <= 7.02 (s is the
+// group's absmax / 7, rounded to bf16 or float32), so w r lies within 2^-21
+// of w / s, RN(w / s) within 2^-22 of it, and the rounding of t (t < 16)
+// adds at most 2^-21: t = RN(w / s) + 8.5 + 2^-18 + e with |e| < 2^-19.
+// floor(t) is therefore rint(RN(w / s)) + 8 unless RN(w / s) is a
+// half-integer (a tie, which rounds to even) or t crossed an integer, and in
+// both cases fract(t) < 2^-17; a wave with any lane where fract(t) <= 2^-17
+// recomputes its codes with the IEEE divide.  The clamp of the code is that
+// of t to [0, 15] before truncation, and s is a normal number, so nothing
+// over- or underflows.  The group's absmax is taken on the fp16 bit
+// patterns: for finite values, magnitude order is the unsigned order of the
+// bits without the sign.
 __device__ __forceinline__ uint32_t pack8(const int (&c)[8], int layout) {
   if (layout == 0)
     return c[0] | c[1] << 4 | c[2] << 8 | c[3] << 12 | c[4] << 16 | c[5] << 20 | c[6] << 24 | c[7] << 28;
@@ -135,18 +140,18 @@ __global__ __launch_bounds__(256) void k_quantize_pack_r(const uint16_t* __restr
   const uint16_t* src = w + (int64_t)row * k + (int64_t)g * group;
 
   uint4 v[WPL];
-  float amax = 0.f;
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mx = {0, 0};  // largest |w| bits, two halves
 #pragma unroll
   for (int i = 0; i < WPL; ++i) {
     const int j = lane + TEAM * i;
     v[i] = j < gw ? *reinterpret_cast<const uint4*>(src + 8 * j) : make_uint4(0, 0, 0, 0);
     const uint32_t h[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      amax = fmaxf(amax, fabsf(f16_to_f32(h[e] & 0xFFFFu)));
-      amax = fmaxf(amax, fabsf(f16_to_f32(h[e] >> 16)));
-    }
+    for (int e = 0; e < 4; ++e)
+      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, h[e] & 0x7FFF7FFFu));
   }
+  float amax = fmaxf(f16_to_f32(mx.x), f16_to_f32(mx.y));
 #pragma unroll
   for (int off = TEAM / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, TEAM));
 
@@ -173,10 +178,9 @@ __global__ __launch_bounds__(256) void k_quantize_pack_r(const uint16_t* __restr
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = f16_to_f32(e & 1 ? h[e >> 1] >> 16 : h[e >> 1] & 0xFFFFu);
-      const float y = x * r;
-      const float q = fmaf(fmaf(-y, s, x), r, y);
-      near |= fabsf(__builtin_amdgcn_fractf(q) - 0.5f) <= 0x1p-19f;
-      c[e] = (int)__builtin_amdgcn_fmed3f(rintf(q), -8.f, 7.f) + 8;
+      const float t = fmaf(x, r, 8.5f + 0x1p-18f);
+      near |= __builtin_amdgcn_fractf(t) <= 0x1p-17f;
+      c[e] = (int)(uint32_t)__builtin_amdgcn_fmed3f(t, 0.f, 15.f);
     }
     word[i] = pack8(c, layout);
   }
