@@ -4,11 +4,20 @@
 #include "../../include/wq.h"
 #include "wq_internal.h"
 
+#include <cstdint>
+
 namespace {
 
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// a * b for non-negative sizes, saturated at INT64_MAX (so that size checks
+// on absurd arguments cannot wrap round and pass)
+int64_t mul_sat(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -42,7 +51,7 @@ int gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* 
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c_out, 16) ||
       !aligned(scales, grouped ? 4 : 2) || (zeros && !aligned(zeros, grouped ? 4 : 2)))
     return WQ_EALIGN;
-  if (((m + 255) / 256) * ((n + 255) / 256) > kMaxGrid) return WQ_ESHAPE;
+  if (mul_sat(m / 256 + 1, n / 256 + 1) > kMaxGrid) return WQ_ESHAPE;
   return hip_status(wq::launch_gemm_w4a16(a, b, scales, zeros, group, zero_const, m, n, k, c_out,
                                           as_stream(stream)));
 }
@@ -71,7 +80,7 @@ int wq_pack_int4(const uint8_t* codes, int64_t n, int64_t k, int layout, uint8_t
   if (!codes || !packed) return WQ_EINVAL;
   if (k % 8 != 0) return WQ_ESHAPE;
   if (!aligned(codes, 4) || !aligned(packed, 4)) return WQ_EALIGN;
-  if (n * k / 8 / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  if (mul_sat(n, k) / 8 / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
   return hip_status(wq::launch_pack_int4(codes, n, k, layout, packed, as_stream(stream)));
 }
 
@@ -85,7 +94,7 @@ int wq_quantize_pack_int4(const uint16_t* w, int64_t n, int64_t k, int64_t group
   if (k % 32 != 0 || !valid_group(group, k)) return WQ_ESHAPE;
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, dtype_size(scale_dtype)))
     return WQ_EALIGN;
-  if (n * (k / group) * 64 / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  if (mul_sat(mul_sat(n, k / group), 64) / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
   return hip_status(wq::launch_quantize_pack_int4(w, n, k, group, layout, packed, scales,
                                                   scale_dtype == WQ_BF16, as_stream(stream)));
 }
@@ -145,7 +154,7 @@ int wq_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
   if (!trits || !d || !blocks) return WQ_EINVAL;
   if (k % 128 != 0) return WQ_ESHAPE;
   if (!aligned(trits, 16) || !aligned(d, 2) || !aligned(blocks, 4)) return WQ_EALIGN;
-  if (n * (k / 128) / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  if (mul_sat(n, k / 128) / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
   return hip_status(wq::launch_pack_ptq1_0(trits, d, n, k, blocks, as_stream(stream)));
 }
 
@@ -155,7 +164,7 @@ int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* 
   if (!x || !x_q8) return WQ_EINVAL;
   if (k % 32 != 0) return WQ_ESHAPE;
   if (!aligned(x, 16) || !aligned(x_q8, 4)) return WQ_EALIGN;
-  if (c * k / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  if (mul_sat(c, k) / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
   return hip_status(wq::launch_quantize_q8_1(x, c, k, x_q8, as_stream(stream)));
 }
 
@@ -169,9 +178,10 @@ int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int
   if (!aligned(w_blocks, 4) || !aligned(x_q8, 4) || !aligned(out, c >= 64 ? 16 : 4)) return WQ_EALIGN;
   if (n / 32 + 1 > kMaxGrid) return WQ_ESHAPE;
   if (c >= 64) {  // 32-bit buffer offsets and the tile grid
-    if (n * (k / 128) * 28 >= (int64_t(1) << 31) || c * (k / 32) * 36 >= (int64_t(1) << 31))
+    if (mul_sat(mul_sat(n, k / 128), 28) >= (int64_t(1) << 31) ||
+        mul_sat(mul_sat(c, k / 32), 36) >= (int64_t(1) << 31))
       return WQ_ESHAPE;
-    if (((c + 127) / 128) * ((n + 127) / 128) > kMaxGrid) return WQ_ESHAPE;
+    if (mul_sat(c / 128 + 1, n / 128 + 1) > kMaxGrid) return WQ_ESHAPE;
   }
   return hip_status(wq::launch_gemv_ternary(w_blocks, x_q8, n, k, c, out, as_stream(stream)));
 }

@@ -1073,7 +1073,9 @@ hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
   int grid = cu_count();
   if ((int64_t)grid * R > ka.n) grid = (int)std::max<int64_t>(1, ka.n / R);
   const int64_t maxrows = (ka.n + grid - 1) / grid;
-  if (maxrows * ngroups * 4 >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // scale offsets
+  // 32-bit offsets within a workgroup's rows: weights and scales
+  if (maxrows * (ka.k / 2) >= (int64_t(1) << 31) || maxrows * ngroups * 4 >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
   const int sph = persist_slots(ka.n, grid, R, nit, NHW);
   const bool hz = ka.zeros != nullptr;
   const int64_t lds = C * nch * (64 + 4) + (int64_t)NHW * sph * R * C * 4 + NHW * 3 * 4;

@@ -79,6 +79,14 @@ def test_validation_errors_without_gpu(lib):
     assert lib.wq_gemv_ternary(FAKE, FAKE, 1 << 22, 4096, 64, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_gemv_ternary(FAKE, FAKE, 64, 4096, 1 << 20, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_pack_ptq1_0(FAKE, FAKE, 2, 64, FAKE, None) == g.WQ_ESHAPE
+    # sizes whose products overflow int64 are rejected, not wrapped round
+    huge = 1 << 40
+    assert lib.wq_pack_int4(FAKE, huge, huge, 1, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_quantize_pack_int4(FAKE, huge, 1 << 39, 1 << 39, 1, FAKE, FAKE, 2, None) == g.WQ_ESHAPE
+    assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, FAKE, 128, 8.0, huge, huge, 128, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_pack_ptq1_0(FAKE, FAKE, huge, 1 << 39, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_quantize_q8_1(FAKE, huge, 1 << 39, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary(FAKE, FAKE, huge, 1 << 39, 64, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_quantize_q8_1(FAKE, 2, 48, FAKE, None) == g.WQ_ESHAPE
     # unsupported combinations
     assert lib.wq_gemm_w4a16(FAKE, FAKE, 0, FAKE, 128, 8.0, 64, 64, 128, FAKE, None) == g.WQ_EUNSUPPORTED
