@@ -72,18 +72,30 @@ def _check(fn: str, status: int) -> None:
         raise WqError(fn, status)
 
 
-def _ptr(t):
+def _require(cond: bool, msg: str) -> None:
+    """Argument check that survives ``python -O`` (unlike assert): the sizes
+    checked here bound what the kernels read and write."""
+    if not cond:
+        raise ValueError(f"wq: {msg}")
+
+
+def _ptr(t, dev=None):
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("wq: tensors must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("wq: tensors must be contiguous")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"wq: tensor on {t.device}, stream on {dev}")
     return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
+def _sptr(s):
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -107,83 +119,111 @@ def wq_abi_version() -> int:
 def wq_pack_int4(codes, layout, packed, stream=None):
     """codes uint8 [n][k] -> packed uint8 [n][k/2] in ``layout``."""
     n, k = codes.shape
-    assert codes.dtype == torch.uint8 and packed.dtype == torch.uint8
-    assert packed.numel() == n * k // 2
-    _check("wq_pack_int4", lib.wq_pack_int4(_ptr(codes), n, k, layout, _ptr(packed), _stream(stream)))
+    _require(codes.dtype == torch.uint8 and packed.dtype == torch.uint8, "codes and packed are uint8")
+    _require(packed.numel() == n * k // 2, "packed holds n * k / 2 bytes")
+    st = _stream(stream)
+    _check("wq_pack_int4", lib.wq_pack_int4(_ptr(codes, st.device), n, k, layout,
+                                            _ptr(packed, st.device), _sptr(st)))
 
 
 def wq_quantize_pack_int4(w, group, layout, packed, scales, stream=None):
     """fp16 w [n][k] -> packed uint8 [n][k/2] + scales [n][k/group] (f32 or bf16)."""
     n, k = w.shape
-    assert w.dtype in (torch.float16, torch.int16, torch.uint16) and packed.dtype == torch.uint8
-    assert packed.numel() == n * k // 2 and scales.numel() == n * (k // group)
+    _require(w.dtype in (torch.float16, torch.int16, torch.uint16), "w is fp16 (or its bits)")
+    _require(packed.dtype == torch.uint8 and packed.numel() == n * k // 2,
+             "packed is uint8 with n * k / 2 bytes")
+    _require(group > 0 and scales.numel() == n * (k // group), "scales hold n * (k / group) values")
+    st = _stream(stream)
     _check("wq_quantize_pack_int4",
-           lib.wq_quantize_pack_int4(_ptr(w), n, k, group, layout, _ptr(packed), _ptr(scales),
-                                     _dtype(scales), _stream(stream)))
+           lib.wq_quantize_pack_int4(_ptr(w, st.device), n, k, group, layout, _ptr(packed, st.device),
+                                     _ptr(scales, st.device), _dtype(scales), _sptr(st)))
 
 
 def wq_gemv_w4(packed, layout, scales, zeros, zero_const, k, group, x, out, stream=None):
     """out[c][n] = sum_k (q - z) s x[c][k]; n = packed rows, c = x rows."""
     n = packed.shape[0]
     c = x.shape[0]
-    assert packed.dtype == torch.uint8 and packed.numel() == n * k // 2
-    assert x.shape[-1] == k and out.numel() == c * n
-    assert scales.numel() == n * (k // group)
+    _require(packed.dtype == torch.uint8 and packed.numel() == n * k // 2,
+             "packed is uint8 with n * k / 2 bytes")
+    _require(x.numel() == c * k and out.numel() == c * n, "x is [c][k] and out [c][n]")
+    _require(group > 0 and scales.numel() == n * (k // group), "scales hold n * (k / group) values")
     if zeros is not None:
-        assert zeros.dtype == scales.dtype and zeros.numel() == scales.numel()
+        _require(zeros.dtype == scales.dtype and zeros.numel() == scales.numel(),
+                 "zeros match the scales in dtype and shape")
+    st = _stream(stream)
+    d = st.device
     _check("wq_gemv_w4",
-           lib.wq_gemv_w4(_ptr(packed), layout, _ptr(scales), _dtype(scales), _ptr(zeros),
-                          float(zero_const), n, k, group, _ptr(x), _dtype(x), c, _ptr(out),
-                          _dtype(out), _stream(stream)))
+           lib.wq_gemv_w4(_ptr(packed, d), layout, _ptr(scales, d), _dtype(scales), _ptr(zeros, d),
+                          float(zero_const), n, k, group, _ptr(x, d), _dtype(x), c, _ptr(out, d),
+                          _dtype(out), _sptr(st)))
+
+
+def _gemm_shapes(a, b, scales, group, c_out):
+    m, k = a.shape
+    n = b.shape[0]
+    _require(a.dtype == torch.bfloat16 and c_out.dtype == torch.bfloat16, "a and c_out are bf16")
+    _require(b.dtype == torch.uint8 and b.numel() == n * k // 2, "b is uint8 with n * k / 2 bytes")
+    _require(c_out.numel() == m * n, "c_out is [m][n]")
+    _require(scales.dtype == torch.bfloat16, "scales are bf16")
+    _require(group > 0 and scales.numel() == (n if group == k else n * (k // group)),
+             "scales hold n (group == k) or n * (k / group) values")
+    return m, n, k
 
 
 def wq_gemm_w4a16(a, b, layout, scales, group, zero_const, c_out, stream=None):
     """C[m][n] = sum_k A[m][k] (q[n][k] - z) s[n]; a bf16 [m][k], b uint8 [n][k/2]."""
-    m, k = a.shape
-    n = b.shape[0]
-    assert a.dtype == torch.bfloat16 and c_out.dtype == torch.bfloat16 and b.dtype == torch.uint8
-    assert b.numel() == n * k // 2 and c_out.numel() == m * n and scales.dtype == torch.bfloat16
+    m, n, k = _gemm_shapes(a, b, scales, group, c_out)
+    st = _stream(stream)
+    d = st.device
     _check("wq_gemm_w4a16",
-           lib.wq_gemm_w4a16(_ptr(a), _ptr(b), layout, _ptr(scales), group, float(zero_const),
-                             m, n, k, _ptr(c_out), _stream(stream)))
+           lib.wq_gemm_w4a16(_ptr(a, d), _ptr(b, d), layout, _ptr(scales, d), group, float(zero_const),
+                             m, n, k, _ptr(c_out, d), _sptr(st)))
 
 
 def wq_gemm_w4a16_zp(a, b, layout, scales, zeros, group, c_out, stream=None):
     """C[m][n] = sum_k A[m][k] (q[n][k] - z[n][k/group]) s[n][k/group] with stored
     bf16 zeros of the scales' shape."""
-    m, k = a.shape
-    n = b.shape[0]
-    assert a.dtype == torch.bfloat16 and c_out.dtype == torch.bfloat16 and b.dtype == torch.uint8
-    assert b.numel() == n * k // 2 and c_out.numel() == m * n
-    assert scales.dtype == torch.bfloat16 and zeros.dtype == torch.bfloat16
-    assert zeros.numel() == scales.numel() == n * (k // group)
+    m, n, k = _gemm_shapes(a, b, scales, group, c_out)
+    _require(zeros is not None and zeros.dtype == torch.bfloat16 and zeros.numel() == scales.numel(),
+             "zeros are bf16 of the scales' shape")
+    st = _stream(stream)
+    d = st.device
     _check("wq_gemm_w4a16_zp",
-           lib.wq_gemm_w4a16_zp(_ptr(a), _ptr(b), layout, _ptr(scales), _ptr(zeros), group,
-                                m, n, k, _ptr(c_out), _stream(stream)))
+           lib.wq_gemm_w4a16_zp(_ptr(a, d), _ptr(b, d), layout, _ptr(scales, d), _ptr(zeros, d), group,
+                                m, n, k, _ptr(c_out, d), _sptr(st)))
 
 
 def wq_pack_ptq1_0(trits, d, blocks, stream=None):
     """trits int8 [n][k], d fp16 [n][k/128] -> PTQ1_0 blocks uint8 [n][k/128][28]."""
     n, k = trits.shape
-    assert trits.dtype == torch.int8 and blocks.dtype == torch.uint8
-    assert d.numel() == n * (k // 128) and blocks.numel() == n * (k // 128) * 28
+    _require(trits.dtype == torch.int8 and blocks.dtype == torch.uint8, "trits int8, blocks uint8")
+    _require(d.element_size() == 2 and d.numel() == n * (k // 128), "d holds n * k / 128 fp16 values")
+    _require(blocks.numel() == n * (k // 128) * 28, "blocks hold n * k / 128 * 28 bytes")
+    st = _stream(stream)
+    dv = st.device
     _check("wq_pack_ptq1_0",
-           lib.wq_pack_ptq1_0(_ptr(trits), _ptr(d), n, k, _ptr(blocks), _stream(stream)))
+           lib.wq_pack_ptq1_0(_ptr(trits, dv), _ptr(d, dv), n, k, _ptr(blocks, dv), _sptr(st)))
 
 
 def wq_quantize_q8_1(x, x_q8, stream=None):
     """fp32 x [c][k] -> block_q8_1 uint8 [c][k/32][36]."""
     c, k = x.shape
-    assert x.dtype == torch.float32 and x_q8.dtype == torch.uint8
-    assert x_q8.numel() == c * (k // 32) * 36
-    _check("wq_quantize_q8_1", lib.wq_quantize_q8_1(_ptr(x), c, k, _ptr(x_q8), _stream(stream)))
+    _require(x.dtype == torch.float32 and x_q8.dtype == torch.uint8, "x fp32, x_q8 uint8")
+    _require(x_q8.numel() == c * (k // 32) * 36, "x_q8 holds c * k / 32 * 36 bytes")
+    st = _stream(stream)
+    _check("wq_quantize_q8_1", lib.wq_quantize_q8_1(_ptr(x, st.device), c, k, _ptr(x_q8, st.device),
+                                                    _sptr(st)))
 
 
 def wq_gemv_ternary(w_blocks, x_q8, k, out, stream=None):
     """out fp32 [c][n] from PTQ1_0 weights [n][k/128][28] and q8_1 x [c][k/32][36]."""
     n = w_blocks.shape[0]
     c = x_q8.shape[0]
-    assert w_blocks.numel() == n * (k // 128) * 28 and x_q8.numel() == c * (k // 32) * 36
-    assert out.dtype == torch.float32 and out.numel() == c * n
+    _require(w_blocks.dtype == torch.uint8 and x_q8.dtype == torch.uint8, "blocks are uint8")
+    _require(w_blocks.numel() == n * (k // 128) * 28 and x_q8.numel() == c * (k // 32) * 36,
+             "w_blocks [n][k/128][28], x_q8 [c][k/32][36]")
+    _require(out.dtype == torch.float32 and out.numel() == c * n, "out is fp32 [c][n]")
+    st = _stream(stream)
+    d = st.device
     _check("wq_gemv_ternary",
-           lib.wq_gemv_ternary(_ptr(w_blocks), _ptr(x_q8), n, k, c, _ptr(out), _stream(stream)))
+           lib.wq_gemv_ternary(_ptr(w_blocks, d), _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
