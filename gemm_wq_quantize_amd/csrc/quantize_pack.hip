@@ -113,23 +113,26 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const uint16_t* __restric
 // floor(t) is therefore rint(RN(w / s)) + 8 unless RN(w / s) is a
 // half-integer (a tie, which rounds to even) or t crossed an integer, and in
 // both cases fract(t) < 2^-17; a wave with any lane where fract(t) <= 2^-17
-// recomputes its codes with the IEEE divide.  The clamp of the code is that
-// of t to [0, 15] before truncation, and s is a normal number, so nothing
-// over- or underflows.  The group's absmax is taken on the fp16 bit
+// recomputes its codes with the IEEE divide.  The clamp to [-8, 7] cannot
+// bind here: s is at least (absmax / 7)(1 - 2^-9) after rounding, so
+// |w / s| < 7.014, t lies in [1.48, 15.52] and floor(t) in [1, 15] (the
+// exact path keeps the clamp).  s is a normal number, so nothing over- or
+// underflows.  The group's absmax is taken on the fp16 bit
 // patterns: for finite values, magnitude order is the unsigned order of the
 // bits without the sign.
-__device__ __forceinline__ uint32_t pack8(const int (&c)[8], int layout) {
-  if (layout == 0)
+template <int LAYOUT>
+__device__ __forceinline__ uint32_t pack8(const int (&c)[8]) {
+  if (LAYOUT == 0)
     return c[0] | c[1] << 4 | c[2] << 8 | c[3] << 12 | c[4] << 16 | c[5] << 20 | c[6] << 24 | c[7] << 28;
   return c[0] | c[2] << 4 | c[4] << 8 | c[6] << 12 | c[1] << 16 | c[3] << 20 | c[5] << 24 | c[7] << 28;
 }
 
-template <int TEAM, int WPL>
+template <int TEAM, int WPL, int LAYOUT>
 __global__ __launch_bounds__(256) void k_quantize_pack_r(const uint16_t* __restrict__ w,
                                                          uint32_t* __restrict__ packed,
                                                          void* __restrict__ scales, int n,
                                                          int ngroups, int64_t k, int group,
-                                                         int layout, int scale_bf16) {
+                                                         int scale_bf16) {
   constexpr int TPW = 256 / TEAM;  // teams per workgroup
   const int tid = threadIdx.x, lane = tid % TEAM;
   const int unit = (int)blockIdx.x * TPW + tid / TEAM;  // (row, group); n * ngroups < 2^31
@@ -180,9 +183,9 @@ __global__ __launch_bounds__(256) void k_quantize_pack_r(const uint16_t* __restr
       const float x = f16_to_f32(e & 1 ? h[e >> 1] >> 16 : h[e >> 1] & 0xFFFFu);
       const float t = fmaf(x, r, 8.5f + 0x1p-18f);
       near |= __builtin_amdgcn_fractf(t) <= 0x1p-17f;
-      c[e] = (int)(uint32_t)__builtin_amdgcn_fmed3f(t, 0.f, 15.f);
+      c[e] = (int)(uint32_t)t;  // floor: t > 0 (the clamp cannot bind, see above)
     }
-    word[i] = pack8(c, layout);
+    word[i] = pack8<LAYOUT>(c);
   }
   if (__builtin_amdgcn_ballot_w64(near) != 0) {  // uniform: exact quotients
 #pragma unroll
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(256) void k_quantize_pack_r(const uint16_t* __restr
         const float x = f16_to_f32(e & 1 ? h[e >> 1] >> 16 : h[e >> 1] & 0xFFFFu);
         c[e] = (int)fminf(fmaxf(rintf(x / s), -8.f), 7.f) + 8;
       }
-      word[i] = pack8(c, layout);
+      word[i] = pack8<LAYOUT>(c);
     }
   }
   if (!active) return;
@@ -233,9 +236,15 @@ hipError_t launch_quantize_pack_int4(const uint16_t* w, int64_t n, int64_t k, in
     const int64_t wpl = (gw + team - 1) / team;  // 1..8
     const int wsel = wpl <= 1 ? 1 : wpl <= 2 ? 2 : wpl <= 4 ? 4 : 8;
     const unsigned blocks = (unsigned)((units * team + 255) / 256);
-#define WQ_QR(T, W)                                                                         \
-  hipLaunchKernelGGL((k_quantize_pack_r<T, W>), dim3(blocks), dim3(256), 0, s, w, out, scales, \
-                     (int)n, (int)(k / group), k, (int)group, layout, sb)
+#define WQ_QR(T, W)                                                                           \
+  do {                                                                                        \
+    if (layout == 0)                                                                          \
+      hipLaunchKernelGGL((k_quantize_pack_r<T, W, 0>), dim3(blocks), dim3(256), 0, s, w, out,   \
+                         scales, (int)n, (int)(k / group), k, (int)group, sb);                \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_quantize_pack_r<T, W, 1>), dim3(blocks), dim3(256), 0, s, w, out,   \
+                         scales, (int)n, (int)(k / group), k, (int)group, sb);                \
+  } while (0)
     bool launched = true;
     if (team == 4) WQ_QR(4, 1);
     else if (team == 8 && wsel == 1) WQ_QR(8, 1);
