@@ -91,6 +91,20 @@ def test_gemm_8192_sampled_rows():
     assert np.all(np.abs(rms / expect - 1) < 0.1)
 
 
+def test_gemm_8192_group128_sampled_rows():
+    # the timed group-scale workload (8192^3, group 128) checked on a seeded
+    # sample of 128 output rows
+    p = wq_inputs.grouped_gemm(8192, 8192, 8192, 128, seed=3)
+    rows = np.sort(np.random.default_rng(3).choice(8192, 128, replace=False))
+    say("gemm 8192^3 group 128, sampled rows", len(rows))
+    c = run(p.a_bits, p.codes, p.scale_bits, group=128)
+    got = c.index_select(0, torch.from_numpy(rows).cuda()).float().cpu().numpy()
+    a = fpformat.bf16_bits_to_f32(p.a_bits[rows])
+    s = fpformat.bf16_bits_to_f32(p.scale_bits)
+    check_bf16_rows(got, o4.gemm_w4a16_rows_bf16w(a, o4.pack(p.codes, 1), 1, s, 8.0, 128))
+    assert torch.isfinite(c.float()).all()
+
+
 # ---- group scales ([N][K/group] bf16; each weight rounded to bf16 before the
 # multiply, as the oracle's ``gemm_w4a16_rows_bf16w`` states)
 @pytest.mark.parametrize("m,n,k,group", [(300, 520, 512, 128), (256, 256, 256, 64),

@@ -120,6 +120,22 @@ def test_ternary_gemm(k, n, c):
     check_f32(gpu_gemv(wb, xq, k), ot.gemv_ternary(ot.encode_ptq1_0(p.trits, p.d_bits), xref))
 
 
+def test_ternary_gemm_timed_shape_sampled_columns():
+    # the timed matrix-core workload (K=5120, N=17280, 4096 columns), checked
+    # on a seeded sample of 8 columns against the oracle, the rest finite
+    k, n, c = 5120, 17280, 4096
+    say("ternary gemm", k, n, c, "sampled columns")
+    p = wq_inputs.ternary_gemv(k, n, cmax=c, seed=11)
+    wb = gpu_blocks(p.trits, p.d_bits)
+    xq = gpu_q8(p.x)
+    got = gpu_gemv(wb, xq, k)
+    cols = np.sort(np.random.default_rng(11).choice(c, 8, replace=False))
+    xref = ot.quantize_q8_1(p.x[cols])
+    assert np.array_equal(xq.cpu().numpy()[cols], xref)
+    check_f32(got[cols], ot.gemv_ternary(ot.encode_ptq1_0(p.trits, p.d_bits), xref))
+    assert np.isfinite(got).all()
+
+
 @pytest.mark.parametrize("k,n,c", [(1024, 300, 64), (5120, 200, 129)])
 def test_ternary_gemm_unit_scale_exact(k, n, c):
     # unit scales and integer x: the int32 products and the float32 sums are
