@@ -11,7 +11,8 @@ the 256 MB Infinity Cache, so every weight byte comes from HBM.
 The same run also times the other rows of the path (quantise + pack, the
 small-batch GEMV, the 8192^3 W4A16 GEMM, the ternary GEMV) and reports them
 under "rows"; and, on rank 0, times the CPU oracle on a bounded sample
-("cpu_baseline").
+("cpu_baseline").  GEMV rows also give tokens-equivalent rows per second
+("Mrows_per_s": output rows times activation columns per second, millions).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -200,7 +201,8 @@ def main():
         per_call[f"K{s['k']}_N{s['n']}_c{c}"] = {
             "us": round(d * 1e3, 2), "weight_GBs": round(s["wbytes"] / (d * 1e-3) / 1e9, 1),
             "alg_GBs": round(alg / (d * 1e-3) / 1e9, 1),
-            "frac_hbm": round(alg / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm": round(alg / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "Mrows_per_s": round(s["n"] * c / (d * 1e-3) / 1e6, 1)}
     traffic = read_traffic(os.path.join(ROOT, "gemm_wq_quantize_amd", "csrc", "gemv_w4.hip"))
     log("per launch:", json.dumps(per_call))
     # roofline of the kernel: algorithmic bytes of one launch over its average
@@ -314,7 +316,8 @@ def secondary_rows(g, torch, np, wq_inputs, dev, log):
             srow[f"K{k}_N{n}_c{c}"] = {
                 "us": round(ms * 1e3, 2), "weight_GBs": round(wb / (ms * 1e-3) / 1e9, 1),
                 "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
-                "frac_valu_fp32": round(flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)}
+                "frac_valu_fp32": round(flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),
+                "Mrows_per_s": round(n * c / (ms * 1e-3) / 1e6, 1)}
         del ws, cps
         torch.cuda.empty_cache()
     rows["quantize_pack_int4"] = qrow
@@ -360,7 +363,8 @@ def secondary_rows(g, torch, np, wq_inputs, dev, log):
         ms = timed(torch, lambda i: g.wq_gemv_ternary(wcs[i % nc], xq[:cc], 5120, y[:cc]), 50)
         trow[f"K5120_N17280_c{cc}"] = {
             "us": round(ms * 1e3, 2), "weight_GBs": round(wb.numel() / (ms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(wb.numel() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm": round(wb.numel() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "Mrows_per_s": round(17280 * cc / (ms * 1e-3) / 1e6, 1)}
     rows["gemv_ternary"] = trow
     log("ternary:", json.dumps(trow))
     # 4096 activation columns: the int8 matrix-core path (2 int8 ops per MAC)
