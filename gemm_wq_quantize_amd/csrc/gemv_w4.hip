@@ -777,7 +777,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // waves; waves w and w + 4 take the same 4 rows and the two halves of the
 // columns, so each SIMD runs two waves on one x tile (the two load the same
 // weights, which the CU's cache serves once).
-template <int C, int CS, int LAYOUT, bool HZ, bool SBF>
+// XS: all of x fits the two buffers (at most two tiles, K <= 4096): both
+// tiles are staged once, buffer t holding tile t, and the item loop has no x
+// loads and no barriers.
+template <int C, int CS, bool XS, int LAYOUT, bool HZ, bool SBF>
 __global__ __launch_bounds__(256 * CS, (C <= 8 && CS == 1) ? 2 : 1) void k_gemv_w4_batch(KArgs p) {
   static_assert(C % (4 * CS) == 0 && C <= 16, "columns per pass");
   constexpr int XC = C / (4 * CS);                       // x columns per wave and tile (loads)
@@ -915,16 +918,22 @@ __global__ __launch_bounds__(256 * CS, (C <= 8 && CS == 1) ? 2 : 1) void k_gemv_
 
   issue_w(0, 0);
   issue_w(1, 1);
-  dma_x(0, 0);
-  wait_vmcnt<0>();
-  sum_x(0);
+  if constexpr (XS) {
+    for (int t = 0; t < nt; ++t) dma_x(t, t);  // nt <= 2
+    wait_vmcnt<0>();
+    for (int t = 0; t < nt; ++t) sum_x(t);
+  } else {
+    dma_x(0, 0);
+    wait_vmcnt<0>();
+    sum_x(0);
+  }
   __syncthreads();
 
   // item i uses ring slot and x buffer i % 2; the loop runs in pairs so that
   // both are compile-time constants (register arrays cannot be indexed at run
   // time)
   auto item = [&](const int i, const int slot) {
-    const int b = slot;
+    const int b = XS ? i % nt : slot;  // x buffer
     // unpack this item's weights: 16 bf16 pairs (128 + q) per row
     uint32_t wp[BT_RW][16];
     float scr[BT_RW], zbr[BT_RW];
@@ -939,7 +948,7 @@ __global__ __launch_bounds__(256 * CS, (C <= 8 && CS == 1) ? 2 : 1) void k_gemv_
       scr[r] = sc[slot][r];
       zbr[r] = zb[slot][r];
     }
-    dma_x(i + 1, b ^ 1);   // buffer b ^ 1 was last read in item i - 1
+    if constexpr (!XS) dma_x(i + 1, b ^ 1);  // buffer b ^ 1 was last read in item i - 1
     issue_w(slot, i + 2);  // reuses the slot just unpacked
 
     // x fragments of two columns live at a time
@@ -979,10 +988,12 @@ __global__ __launch_bounds__(256 * CS, (C <= 8 && CS == 1) ? 2 : 1) void k_gemv_
       mac(cc + 1, xb, sb);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // x of item i + 1 landed once only the weights of i + 2 are in flight
-    wait_vmcnt<WLOADS>();
-    sum_x(b ^ 1);
-    __syncthreads();
+    if constexpr (!XS) {
+      // x of item i + 1 landed once only the weights of i + 2 are in flight
+      wait_vmcnt<WLOADS>();
+      sum_x(b ^ 1);
+      __syncthreads();
+    }
     if (i % nt == nt - 1) finish_rowgroup(i);  // uniform
   };
   for (int i = 0; i < nitems; i += 2) {
@@ -1157,8 +1168,14 @@ hipError_t launch_batch(const KArgs& ka, int layout, hipStream_t s) {
   const int64_t nrg = (ka.n + 4 * BT_RW - 1) / (4 * BT_RW);
   const unsigned blocks = (unsigned)std::min<int64_t>(nrg, (int64_t)cu_count() * (C <= 8 ? 2 : 1));
   const bool hz = ka.zeros != nullptr, sb = ka.scale_bf16 != 0;
-#define WQ_BL(L, Z, S) \
-  hipLaunchKernelGGL((k_gemv_w4_batch<C, CS, L, Z, S>), dim3(blocks), dim3(256 * CS), 0, s, ka)
+  const bool xs = (ka.k / 32 + BT_CH - 1) / BT_CH <= 2;  // x fits both buffers
+#define WQ_BL(L, Z, S)                                                                           \
+  do {                                                                                           \
+    if (xs)                                                                                      \
+      hipLaunchKernelGGL((k_gemv_w4_batch<C, CS, true, L, Z, S>), dim3(blocks), dim3(256 * CS), 0, s, ka); \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_gemv_w4_batch<C, CS, false, L, Z, S>), dim3(blocks), dim3(256 * CS), 0, s, ka); \
+  } while (0)
   if (layout == 1) {
     if (hz) { if (sb) WQ_BL(1, true, true); else WQ_BL(1, true, false); }
     else    { if (sb) WQ_BL(1, false, true); else WQ_BL(1, false, false); }
