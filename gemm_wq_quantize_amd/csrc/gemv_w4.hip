@@ -1156,17 +1156,13 @@ hipError_t launch_c(const KArgs& ka, int layout, hipStream_t s) {
 #ifndef WQ_B_CS16
 #define WQ_B_CS16 2  // column sets per workgroup for 16-column passes
 #endif
-#ifndef WQ_B_CS8
-#define WQ_B_CS8 1   // ... and for 8-column passes
-#endif
 
-template <int C>
-hipError_t launch_batch(const KArgs& ka, int layout, hipStream_t s) {
+template <int C, int CS>
+hipError_t launch_batch_cs(const KArgs& ka, int layout, hipStream_t s, int64_t nrg) {
   // persistent grid: as many workgroups as fit at once (two per CU for 8
-  // columns, one for 16), or one per row-group if there are fewer
-  constexpr int CS = C <= 8 ? WQ_B_CS8 : WQ_B_CS16;
-  const int64_t nrg = (ka.n + 4 * BT_RW - 1) / (4 * BT_RW);
-  const unsigned blocks = (unsigned)std::min<int64_t>(nrg, (int64_t)cu_count() * (C <= 8 ? 2 : 1));
+  // columns in 256 lanes, else one), or one per row-group if there are fewer
+  const unsigned blocks =
+      (unsigned)std::min<int64_t>(nrg, (int64_t)cu_count() * (C <= 8 && CS == 1 ? 2 : 1));
   const bool hz = ka.zeros != nullptr, sb = ka.scale_bf16 != 0;
   const bool xs = (ka.k / 32 + BT_CH - 1) / BT_CH <= 2;  // x fits both buffers
 #define WQ_BL(L, Z, S)                                                                           \
@@ -1185,6 +1181,20 @@ hipError_t launch_batch(const KArgs& ka, int layout, hipStream_t s) {
   }
 #undef WQ_BL
   return hipGetLastError();
+}
+
+template <int C>
+hipError_t launch_batch(const KArgs& ka, int layout, hipStream_t s) {
+  const int64_t nrg = (ka.n + 4 * BT_RW - 1) / (4 * BT_RW);
+  if constexpr (C > 8) {
+    return launch_batch_cs<C, WQ_B_CS16>(ka, layout, s, nrg);
+  } else {
+    // 8 columns: two 256-lane workgroups per CU when there are row-groups
+    // for them, else one 512-lane workgroup whose two column sets give each
+    // SIMD a second wave
+    if (nrg < 2 * (int64_t)cu_count()) return launch_batch_cs<C, 2>(ka, layout, s, nrg);
+    return launch_batch_cs<C, 1>(ka, layout, s, nrg);
+  }
 }
 
 hipError_t launch_bf16(const KArgs& ka, int layout, hipStream_t s) {
