@@ -723,7 +723,12 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
 //    at the small-batch shapes;
 //  * x is double-buffered in LDS per tile and filled by buffer loads that
 //    write LDS directly; each lane then sums the chunks it loaded itself
-//    (the per-chunk sums of x), so one barrier per tile suffices;
+//    (the per-chunk sums of x), so one barrier per tile suffices; when all
+//    of x fits the two buffers (K <= 4096) it is staged once instead and the
+//    loop has no barrier at all;
+//  * 16-column passes run 512-lane workgroups of two column sets; 8-column
+//    passes run two 256-lane workgroups per CU, or one of two column sets
+//    when there are fewer than two row-groups per CU;
 //  * weights and scales run two tiles ahead in a register ring, issued
 //    without branches (past-the-end offsets read zero);
 //  * after the last tile each wave sums its 64 lanes with DPP in a fixed
