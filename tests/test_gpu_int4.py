@@ -265,16 +265,21 @@ def test_gemv_closed_forms():
     assert np.all(np.abs(got) <= bound)
 
 
-def test_gemv_repeatable():
-    say("gemv bitwise repeatable")
-    p = wq_inputs.decode_int4(5120, 4096, cmax=4, seed=3)
+@pytest.mark.parametrize("k,n,c", [(5120, 4096, 4), (5120, 4096, 8), (4096, 11008, 8),
+                                   (4096, 4096, 16), (5120, 1000, 32)])
+def test_gemv_repeatable(k, n, c):
+    # fixed-order sums in every path: the persistent decode kernel (c <= 4)
+    # and the wide-batch kernel in each of its forms (x staged once or per
+    # tile, one or two column sets) give the same bits on every call
+    say("gemv bitwise repeatable", k, n, c)
+    p = wq_inputs.decode_int4(k, n, cmax=c, seed=3)
     packed = gpu_pack(p.codes, 1)
     s_d = dev(p.scale_bits, torch.bfloat16)
     xb = dev(p.x_bits, torch.bfloat16)
     outs = []
     for _ in range(3):
-        out = torch.empty((4, 4096), dtype=torch.float32, device="cuda")
-        G.wq_gemv_w4(packed, 1, s_d, None, 8.0, 5120, 128, xb, out)
+        out = torch.empty((c, n), dtype=torch.float32, device="cuda")
+        G.wq_gemv_w4(packed, 1, s_d, None, 8.0, k, 128, xb, out)
         outs.append(out.cpu().numpy().copy())
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
