@@ -675,9 +675,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restr
 
   // Per row block bi: its 8 products (sub-block j, column block bj) with
   // the x scale applied to each product's int32 sums, then the weight scales
-  // of its rows.  The j loop is not unrolled, so at most two products' sums
-  // are live (unrolled, the compiler issued all 16 products of a step at
-  // once and spilled their results).
+  // of its rows.  The j loop is unrolled by two only, so at most four
+  // products' sums are live (fully unrolled, the compiler issued all 16
+  // products of a step at once and spilled their results; by two it saves
+  // address arithmetic, 1.19 -> 1.14 ms at 4096 x 17280 x 5120).
   auto compute = [&](int st) {
     const uint8_t* ws = wt + st * TG_WST;
     const uint8_t* xs = xt + st * TG_XST;
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restr
       f32x16 t0, t1;
 #pragma unroll
       for (int e = 0; e < 16; ++e) t0[e] = t1[e] = 0.f;
-#pragma unroll 1
+#pragma unroll 2
       for (int j = 0; j < 4; ++j) {  // 32-k sub-block: one q8_1 block of every column
         const i32x4 af = *reinterpret_cast<const i32x4*>(wrow0 + bi * 32 * TG_PITCH + 32 * j);
         const i32x4 b0 = *reinterpret_cast<const i32x4*>(xcol0 + 32 * j);
