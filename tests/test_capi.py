@@ -55,6 +55,12 @@ def test_validation_errors_without_gpu(lib):
     # empty problems are no-ops that succeed without touching pointers
     assert lib.wq_gemv_w4(None, 1, None, 2, None, 8.0, 0, 128, 128, None, 2, 1, None, 2, None) == 0
     assert lib.wq_gemv_ternary(None, None, 10, 128, 0, None, None) == 0
+    assert lib.wq_pack_int4(None, 0, 8, 1, None, None) == 0
+    assert lib.wq_quantize_pack_int4(None, 4, 0, 128, 1, None, None, 2, None) == 0
+    assert lib.wq_gemm_w4a16(None, None, 1, None, 128, 8.0, 0, 64, 128, None, None) == 0
+    assert lib.wq_gemm_w4a16_zp(None, None, 1, None, None, 128, 64, 0, 128, None, None) == 0
+    assert lib.wq_pack_ptq1_0(None, None, 0, 128, None, None) == 0
+    assert lib.wq_quantize_q8_1(None, 0, 64, None, None) == 0
     # null pointers / bad enums / negative sizes
     assert lib.wq_pack_int4(None, 4, 8, 1, FAKE, None) == g.WQ_EINVAL
     assert lib.wq_pack_int4(FAKE, 4, 8, 7, FAKE, None) == g.WQ_EINVAL
