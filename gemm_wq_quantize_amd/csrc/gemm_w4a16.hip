@@ -38,12 +38,12 @@
 // Each step's stage also holds, for every column of the tile, the aligned
 // 4-byte word of the scale array that contains s[j][group of the step]
 // (one 4-byte buffer-to-LDS load per lane; which half holds the scale
-// follows from the parity of j * groups + group).  A lane unpacks each code
-// straight to float32 (128 + q, by OR-ing the nibble into the mantissa of
-// 128.0f), forms (128 + q) * s - (128 + z) * s = (q - z) * s with one FMA --
-// exact, the product needs at most 21 significant bits -- and rounds the
-// pair to bf16 (RNE) for the MFMA.  No row sums are needed; the only
-// rounding beyond the float32 accumulation is that of (q - z) * s to bf16.
+// follows from the parity of j * groups + group).  A lane converts each code
+// straight to float32 (a byte convert after one mask), forms
+// q * s - z * s = (q - z) * s with one FMA -- exact, the product needs at
+// most 17 significant bits -- and rounds the pair to bf16 (RNE) for the
+// MFMA.  No row sums are needed; the only rounding beyond the float32
+// accumulation is that of (q - z) * s to bf16.
 #include "wq_internal.h"
 
 namespace wq {
@@ -134,21 +134,36 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds_bas
                : "memory", "m0");
 }
 
-// eight codes of one gfx950-layout word -> bf16x8 of (q - z) * s, k order:
-// c = -(128 + z) * s.  Element 2j sits in bits 4j..4j+3, element 2j+1 in bits
-// 16+4j..16+4j+3; moved to bits 16..19 under the exponent of 128.0f
-// (magic_v = 0x43000000) they read as 128 + q.  VOP3 takes no literal, so the
-// mask is a scalar operand of v_and_or_b32.
-__device__ __forceinline__ bf16x8 unpack8_scaled(uint32_t w, float s, float c, uint32_t magic_v) {
+// byte b of v as float32: v_cvt_f32_ubyte{0..3} (written out: the compiler
+// otherwise extracts the byte with a separate v_bfe_u32)
+__device__ __forceinline__ float cvt_ubyte(uint32_t v, int b) {
+  float r;
+  if (b == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+  else if (b == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+  else if (b == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
+// eight codes of one gfx950-layout word -> bf16x8 of (q - z) * s, k order,
+// with c = -z * s.  Nibble p holds element {0,2,4,6,1,3,5,7}[p]; the even
+// nibbles masked in place are the bytes of elements 0, 4, 1, 5, the odd ones
+// shifted down those of 2, 6, 3, 7, and each byte converts to float with one
+// v_cvt_f32_ubyteN.  q * s + c is exact in float32 (bf16 s, and z an integer
+// or bf16, so z * s and the sum need at most 17 significant bits), so the
+// only rounding is the one to bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 unpack8_scaled(uint32_t w, float s, float c) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   typedef float f2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint32_t ev = w & 0x0F0F0F0Fu;         // bytes: elements 0, 4, 1, 5
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // bytes: elements 2, 6, 3, 7
+  auto ub = [](uint32_t v, int b) { return cvt_ubyte(v, b); };
+  const float e[8] = {ub(ev, 0), ub(ev, 2), ub(od, 0), ub(od, 2), ub(ev, 1), ub(ev, 3), ub(od, 1), ub(od, 3)};
   u32x4 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float lo = __uint_as_float(and_or(w << (16 - 4 * j), 0x000F0000u, magic_v));
-    const float hi = __uint_as_float(and_or(j == 0 ? w : w >> (4 * j), 0x000F0000u, magic_v));
-    const f2 v = {fmaf(lo, s, c), fmaf(hi, s, c)};
+    const f2 v = {fmaf(e[2 * j], s, c), fmaf(e[2 * j + 1], s, c)};
     r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
   }
   return __builtin_bit_cast(bf16x8, r);
@@ -309,7 +324,6 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   const int lr = lane & 31;   // operand row (A) / column (B) within a 32-block
   const int lh = lane >> 5;   // k half: chunks 4 lh .. 4 lh + 3 of every step
   const uint32_t magic_v = vconst(0x43004300u);
-  const uint32_t magic_m = vconst(0x43000000u);
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 
   // LDS byte offsets (within a stage) of this lane's operands
@@ -347,7 +361,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       gsc[j] = __uint_as_float(hi ? (sw[j] & 0xFFFF0000u) : (sw[j] << 16));
-      const float z = GZ ? 128.f + __uint_as_float(hi ? (zw[j] & 0xFFFF0000u) : (zw[j] << 16)) : zb;
+      const float z = GZ ? __uint_as_float(hi ? (zw[j] & 0xFFFF0000u) : (zw[j] << 16)) : p.zero_const;
       gof[j] = -z * gsc[j];
     }
   };
@@ -395,7 +409,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
-      bfr[j] = unpack8_scaled(w, gsc[j], gof[j], magic_m);
+      bfr[j] = unpack8_scaled(w, gsc[j], gof[j]);
     }
   };
   auto mm = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
