@@ -112,8 +112,10 @@ __global__ __launch_bounds__(256) void k_quantize_pack(const uint16_t* __restric
 // adds at most 2^-21: t = RN(w / s) + 8.5 + 2^-18 + e with |e| < 2^-19.
 // floor(t) is therefore rint(RN(w / s)) + 8 unless RN(w / s) is a
 // half-integer (a tie, which rounds to even) or t crossed an integer, and in
-// both cases fract(t) < 2^-17; a wave with any lane where fract(t) <= 2^-17
-// recomputes its codes with the IEEE divide.  The clamp to [-8, 7] cannot
+// both cases fract(t) < 2^-17; a lane where fract(t) <= 2^-17 recomputes
+// that code with the IEEE divide (one uniform branch per code: ties of an
+// fp16 weight and a bf16 scale land in a sizeable share of the waves, but
+// rarely on the same code).  The clamp to [-8, 7] cannot
 // bind here: s is at least (absmax / 7)(1 - 2^-9) after rounding, so
 // |w / s| < 7.014, t lies in [1.48, 15.52] and floor(t) in [1, 15] (the
 // exact path keeps the clamp).  s is a normal number, so nothing over- or
@@ -173,7 +175,6 @@ __global__ __launch_bounds__(256) void k_quantize_pack_r(const uint16_t* __restr
   }
   const float r = 1.0f / s;  // IEEE; +inf when s == 0 (codes are then 8)
   uint32_t word[WPL];
-  bool near = false;
 #pragma unroll
   for (int i = 0; i < WPL; ++i) {
     const uint32_t h[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -182,23 +183,17 @@ __global__ __launch_bounds__(256) void k_quantize_pack_r(const uint16_t* __restr
     for (int e = 0; e < 8; ++e) {
       const float x = f16_to_f32(e & 1 ? h[e >> 1] >> 16 : h[e >> 1] & 0xFFFFu);
       const float t = fmaf(x, r, 8.5f + 0x1p-18f);
-      near |= __builtin_amdgcn_fractf(t) <= 0x1p-17f;
+      const bool near = __builtin_amdgcn_fractf(t) <= 0x1p-17f;
       c[e] = (int)(uint32_t)t;  // floor: t > 0 (the clamp cannot bind, see above)
+      // exact quotient for this code where any lane of the wave needs it:
+      // exact ties of an fp16 weight and a bf16 scale are common enough
+      // that most waves have one somewhere, but rarely at the same code
+      if (__builtin_amdgcn_ballot_w64(near) != 0) {  // uniform
+        const int ce = (int)fminf(fmaxf(rintf(x / s), -8.f), 7.f) + 8;
+        if (near) c[e] = ce;
+      }
     }
     word[i] = pack8<LAYOUT>(c);
-  }
-  if (__builtin_amdgcn_ballot_w64(near) != 0) {  // uniform: exact quotients
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-      const uint32_t h[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      int c[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = f16_to_f32(e & 1 ? h[e >> 1] >> 16 : h[e >> 1] & 0xFFFFu);
-        c[e] = (int)fminf(fmaxf(rintf(x / s), -8.f), 7.f) + 8;
-      }
-      word[i] = pack8<LAYOUT>(c);
-    }
   }
   if (!active) return;
   uint32_t* dst = packed + ((int64_t)row * k + (int64_t)g * group) / 8;
