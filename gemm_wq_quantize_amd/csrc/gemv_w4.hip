@@ -461,6 +461,7 @@ __device__ __forceinline__ float halfwave_sum(float v) {
 // zero scale -- they contribute exactly nothing.  Offsets are 32-bit,
 // relative to the workgroup's rows, and advance by additions only.
 constexpr uint32_t OOB = 0x80000000u;
+constexpr int PERSIST_XCHUNKS = 3;  // x chunks a lane stages (C * K / 32 <= 3 * lanes)
 
 template <int NT, int R, int C, int LAYOUT, int D, bool HZ, bool SBF>
 __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
@@ -542,19 +543,23 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
 
   // Staging loads are issued before the weight prologue: loads complete in
   // issue order, so waiting for them must not also wait for the weights.
-  constexpr int XU = 10;  // per-lane x staging loads (the launcher bounds x)
-  const int xunits = C * nch * 4;
-  uint4 xr[XU];
+  // A lane stages whole 32-k chunks (all four 16-byte pieces), so the
+  // lanes of one LDS write cover consecutive chunks of one piece plane:
+  // no bank conflicts (lanes writing the four pieces of one chunk would hit
+  // the same banks, the planes being a multiple of 256 bytes apart).
+  constexpr int XCU = PERSIST_XCHUNKS;  // chunks per lane (the launcher bounds x)
+  const int cunits = C * nch;
+  uint4 xr[XCU][4];
 #pragma unroll
-  for (int i = 0; i < XU; ++i) {
-    const int idx = tid + i * NT;
-    xr[i] = make_uint4(0, 0, 0, 0);
-    if (idx < xunits) {
-      const int col = idx / (nch * 4);
-      const int kk = (idx - col * nch * 4) * 8;
-      if (col < p.c && kk < p.k)
-        xr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) + col * p.k + kk);
-    }
+  for (int i = 0; i < XCU; ++i) {
+    const int cidx = tid + i * NT;
+    const int col = cidx / nch;
+    const int kk = (cidx - col * nch) * 32;
+    const bool ok = cidx < cunits && col < p.c && kk < p.k;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      xr[i][q] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) + col * p.k + kk + 8 * q)
+                    : make_uint4(0, 0, 0, 0);
   }
   // weight prologue: D items in flight per half-wave
 #pragma unroll
@@ -562,22 +567,23 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
 
   // x (zero beyond k and beyond c) and the per-chunk sums of x into LDS
 #pragma unroll
-  for (int i = 0; i < XU; ++i) {
-    const int idx = tid + i * NT;
-    if (i * NT >= xunits) break;  // uniform over the workgroup
-    const uint4 xv = xr[i];
-    float ps = ((bf16_to_f32(xv.x & 0xFFFFu) + bf16_to_f32(xv.x >> 16)) +
-                (bf16_to_f32(xv.y & 0xFFFFu) + bf16_to_f32(xv.y >> 16))) +
-               ((bf16_to_f32(xv.z & 0xFFFFu) + bf16_to_f32(xv.z >> 16)) +
-                (bf16_to_f32(xv.w & 0xFFFFu) + bf16_to_f32(xv.w >> 16)));
-    ps += __shfl_xor(ps, 1);
-    ps += __shfl_xor(ps, 2);
-    if (idx < xunits) {
-      const int col = idx / (nch * 4);
-      const int u = idx - col * nch * 4;
-      const int ch = u >> 2, piece = u & 3;
-      xs[(col * 4 + piece) * nch + ch] = xv;
-      if (piece == 0) sxs[col * nch + ch] = ps;
+  for (int i = 0; i < XCU; ++i) {
+    const int cidx = tid + i * NT;
+    if (i * NT >= cunits) break;  // uniform over the workgroup
+    if (cidx < cunits) {
+      const int col = cidx / nch;
+      const int ch = cidx - col * nch;
+      float pq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 xv = xr[i][q];
+        pq[q] = ((bf16_to_f32(xv.x & 0xFFFFu) + bf16_to_f32(xv.x >> 16)) +
+                 (bf16_to_f32(xv.y & 0xFFFFu) + bf16_to_f32(xv.y >> 16))) +
+                ((bf16_to_f32(xv.z & 0xFFFFu) + bf16_to_f32(xv.z >> 16)) +
+                 (bf16_to_f32(xv.w & 0xFFFFu) + bf16_to_f32(xv.w >> 16)));
+        xs[(col * 4 + q) * nch + ch] = xv;
+      }
+      sxs[col * nch + ch] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
     }
   }
   __syncthreads();
@@ -1096,8 +1102,8 @@ hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
   const bool hz = ka.zeros != nullptr;
   const int64_t lds = C * nch * (64 + 4) + (int64_t)NHW * sph * R * C * 4 + NHW * 3 * 4;
   if (lds > PERSIST_LDS_MAX) return hipErrorInvalidValue;
-  // per-lane staging registers of the kernel (x: 10 units)
-  if (C * nch * 4 > 10 * NT) return hipErrorInvalidValue;
+  // per-lane staging registers of the kernel (x: PERSIST_XCHUNKS chunks)
+  if (C * nch > PERSIST_XCHUNKS * NT) return hipErrorInvalidValue;
   const int sb = ka.scale_bf16 ? 1 : 0;
 #define WQ_PFN(L, Z, S) reinterpret_cast<const void*>(&k_gemv_w4_persist<NT, R, C, L, D, Z, S>)
   const void* fns[2][2][2] = {{{WQ_PFN(0, false, false), WQ_PFN(0, false, true)},
