@@ -210,9 +210,13 @@ def main():
     avg_launch_ms = sum(v["us"] for v in per_call.values()) / len(per_call) * 1e-3
     achieved = (alg_step / n_launch) / (avg_launch_ms * 1e-3) / 1e9
 
+    peaks = measured_peaks(g, torch, dev, alg_step // n_launch, log)
+
     rows = {"gemv_w4_decode": per_call}
     if not args.no_rows:
         rows.update(secondary_rows(g, torch, np, wq_inputs, dev, log))
+        for key in ("gemm_w4a16_8192", "gemm_w4a16_8192_group128"):
+            rows[key]["frac_of_measured_mfma_loop"] = round(rows[key]["TFLOPs"] / peaks["mfma_bf16_TFLOPs"], 4)
 
     if args.calibrate_copy_mb:
         nb = args.calibrate_copy_mb << 20
@@ -259,11 +263,48 @@ def main():
             "alg_bytes_per_launch": round(alg_step / n_launch),
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
             "graph_replay_ms_per_step": round(graph_ms_per_step, 5),
+            "frac_of_measured_read": round(achieved / peaks["hbm_read_GBs_same_bytes"], 4),
         },
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "rows": rows,
     }
     print(json.dumps(result), flush=True)
+
+
+def measured_peaks(g, torch, dev, launch_bytes, log):
+    """What this device sustains, from the library's calibration kernels: a
+    plain streaming read of one decode launch's byte count (rotating copies,
+    so HBM serves it) and of 1 GiB, a bf16 matrix-core loop and an fp32 FMA
+    loop, each timed from HIP graphs of back-to-back launches."""
+    sink = torch.empty(g.wq_peak_read_sink_words(), dtype=torch.int32, device=dev)
+    nb = (launch_bytes + 15) // 16 * 16
+    nc = copies_for(nb, minimum=4)
+    bufs = [torch.empty(nb, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(nc)]
+    same = timed(torch, lambda i: g.wq_peak_read(bufs[i % nc], sink), 4 * nc)
+    del bufs
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    gib = timed(torch, lambda i: g.wq_peak_read(big, sink), 4)
+    del big
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wg_m, it_m = 8 * cus, 512
+    msink = torch.empty(max(wg_m, 64 * cus) * 256, dtype=torch.float32, device=dev)
+    mfma = timed(torch, lambda i: g.wq_peak_mfma_bf16(wg_m, it_m, msink), 4)
+    wg_v, it_v = 64 * cus, 2048
+    valu = timed(torch, lambda i: g.wq_peak_valu_fma(wg_v, it_v, msink), 4)
+    out = {
+        "hbm_read_GBs_same_bytes": round(nb / (same * 1e-3) / 1e9, 1),
+        "read_bytes": nb,
+        "read_us_same_bytes": round(same * 1e3, 2),
+        "hbm_read_GBs_1GiB": round((1 << 30) / (gib * 1e-3) / 1e9, 1),
+        "mfma_bf16_TFLOPs": round(wg_m * 4 * it_m * 8 * 32768 / (mfma * 1e-3) / 1e12, 1),
+        "valu_fp32_fma_TFLOPs": round(wg_v * 256 * it_v * 8 * 2 / (valu * 1e-3) / 1e12, 1),
+        "kernels": "wq_peak_read (1024 lanes per CU, 16-B loads, 4 in flight), wq_peak_mfma_bf16 "
+                   "(8 independent 32x32x16 chains per wave, one wave per SIMD), wq_peak_valu_fma "
+                   "(8 independent v_fma_f32 chains per lane, 64 workgroups per CU)",
+    }
+    log("measured peaks:", json.dumps(out))
+    return out
 
 
 def timed(torch, fn, iters):

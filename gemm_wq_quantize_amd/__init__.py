@@ -33,6 +33,11 @@ _SIGS = {
     "wq_pack_ptq1_0": ([_p, _p, _i64, _i64, _p, _p], _i),
     "wq_quantize_q8_1": ([_p, _i64, _i64, _p, _p], _i),
     "wq_gemv_ternary": ([_p, _p, _i64, _i64, _i64, _p, _p], _i),
+    # calibration kernels (include/wq_peaks.h)
+    "wq_peak_read_sink_words": ([], _i64),
+    "wq_peak_read": ([_p, _i64, _p, _i64, _p], _i),
+    "wq_peak_mfma_bf16": ([_i, _i, _p, _i64, _p], _i),
+    "wq_peak_valu_fma": ([_i, _i, _p, _i64, _p], _i),
 }
 _LIB = None
 
@@ -227,3 +232,38 @@ def wq_gemv_ternary(w_blocks, x_q8, k, out, stream=None):
     d = st.device
     _check("wq_gemv_ternary",
            lib.wq_gemv_ternary(_ptr(w_blocks, d), _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
+
+
+# ---- calibration kernels (include/wq_peaks.h): practical ceilings of the
+# device, for setting kernel times against what it sustains
+
+def wq_peak_read_sink_words() -> int:
+    return lib.wq_peak_read_sink_words()
+
+
+def wq_peak_read(buf, sink, stream=None):
+    """Stream all bytes of ``buf`` (any dtype, 16-byte multiple) through one
+    1024-lane workgroup per CU; ``sink`` is uint32-sized storage of at least
+    ``wq_peak_read_sink_words()`` words (overwritten)."""
+    nbytes = buf.numel() * buf.element_size()
+    _require(sink.element_size() == 4 and sink.numel() >= wq_peak_read_sink_words(),
+             "sink holds wq_peak_read_sink_words() 32-bit words")
+    st = _stream(stream)
+    _check("wq_peak_read", lib.wq_peak_read(_ptr(buf, st.device), nbytes, _ptr(sink, st.device),
+                                            sink.numel(), _sptr(st)))
+
+
+def wq_peak_mfma_bf16(workgroups, iters, sink, stream=None):
+    """bf16 matrix-core loop; flops = workgroups * 4 * iters * 8 * 32768 (2 * 32 * 32 * 16 per product)."""
+    _require(sink.dtype == torch.float32 and sink.numel() >= workgroups * 256, "sink fp32, workgroups * 256")
+    st = _stream(stream)
+    _check("wq_peak_mfma_bf16", lib.wq_peak_mfma_bf16(workgroups, iters, _ptr(sink, st.device), sink.numel(),
+                                                      _sptr(st)))
+
+
+def wq_peak_valu_fma(workgroups, iters, sink, stream=None):
+    """fp32 FMA loop; flops = workgroups * 256 * iters * 8 * 2."""
+    _require(sink.dtype == torch.float32 and sink.numel() >= workgroups * 256, "sink fp32, workgroups * 256")
+    st = _stream(stream)
+    _check("wq_peak_valu_fma", lib.wq_peak_valu_fma(workgroups, iters, _ptr(sink, st.device), sink.numel(),
+                                                    _sptr(st)))

@@ -20,7 +20,8 @@ def lib():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "wq.h")).read()
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     return sorted(set(re.findall(r"^(?:const\s+)?\w+\**\s+\**(wq_\w+)\s*\(", text, re.M)))
 
 
@@ -28,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("wq_pack_int4", "wq_quantize_pack_int4", "wq_gemv_w4", "wq_gemm_w4a16",
                  "wq_pack_ptq1_0", "wq_quantize_q8_1", "wq_gemv_ternary", "wq_status_string",
-                 "wq_abi_version"):
+                 "wq_abi_version", "wq_peak_read", "wq_peak_read_sink_words", "wq_peak_mfma_bf16",
+                 "wq_peak_valu_fma"):
         assert want in names
 
 
@@ -111,3 +113,24 @@ def test_validation_errors_without_gpu(lib):
     assert lib.wq_gemm_w4a16(FAKE, FAKE, 1, P(0x1002), 128, 8.0, 64, 64, 256, FAKE, None) == g.WQ_EALIGN
     assert lib.wq_gemv_ternary(ODD, FAKE, 4, 128, 1, FAKE, None) == g.WQ_EALIGN
     assert lib.wq_gemv_ternary(FAKE, FAKE, 4, 128, 64, P(0x1004), None) == g.WQ_EALIGN
+
+
+def test_calibration_kernels_validate_without_gpu(lib):
+    import gemm_wq_quantize_amd as g
+    words = lib.wq_peak_read_sink_words()
+    assert words >= 4096 * 16
+    assert lib.wq_peak_read(None, 0, None, 0, None) == g.WQ_OK
+    assert lib.wq_peak_read(None, 64, FAKE, words, None) == g.WQ_EINVAL
+    assert lib.wq_peak_read(FAKE, -16, FAKE, words, None) == g.WQ_EINVAL
+    assert lib.wq_peak_read(P(0x1008), 64, FAKE, words, None) == g.WQ_EALIGN
+    assert lib.wq_peak_read(FAKE, 72, FAKE, words, None) == g.WQ_ESHAPE
+    assert lib.wq_peak_read(FAKE, 64, FAKE, words - 1, None) == g.WQ_ESHAPE
+    assert lib.wq_peak_read(FAKE, 1 << 40, FAKE, words, None) == g.WQ_ESHAPE
+    for fn in (lib.wq_peak_mfma_bf16, lib.wq_peak_valu_fma):
+        assert fn(0, 10, None, 0, None) == g.WQ_OK
+        assert fn(4, 10, None, 1024, None) == g.WQ_EINVAL
+        assert fn(-1, 10, FAKE, 1024, None) == g.WQ_EINVAL
+        assert fn(4, 10, ODD, 1024, None) == g.WQ_EALIGN
+        assert fn(4, 0, FAKE, 1024, None) == g.WQ_ESHAPE
+        assert fn(4, 10, FAKE, 1023, None) == g.WQ_ESHAPE
+        assert fn((1 << 20) + 1, 10, FAKE, 1 << 40, None) == g.WQ_ESHAPE
