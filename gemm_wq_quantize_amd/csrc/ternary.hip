@@ -257,15 +257,9 @@ __global__ __launch_bounds__(256) void k_gemv_ternary(const uint32_t* __restrict
 // returns zeros (an all-zero block decodes to digits 0 and scale 0).
 constexpr uint32_t T_OOB = 0x80000000u;
 
-// LDS bank plan (64 banks, 4 bytes): the digit table is stored in LC = 16 or
-// 32 copies interleaved by entry (word LC e + l % LC holds entry e for lane
-// l), so the 64 / LC lanes that share a copy are the only ones that can
-// collide: four lanes over four banks (16 copies) cost a table read about
-// three cycles, two over two (32 copies) two.  32 copies take 32 KB, so they
-// pay where LDS is not what limits the workgroups per CU (c <= 2 and the
-// GEMM: 10.9 -> 10.4 us at c = 1, 1.19 -> 1.15 ms for the GEMM) and cost
-// more than they save at c = 4 and 8 (19.4 -> 22.3 and 29.3 -> 37.1 us, a
-// workgroup fewer per CU); x blocks
+// LDS bank plan (64 banks, 4 bytes): the digit table is stored in 16 copies
+// interleaved by entry (word 16 e + l % 16 holds entry e for lane l), so the
+// four lanes that share a copy are the only ones that can collide; x blocks
 // of 128 int8 are padded to 144 bytes so that the 8 blocks a wave reads at
 // once start in 8 different bank quads.
 #ifndef WQ_T_LPR
@@ -278,39 +272,35 @@ constexpr uint32_t T_OOB = 0x80000000u;
 #define WQ_T_WAVES 4  // waves per SIMD the register budget is sized for
 #endif
 constexpr int TP_LPR = WQ_T_LPR;
-template <int C>
-constexpr int lut_copies() { return C <= 2 ? 32 : 16; }
+constexpr int LUT_COPIES = 16;
 constexpr int XB_WORDS = 36;  // words per padded 128-element x block
 
-// The digit table in LC interleaved copies (256 threads).
-template <int LC>
+// The digit table in LUT_COPIES interleaved copies (256 threads).
 __device__ __forceinline__ void tern_lut_init(uint32_t* lut) {
   const int tid = threadIdx.x;
   {
-    // Thread t owns entry t (words LC t .. LC t + LC - 1) and writes its
-    // copies as LC / 4 16-byte quads in the order (m + t / (64 / LC)) %
-    // (LC / 4): the 16 lanes one ds_write_b128 cycle serves then cover all
-    // 64 banks (writing the copies in order would put every lane of a cycle
-    // in LC / 4 banks).
-    static_assert(LC == 16 || LC == 32, "copy quads");
-    constexpr int NQ = LC / 4;
+    // Thread t owns entry t (words 16 t .. 16 t + 15) and writes its copies
+    // as four 16-byte quads in the order (m + t / 4) % 4: the 16 lanes one
+    // ds_write_b128 cycle serves then cover all 64 banks (writing the copies
+    // in order would put every lane of a cycle in 4 banks).
+    static_assert(LUT_COPIES == 16, "copy quads");
     const uint32_t v = tid;
     const uint32_t ent = (v % 3) | ((v / 3) % 3) << 8 | ((v / 9) % 3) << 16 | ((v / 27) % 3) << 24 |
                          ((v / 81) % 3) << 4;  // entries >= 243 are never indexed by valid data
 #pragma unroll
-    for (int m = 0; m < NQ; ++m)
-      *reinterpret_cast<uint4*>(lut + tid * LC + 4 * ((m + tid / (64 / LC)) % NQ)) =
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<uint4*>(lut + tid * LUT_COPIES + 4 * ((m + (tid >> 2)) & 3)) =
           make_uint4(ent, ent, ent, ent);
   }
 }
 
-// One-time staging of a workgroup's LDS: the digit table in LC
+// One-time staging of a workgroup's LDS: the digit table in LUT_COPIES
 // interleaved copies and the activations (x blocks padded to XB_WORDS words,
 // per-32 sum of q and d).  Columns c..C-1 stage zeros.
-template <int C, int LC>
+template <int C>
 __device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsum, float* xd,
                                            const uint8_t* __restrict__ xq, int bpr, int nsb, int c) {
-  tern_lut_init<LC>(lut);
+  tern_lut_init(lut);
   const int tid = threadIdx.x;
   for (int idx = tid; idx < C * nsb; idx += 256) {
     const int col = idx / nsb, sb = idx - col * nsb;
@@ -339,13 +329,12 @@ __device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsu
 // The 128 digits u = t + 1 of one block (its 7 words in v) in k order:
 // dg[i] holds elements 4i..4i+3, one per byte.  lt is this lane's copy of
 // the digit table.
-template <int LC>
 __device__ __forceinline__ void tern_decode(const uint32_t (&v)[7], const uint32_t* lt,
                                             uint32_t (&dg)[32]) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {  // qs bytes 0..15: element 16 j + b
-    const uint32_t l0 = lt[(v[g] & 0xFF) * LC], l1 = lt[((v[g] >> 8) & 0xFF) * LC];
-    const uint32_t l2 = lt[((v[g] >> 16) & 0xFF) * LC], l3 = lt[(v[g] >> 24) * LC];
+    const uint32_t l0 = lt[(v[g] & 0xFF) * LUT_COPIES], l1 = lt[((v[g] >> 8) & 0xFF) * LUT_COPIES];
+    const uint32_t l2 = lt[((v[g] >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(v[g] >> 24) * LUT_COPIES];
     uint32_t d0, d1, d2, d3, d4;
     transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
     dg[g] = d0; dg[4 + g] = d1; dg[8 + g] = d2; dg[12 + g] = d3; dg[16 + g] = d4;
@@ -353,8 +342,8 @@ __device__ __forceinline__ void tern_decode(const uint32_t (&v)[7], const uint32
 #pragma unroll
   for (int g = 0; g < 2; ++g) {  // qs bytes 16..23: element 80 + 8 j + b
     const uint32_t x = v[4 + g];
-    const uint32_t l0 = lt[(x & 0xFF) * LC], l1 = lt[((x >> 8) & 0xFF) * LC];
-    const uint32_t l2 = lt[((x >> 16) & 0xFF) * LC], l3 = lt[(x >> 24) * LC];
+    const uint32_t l0 = lt[(x & 0xFF) * LUT_COPIES], l1 = lt[((x >> 8) & 0xFF) * LUT_COPIES];
+    const uint32_t l2 = lt[((x >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(x >> 24) * LUT_COPIES];
     uint32_t d0, d1, d2, d3, d4;
     transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
     dg[20 + g] = d0; dg[22 + g] = d1; dg[24 + g] = d2; dg[26 + g] = d3; dg[28 + g] = d4;
@@ -366,12 +355,12 @@ __device__ __forceinline__ void tern_decode(const uint32_t (&v)[7], const uint32
   }
 }
 
-template <int C, int LC>
+template <int C>
 __device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_t* lt,
                                            const uint32_t* xs, const int* xsum, const float* xd,
                                            int bx, int bpr, int nsb, float (&acc)[C]) {
   uint32_t dg[32];
-  tern_decode<LC>(v, lt, dg);
+  tern_decode(v, lt, dg);
   const float dw = f16_to_f32(v[6] >> 16);  // 0 for blocks past the end
 #pragma unroll
   for (int col = 0; col < C; ++col) {
@@ -395,7 +384,7 @@ __device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_
   }
 }
 
-// dynamic LDS: table [256][LC], x [C][bpr][36 words], sum q [C][k/32], d [C][k/32]
+// dynamic LDS: table [256][16], x [C][bpr][36 words], sum q [C][k/32], d [C][k/32]
 // LPR lanes per row (8 or 16): a wave holds 64 / LPR rows, a lane one block
 // of its row per item (an item = LPR consecutive blocks of each row).
 template <int C, int D, int LPR>
@@ -406,9 +395,8 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
   extern __shared__ uint32_t tsm[];
   const int nsb = k / 32;
   const int bpr = k / 128;                                // blocks per row
-  constexpr int LC = lut_copies<C>();
-  uint32_t* lut = tsm;                                    // [256][LC]
-  uint32_t* xs = tsm + 256 * LC;                          // [C][bpr][XB_WORDS]
+  uint32_t* lut = tsm;                                    // [256][LUT_COPIES]
+  uint32_t* xs = tsm + 256 * LUT_COPIES;                  // [C][bpr][XB_WORDS]
   int* xsum = reinterpret_cast<int*>(xs + C * bpr * XB_WORDS);  // [C][nsb]
   float* xd = reinterpret_cast<float*>(xsum + C * nsb);   // [C][nsb]
 
@@ -437,7 +425,7 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
   for (int d = 0; d < D; ++d) issue(d, d);
 
   // ---- one-time staging: digit table and the activations
-  tern_stage<C, LC>(lut, xs, xsum, xd, xq, bpr, nsb, c);
+  tern_stage<C>(lut, xs, xsum, xd, xq, bpr, nsb, c);
   __syncthreads();
 
   float acc[C];
@@ -455,7 +443,7 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
     issue(slot, i + D);  // the slot is free once copied out
     if (i >= nitems) return;  // uniform; no load below
     // blocks past the end loaded zeros (scale 0); x reads stay in the staged range
-    tern_block<C, LC>(v, lut + (lane & (LC - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
+    tern_block<C>(v, lut + (lane & (LUT_COPIES - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
     if (t == ntiles - 1) {  // uniform: the wave leaves its 8-row group
       const int row = (gw + (i / ntiles) * nw) * RPW + lane / LPR;
 #pragma unroll
@@ -501,9 +489,8 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_ksplit(const u
   extern __shared__ uint32_t tsm[];
   const int nsb = k / 32;
   const int bpr = k / 128;
-  constexpr int LC = lut_copies<C>();
-  uint32_t* lut = tsm;                                    // [256][LC]
-  uint32_t* xs = tsm + 256 * LC;                          // [C][bpr][XB_WORDS]
+  uint32_t* lut = tsm;                                    // [256][LUT_COPIES]
+  uint32_t* xs = tsm + 256 * LUT_COPIES;                  // [C][bpr][XB_WORDS]
   int* xsum = reinterpret_cast<int*>(xs + C * bpr * XB_WORDS);  // [C][nsb]
   float* xd = reinterpret_cast<float*>(xsum + C * nsb);   // [C][nsb]
   float* psum = xd + C * nsb;                             // [4 waves][RPW rows][C]
@@ -533,7 +520,7 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_ksplit(const u
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
 
-  tern_stage<C, LC>(lut, xs, xsum, xd, xq, bpr, nsb, c);
+  tern_stage<C>(lut, xs, xsum, xd, xq, bpr, nsb, c);
   __syncthreads();
 
   float acc[C];
@@ -546,7 +533,7 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_ksplit(const u
     issue(slot, i + D);       // the slot is free once copied out
     if (i >= nitems) return;  // uniform; no load below
     const int blk = (t0 + i) * LPR + sub;
-    tern_block<C, LC>(v, lut + (lane & (LC - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
+    tern_block<C>(v, lut + (lane & (LUT_COPIES - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
   };
   for (int i = 0; i < nitems; i += D) {
 #pragma unroll
@@ -607,8 +594,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restr
                                                          const uint8_t* __restrict__ xq,
                                                          float* __restrict__ out, int n, int k,
                                                          int m, int tiles_m) {
-  constexpr int LC = 32;
-  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * LC];
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * LUT_COPIES];
   __shared__ __attribute__((aligned(16))) uint8_t wt[2 * TG_WST];
   __shared__ __attribute__((aligned(16))) uint8_t xt[2 * TG_XST];
   __shared__ __attribute__((aligned(16))) float dws[2 * TG_BN];
@@ -651,7 +637,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restr
   auto put = [&](int st) {  // registers -> LDS stage st
     if (wl) {
       uint32_t dg[32];
-      tern_decode<LC>(pw, lut + (lane & (LC - 1)), dg);
+      tern_decode(pw, lut + (lane & (LUT_COPIES - 1)), dg);
       uint4* dst = reinterpret_cast<uint4*>(wt + st * TG_WST + tid * TG_PITCH);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -734,7 +720,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restr
   };
 
   fetch(0);
-  if (tid < 256) tern_lut_init<LC>(lut);
+  if (tid < 256) tern_lut_init(lut);
   __syncthreads();
   put(0);
   if (bpr > 1) fetch(1);
@@ -814,7 +800,7 @@ template <int C>
 hipError_t launch_ternary_ksplit(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k,
                                  int64_t c, float* out, hipStream_t s) {
   constexpr int S = 2;
-  const int64_t lds = 256 * lut_copies<C>() * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8 +
+  const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8 +
                       4 * 8 * C * 4;
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
@@ -839,7 +825,7 @@ hipError_t launch_ternary_ksplit(const uint32_t* wp, const uint8_t* xq, int64_t 
 template <int C>
 hipError_t launch_ternary_persist(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k,
                                   int64_t c, float* out, hipStream_t s) {
-  const int64_t lds = 256 * lut_copies<C>() * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8;
+  const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8;
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
   static bool attr_set[64] = {};  // per instantiation and device
