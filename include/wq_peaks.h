@@ -24,8 +24,10 @@ extern "C" {
  * reads its own contiguous share, 16 bytes per lane and load, four loads in
  * flight per lane -- the access shape of the decode GEMV without its
  * arithmetic.  sink: sink_words >= wq_peak_read_sink_words() uint32 words,
- * 4-byte aligned (overwritten).  Bytes moved per call: nbytes read, and
- * sink_words * 4 written.
+ * 4-byte aligned; each wave stores the XOR of the words its lanes read into
+ * its own word (16 per workgroup, workgroups = min(CUs, 4096, nbytes / 16)),
+ * the rest of sink is left as it was.  Bytes moved per call: nbytes read,
+ * 64 per workgroup written.
  */
 int64_t wq_peak_read_sink_words(void);
 int wq_peak_read(const void* buf, int64_t nbytes, uint32_t* sink, int64_t sink_words,
