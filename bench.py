@@ -65,8 +65,10 @@ def copies_for(nbytes, minimum=2):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    # about 0.3 s of steps: the device settles at its loaded clock (with 10
+    # warmup steps the timed steps ran 10-15% slower than in steady state)
+    ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the secondary rows")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -187,16 +189,17 @@ def main():
             with torch.cuda.graph(gr, stream=cap):
                 for j in range(ncopy):
                     call(si, c, j)
-        gr.replay()
+        for _ in range(20):
+            gr.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(10):
+        for _ in range(50):
             gr.replay()
         e1.record()
         torch.cuda.synchronize()
-        d = e0.elapsed_time(e1) / (10 * ncopy)
+        d = e0.elapsed_time(e1) / (50 * ncopy)
         alg = s["wbytes"] + 2 * s["k"] * c + 2 * s["n"] * c
         per_call[f"K{s['k']}_N{s['n']}_c{c}"] = {
             "us": round(d * 1e3, 2), "weight_GBs": round(s["wbytes"] / (d * 1e-3) / 1e9, 1),
