@@ -269,7 +269,7 @@ constexpr uint32_t T_OOB = 0x80000000u;
 #define WQ_T_PRIO 1  // progress-based issue priority in the persistent loop
 #endif
 #ifndef WQ_T_WAVES
-#define WQ_T_WAVES 4  // waves per SIMD the register budget is sized for
+#define WQ_T_WAVES 5  // waves per SIMD the register budget is sized for
 #endif
 constexpr int TP_LPR = WQ_T_LPR;
 constexpr int LUT_COPIES = 16;
@@ -788,7 +788,12 @@ int cu_count_t() {
   return cached[dev];
 }
 
-constexpr int TP_D = 4;  // items in flight per lane
+// Items in flight per lane.  Two (with registers for five waves per SIMD)
+// ran c = 2 and 4 14-15% faster than four with four waves (K=5120,
+// N=17280: 14.0 -> 11.9 and 18.4 -> 15.8 us), c = 1 and 8 the same: the
+// shorter ring leaves the registers for a fifth wave, and more waves hide
+// the table-read and permute latencies better than deeper prefetch.
+constexpr int TP_D = 2;
 
 #ifndef WQ_T_KSPLIT_CMAX
 #define WQ_T_KSPLIT_CMAX 1  // widest batch routed to the K-split kernel
