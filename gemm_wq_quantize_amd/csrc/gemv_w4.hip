@@ -1049,7 +1049,11 @@ constexpr int PERSIST_LDS_MAX = 160 * 1024;  // all of a gfx950 CU's LDS
 #define WQ_P_R 2
 #endif
 #ifndef WQ_P_D
-#define WQ_P_D 2
+// Items in flight per half-wave.  One ran 4-6% faster than two at c = 1
+// and 2 and ~1.5% at c = 4 (alternating order, bit-identical), three and
+// four were slower: with 16 waves per CU the loads of the other waves keep
+// HBM busy, and the shorter ring frees registers and issue slots.
+#define WQ_P_D 1
 #endif
 #ifndef WQ_P_PRIO
 #define WQ_P_PRIO 1  // progress-based issue priority in the decode loop
