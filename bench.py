@@ -71,6 +71,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the secondary rows")
+    ap.add_argument("--rows", default="small,gemm,ternary",
+                    help="secondary rows to time (comma list of small, gemm, ternary)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this size (PMC scaling)")
     args = ap.parse_args()
@@ -217,9 +219,11 @@ def main():
 
     rows = {"gemv_w4_decode": per_call}
     if not args.no_rows:
-        rows.update(secondary_rows(g, torch, np, wq_inputs, dev, log))
+        which = {w.strip() for w in args.rows.split(",") if w.strip()}
+        rows.update(secondary_rows(g, torch, np, wq_inputs, dev, log, which))
         for key in ("gemm_w4a16_8192", "gemm_w4a16_8192_group128"):
-            rows[key]["frac_of_measured_mfma_loop"] = round(rows[key]["TFLOPs"] / peaks["mfma_bf16_TFLOPs"], 4)
+            if key in rows:
+                rows[key]["frac_of_measured_mfma_loop"] = round(rows[key]["TFLOPs"] / peaks["mfma_bf16_TFLOPs"], 4)
 
     if args.calibrate_copy_mb:
         nb = args.calibrate_copy_mb << 20
@@ -333,7 +337,18 @@ def timed(torch, fn, iters):
     return s.elapsed_time(e) / (3 * iters)  # ms
 
 
-def secondary_rows(g, torch, np, wq_inputs, dev, log):
+def secondary_rows(g, torch, np, wq_inputs, dev, log, which):
+    rows = {}
+    if "small" in which:
+        rows.update(small_batch_rows(g, torch, wq_inputs, dev, log))
+    if "gemm" in which:
+        rows.update(gemm_rows(g, torch, wq_inputs, dev, log))
+    if "ternary" in which:
+        rows.update(ternary_rows(g, torch, wq_inputs, dev, log))
+    return rows
+
+
+def small_batch_rows(g, torch, wq_inputs, dev, log):
     rows = {}
     # quantise + pack and the small-batch GEMV (bf16 group-128 scales)
     qrow, srow = {}, {}
@@ -367,7 +382,11 @@ def secondary_rows(g, torch, np, wq_inputs, dev, log):
     rows["quantize_pack_int4"] = qrow
     rows["gemv_w4_small_batch"] = srow
     log("quantise / small batch:", json.dumps(qrow), json.dumps(srow))
+    return rows
 
+
+def gemm_rows(g, torch, wq_inputs, dev, log):
+    rows = {}
     # 8192^3 W4A16 GEMM
     q = wq_inputs.large_gemm(n_rows=1)
     a = torch.from_numpy(q.a_bits).view(torch.bfloat16).to(dev)
@@ -391,7 +410,11 @@ def secondary_rows(g, torch, np, wq_inputs, dev, log):
     log("gemm 8192^3, group 128:", json.dumps(rows["gemm_w4a16_8192_group128"]))
     del a, b, c, sg
     torch.cuda.empty_cache()
+    return rows
 
+
+def ternary_rows(g, torch, wq_inputs, dev, log):
+    rows = {}
     # ternary GEMV, K=5120 N=17280
     t = wq_inputs.ternary_gemv(5120, 17280, cmax=8)
     wb = torch.empty((17280, 40, 28), dtype=torch.uint8, device=dev)

@@ -439,8 +439,8 @@ __device__ __forceinline__ float halfwave_sum(float v) {
   return v;
 }
 
-// Persistent variant for bf16 activations whose whole x fits in LDS (the
-// decode batches).  One workgroup of NT lanes per CU; workgroup w owns a
+// Persistent variant for one column of bf16 activations whose whole x fits
+// in LDS (single-token decode).  One workgroup of NT lanes per CU; workgroup w owns a
 // contiguous, balanced block of rows (+-1 row).  Its work is a list of items
 // (row-group of R rows, tile of 1024 k) in row-group-major order, cut into
 // NT/32 equal contiguous ranges, one per half-wave, so every half-wave
@@ -600,7 +600,6 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
   int cg = rg_first, ct = i0 - rg_first * nit;
   const int nsteps = i1 - i0;
   for (int base = 0; base < nsteps; base += D) {
-#if WQ_P_PRIO
     {
       // issue priority from the share of items still to do: waves that
       // are behind (the youngest, which oldest-first arbitration serves last)
@@ -612,7 +611,6 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
       else if (left4 > tot) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
     }
-#endif
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const bool valid = base + d < nsteps;
@@ -711,6 +709,337 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
       if (b > a && a < ihi && b > ilo) v += slots[((h * sph + (rg - hwtab[h * 3 + 2])) * R + r) * C + col];
     }
     const int64_t row = (int64_t)r0 + rg * R + r;
+    if (p.out_bf16)
+      reinterpret_cast<uint16_t*>(p.out)[col * p.n + row] = (uint16_t)f32_to_bf16_rne(v);
+    else
+      reinterpret_cast<float*>(p.out)[col * p.n + row] = v;
+  }
+}
+
+// Decode kernel with activations broadcast inside lane quads (bf16 x, c <= 4,
+// all of x in LDS).
+//
+// Lane l of a wave is (q, r) = (l / 4, l % 4): it owns output row r of the
+// wave's current row-quad and chunk q (32 k) of the current item of 16
+// chunks (512 k), one 16-byte load of its row per item.  The four lanes of
+// a quad sit on four rows at the same k, so they need the same activations:
+// lane r of the quad reads dwords 4r .. 4r + 3 of the chunk's x (16 bytes)
+// from LDS, and each v_dot2c takes x dword e from lane e / 4 of the quad
+// through a DPP quad_perm broadcast on its first operand.  Each x byte read
+// from LDS thus feeds four rows, with no per-row copies in registers.
+//
+// One workgroup of 1024 lanes per CU owns a balanced contiguous block of
+// rows (+-1); its items (row-quad, 512-k slice) in row-quad-major order are
+// cut into 16 equal contiguous ranges, one per wave.  x, and per chunk the
+// offset term -(128 + z) * sum x of the zero-point fold, are staged in LDS
+// once.  A wave sums its partial for a row-quad over the 16 quads (fixed
+// DPP/swizzle order) when it leaves it and parks it in an LDS slot; each
+// output is the sum of its parked partials in wave order (deterministic).
+// Weight loads run D items ahead, issued without branches (past-the-end
+// items read zeros with a zero scale and contribute nothing).
+constexpr int QK_CH = 16;             // chunks per item: one per quad
+constexpr int QK_NT = 1024;           // lanes per workgroup (one per CU)
+constexpr int QK_NW = QK_NT / 64;     // waves per workgroup
+constexpr int QK_XP = 9;              // 16-byte x pieces a lane stages (C * nchp * 4 <= QK_XP * QK_NT)
+
+// chain{0,1} += 16 products of one 32-k chunk (two columns): pair e of the
+// lane's weights times x dword e, taken by DPP from component e % 4 of quad
+// lane e / 4.  The compiler cannot see inside the asm, so the block keeps its
+// own wait states: two before the first DPP read (after a VALU write of its
+// source) and three after the last dot product (before another VALU
+// instruction may read its result).
+__device__ __forceinline__ void qdot2(float& a0, float& a1, const uint4& x0, const uint4& x1,
+                                      const uint32_t (&w)[16]) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %10 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %6, %10 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %3, %11 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %7, %11 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %8, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %5, %13 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %9, %13 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %14 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %6, %14 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %3, %15 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %7, %15 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %16 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %8, %16 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %5, %17 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %9, %17 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %18 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %6, %18 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %3, %19 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %7, %19 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %20 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %8, %20 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %5, %21 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %9, %21 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %22 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %6, %22 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %3, %23 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %7, %23 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %24 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %8, %24 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %5, %25 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %9, %25 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 2"
+      : "+v"(a0), "+v"(a1)
+      : "v"(x0.x), "v"(x0.y), "v"(x0.z), "v"(x0.w), "v"(x1.x), "v"(x1.y), "v"(x1.z), "v"(x1.w),
+        "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]),
+        "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]));
+}
+
+// chain += 16 products of one 32-k chunk (one column)
+__device__ __forceinline__ void qdot1(float& a0, const uint4& x0, const uint32_t (&w)[16]) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %1, %5 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %6 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %3, %7 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %8 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %1, %9 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %10 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %3, %11 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %12 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %1, %13 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %3, %15 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %16 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %1, %17 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %18 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %3, %19 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %20 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 2"
+      : "+v"(a0)
+      : "v"(x0.x), "v"(x0.y), "v"(x0.z), "v"(x0.w),
+        "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]),
+        "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]));
+}
+
+// Sum over the 16 quads of a wave (lanes with the same l % 4), fixed order:
+// the four quads of each DPP row by rotation, then the four rows.
+__device__ __forceinline__ float quadset_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror 4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror 8
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <int C, int LAYOUT, int D, bool HZ, bool SBF>
+__global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
+  extern __shared__ uint4 smem[];
+  const int nchunks = (int)(p.k / 32);
+  const int nkit = (nchunks + QK_CH - 1) / QK_CH;                  // items per row-quad
+  const int nchp = nkit * QK_CH;                                     // chunks per column in LDS
+  const int ngroups = p.gshift < 0 ? 1 : (nchunks >> p.gshift);
+  uint4* xs = smem;                                                  // [C][nchp][4] x pieces
+  float* zs = reinterpret_cast<float*>(xs + C * nchp * 4);          // [C][nchp] chunk terms
+  float* slots = zs + C * nchp;                                      // [NW][spw][4][C]
+  int* wtab = reinterpret_cast<int*>(slots + QK_NW * spw * 4 * C);  // [NW][3]: i0, i1, rq_first
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 2, r = lane & 3;
+  // this workgroup's rows (n < 2^31 is checked by the launcher)
+  const int n32 = (int)p.n, nwg = (int)gridDim.x, b = (int)blockIdx.x;
+  const int r0 = b * (n32 / nwg) + min(b, n32 % nwg);
+  const int count = n32 / nwg + (b < n32 % nwg ? 1 : 0);
+  const int nrq = (count + 3) / 4;
+  const int items = nrq * nkit;
+  const int i0 = wave * items / QK_NW, i1 = (wave + 1) * items / QK_NW;
+  const int rq_first = i0 / nkit;
+  if (lane == 0) {
+    wtab[wave * 3 + 0] = i0;
+    wtab[wave * 3 + 1] = i1;
+    wtab[wave * 3 + 2] = rq_first;
+  }
+
+  const int rowbytes = (int)(p.k / 2);
+  constexpr int ESZ = SBF ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.packed + (int64_t)r0 * rowbytes), 0, count * rowbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)p.scales + (int64_t)r0 * ngroups * ESZ), 0, count * ngroups * ESZ, 0x00020000);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)(HZ ? p.zeros : p.scales) + (int64_t)r0 * ngroups * ESZ), 0,
+      HZ ? count * ngroups * ESZ : 0, 0x00020000);
+
+  // issue position: item (row-quad, slice), this lane's chunk, byte offset of
+  // its 16 bytes and its row's first scale; items left to issue
+  int ikit = i0 - rq_first * nkit, left = i1 - i0;
+  int ich = ikit * QK_CH + q;
+  int ioff = (rq_first * 4 + r) * rowbytes + ich * 16;
+  int isrow = (rq_first * 4 + r) * ngroups;
+  uint4 wv[D];
+  uint32_t sv[D], zv[D];
+  auto issue = [&](const int slot) {
+    const bool ok = left > 0 && ich < nchunks;  // rows past the block read zeros (descriptor)
+    const int g = p.gshift < 0 ? 0 : (ich >> p.gshift);
+    const uint32_t wo = ok ? (uint32_t)ioff : OOB;
+    const uint32_t so = ok ? (uint32_t)((isrow + g) * ESZ) : OOB;
+    wv[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wo, 0, 0));
+    if (SBF) {
+      sv[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)so, 0, 0);
+      if (HZ) zv[slot] = __builtin_amdgcn_raw_buffer_load_b16(zrs, (int)so, 0, 0);
+    } else {
+      sv[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)so, 0, 0);
+      if (HZ) zv[slot] = __builtin_amdgcn_raw_buffer_load_b32(zrs, (int)so, 0, 0);
+    }
+    --left;
+    ich += QK_CH;
+    ioff += QK_CH * 16;
+    if (++ikit == nkit) {
+      ikit = 0;
+      ich = q;
+      ioff += 4 * rowbytes - nkit * QK_CH * 16;
+      isrow += 4 * ngroups;
+    }
+  };
+
+  // x staging loads go out before the weight prologue (loads complete in
+  // issue order, so waiting for x does not wait for the weights).  A lane
+  // stages 16-byte pieces u of the [C][nchp][4] array, u = tid + i * NT
+  // rotated by a per-workgroup offset: every CU reads the same x, and in the
+  // same order they would all ask the same L2 channel at once.  The four
+  // pieces of a chunk stay on four consecutive lanes (the offset is a
+  // multiple of 4).
+  const int npieces = C * nchp * 4;
+  const int xrot = (int)(((uint32_t)b * 2654435761u) % (uint32_t)(npieces >> 2)) * 4;
+  auto piece = [&](int i) {
+    const int v = tid + i * QK_NT + xrot;
+    return v >= npieces ? v - npieces : v;
+  };
+  uint4 xr[QK_XP];
+#pragma unroll
+  for (int i = 0; i < QK_XP; ++i) {
+    const int u = piece(i);
+    const int col = u / (nchp * 4);
+    const int ch = (u >> 2) - col * nchp;
+    const bool ok = tid + i * QK_NT < npieces && col < p.c && ch < nchunks;
+    xr[i] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) +
+                                                 (int64_t)col * p.k + ch * 32 + (u & 3) * 8)
+               : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d);
+
+  // x into LDS; per chunk the offset term of the zero-point fold
+  // -(128 + z) * sum x (with stored zeros: sum x, scaled per row later)
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  const float zfold = HZ ? 1.f : -(128.f + p.zero_const);
+#pragma unroll
+  for (int i = 0; i < QK_XP; ++i) {
+    if (i * QK_NT >= npieces) break;  // uniform
+    const int u = piece(i);
+    const uint4 v = xr[i];
+    float sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), ones, 0.f, false);
+    sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), ones, sx, false);
+    sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), ones, sx, false);
+    sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), ones, sx, false);
+    sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0xB1, 0xF, 0xF, false));  // quad xor 1
+    sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0x4E, 0xF, 0xF, false));  // quad xor 2
+    if (tid + i * QK_NT < npieces) {
+      xs[u] = v;
+      if ((u & 3) == 0) zs[u >> 2] = sx * zfold;
+    }
+  }
+  __syncthreads();
+
+  const float zconst = 128.f + p.zero_const;
+  const uint32_t magic_v = vconst(0x43004300u);
+  float acc[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) acc[j] = 0.f;
+
+  // park the partials of row-quad rq (this wave's slot rq - rq_first)
+  auto park = [&](int rq) {
+    float* dst = slots + ((wave * spw + (rq - rq_first)) * 4 + r) * C;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const float v = quadset_sum(acc[j]);
+      if (q == 0) dst[j] = v;
+      acc[j] = 0.f;
+    }
+  };
+
+  int crq = rq_first, ckit = i0 - rq_first * nkit;  // consume position
+  const int nsteps = i1 - i0;
+  for (int base = 0; base < nsteps; base += D) {
+    {
+      // issue priority from the share of items still to do: waves that are
+      // behind (the youngest, which oldest-first arbitration serves last)
+      // win the SIMD's issue slots
+      const int left4 = 4 * (nsteps - base);
+      if (left4 > 3 * nsteps) __builtin_amdgcn_s_setprio(3);
+      else if (left4 > 2 * nsteps) __builtin_amdgcn_s_setprio(2);
+      else if (left4 > nsteps) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const bool valid = base + d < nsteps;
+      uint32_t wp[16];
+      {
+        const uint32_t w4[4] = {wv[d].x, wv[d].y, wv[d].z, wv[d].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            wp[4 * m + j] = LAYOUT == 1 ? pair_bf16_fast(w4[m], j, magic_v) : pair_bf16<LAYOUT>(w4[m], j);
+      }
+      // past-the-range items and chunks past k loaded a zero scale
+      float sc, zb = zconst;
+      if constexpr (SBF) {
+        sc = bf16_to_f32(sv[d]);
+        if (HZ) zb = 128.f + bf16_to_f32(zv[d]);
+      } else {
+        sc = __uint_as_float(sv[d]);
+        if (HZ) zb = 128.f + __uint_as_float(zv[d]);
+      }
+      issue(d);  // the ring slot is free once unpacked
+      float ch[C];
+      uint4 xv[C];
+      const int xo = ckit * QK_CH + q;  // chunk of this lane, < nchp
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        xv[j] = xs[(j * nchp + xo) * 4 + r];
+        const float z = zs[j * nchp + xo];
+        ch[j] = HZ ? -zb * z : z;
+      }
+#pragma unroll
+      for (int j = 0; j + 1 < C; j += 2) qdot2(ch[j], ch[j + 1], xv[j], xv[j + 1], wp);
+      if constexpr (C % 2 == 1) qdot1(ch[C - 1], xv[C - 1], wp);
+#pragma unroll
+      for (int j = 0; j < C; ++j) acc[j] = fmaf(sc, ch[j], acc[j]);
+      if (valid && ++ckit == nkit) {
+        park(crq);
+        ckit = 0;
+        ++crq;
+      }
+    }
+  }
+  if (nsteps > 0 && ckit != 0) park(crq);
+  __syncthreads();
+
+  // sum the parked partials of each (row, column) in wave order
+  for (int idx = tid; idx < nrq * 4 * C; idx += QK_NT) {
+    const int rq = idx / (4 * C);
+    const int rc = idx - rq * 4 * C;
+    const int rr = rc / C, col = rc - rr * C;
+    if (col >= p.c || rq * 4 + rr >= count) continue;
+    const int ilo = rq * nkit, ihi = ilo + nkit;
+    // wave h owns items [floor(h items / NW), floor((h + 1) items / NW)); the
+    // one owning item i is floor(((i + 1) NW - 1) / items)
+    const int hlo = ((ilo + 1) * QK_NW - 1) / items, hhi = (ihi * QK_NW - 1) / items;
+    float v = 0.f;
+    for (int h = hlo; h <= hhi; ++h) {
+      const int a = wtab[h * 3 + 0], e = wtab[h * 3 + 1];
+      if (e > a && a < ihi && e > ilo) v += slots[((h * spw + (rq - wtab[h * 3 + 2])) * 4 + rr) * C + col];
+    }
+    const int64_t row = (int64_t)r0 + rq * 4 + rr;
     if (p.out_bf16)
       reinterpret_cast<uint16_t*>(p.out)[col * p.n + row] = (uint16_t)f32_to_bf16_rne(v);
     else
@@ -1042,35 +1371,8 @@ hipError_t launch_stream(const KArgs& ka, int layout, hipStream_t s) {
 // ---- persistent launcher
 constexpr int PERSIST_LDS_MAX = 160 * 1024;  // all of a gfx950 CU's LDS
 
-#ifndef WQ_P_NT
-#define WQ_P_NT 1024
-#endif
-#ifndef WQ_P_R
-#define WQ_P_R 2
-#endif
-#ifndef WQ_P_D
-// Items in flight per half-wave.  One ran 4-6% faster than two at c = 1
-// and 2 and ~1.5% at c = 4 (alternating order, bit-identical), three and
-// four were slower: with 16 waves per CU the loads of the other waves keep
-// HBM busy, and the shorter ring frees registers and issue slots.
-#define WQ_P_D 1
-#endif
-#ifndef WQ_P_PRIO
-#define WQ_P_PRIO 1  // progress-based issue priority in the decode loop
-#endif
 
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
+int cu_count() { return device_cu_count(); }
 
 // Largest number of row-groups one half-wave touches, over the two row
 // counts (q and q + 1) the workgroups get.
@@ -1090,7 +1392,11 @@ int persist_slots(int64_t n, int grid, int R, int nit, int nhw) {
 // Returns hipErrorInvalidValue (without launching) when x does not fit in LDS.
 template <int C>
 hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
-  constexpr int NT = WQ_P_NT, R = WQ_P_R, D = WQ_P_D, NHW = NT / 32;
+  // 1024 lanes, two rows per half-wave item, one item in flight per
+  // half-wave (two ran 4-6% slower at one column: with 16 waves per CU the
+  // loads of the other waves keep HBM busy, and the shorter ring frees
+  // registers and issue slots)
+  constexpr int NT = 1024, R = 2, D = 1, NHW = NT / 32;
   if (ka.n >= (int64_t(1) << 31) || ka.k >= (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int64_t nchunks = ka.k / 32;
   const int nit = (int)((nchunks + TILE_CHUNKS - 1) / TILE_CHUNKS);
@@ -1116,37 +1422,81 @@ hipError_t launch_persist(const KArgs& ka, int layout, hipStream_t s) {
                                {WQ_PFN(1, true, false), WQ_PFN(1, true, true)}}};
 #undef WQ_PFN
   const void* fn = fns[layout][hz][sb];
-  // the attribute is per device: set it once on each
-  static bool attr_set[64][2][2][2] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!attr_set[dev][layout][hz][sb]) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, PERSIST_LDS_MAX);
-    if (e != hipSuccess) return e;
-    attr_set[dev][layout][hz][sb] = true;
-  }
+  static std::atomic<uint64_t> lds_ok[2][2][2];  // devices where fn may use all of the LDS
+  const hipError_t le = allow_dynamic_lds(fn, lds_ok[layout][hz][sb], PERSIST_LDS_MAX);
+  if (le != hipSuccess) return le;
   int sph_arg = sph;
   void* args[] = {const_cast<KArgs*>(&ka), &sph_arg};
   return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, (size_t)lds, s);
 }
 
-#ifndef WQ_STREAM_ROWS
-#define WQ_STREAM_ROWS 0
-#endif
+// Largest number of row-quads one wave of the quad kernel touches, over the
+// two row counts (q and q + 1) the workgroups get.
+int quad_slots(int64_t n, int grid, int nkit) {
+  const int64_t q = n / grid;
+  int best = 1;
+  for (int64_t cnt = q; cnt <= q + 1; ++cnt) {
+    const int64_t items = ((cnt + 3) / 4) * nkit;
+    for (int h = 0; h < QK_NW; ++h) {
+      const int64_t a = h * items / QK_NW, b = (h + 1) * items / QK_NW;
+      if (b > a) best = std::max(best, (int)((b - 1) / nkit - a / nkit + 1));
+    }
+  }
+  return best;
+}
 
+// Returns hipErrorInvalidValue (without launching) when x does not fit in LDS.
+template <int C>
+hipError_t launch_quad(const KArgs& ka, int layout, hipStream_t s) {
+  // items in flight per lane: two at c = 2 (one or three were 2-4% slower),
+  // one at c = 3 and 4 (4-5% faster than two there: the loop is bound by
+  // the VALU, and a shorter ring leaves the other waves' loads the HBM)
+  constexpr int D = C <= 2 ? 2 : 1;
+  if (ka.n >= (int64_t(1) << 31) || ka.k >= (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int64_t nchunks = ka.k / 32;
+  const int nkit = (int)((nchunks + QK_CH - 1) / QK_CH);
+  const int64_t nchp = (int64_t)nkit * QK_CH;
+  const int64_t ngroups = ka.gshift < 0 ? 1 : (nchunks >> ka.gshift);
+  int grid = cu_count();
+  if ((int64_t)grid * 4 > ka.n) grid = (int)std::max<int64_t>(1, ka.n / 4);
+  const int64_t maxrows = (ka.n + grid - 1) / grid + 4;
+  // 32-bit offsets within a workgroup's rows (weights and scales)
+  if (maxrows * (ka.k / 2) >= (int64_t(1) << 31) || maxrows * ngroups * 4 >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  if (C * nchp * 4 > (int64_t)QK_XP * QK_NT) return hipErrorInvalidValue;  // staging registers
+  const int spw = quad_slots(ka.n, grid, nkit);
+  const int64_t lds = C * nchp * (64 + 4) + (int64_t)QK_NW * spw * 4 * C * 4 + QK_NW * 3 * 4;
+  if (lds > PERSIST_LDS_MAX) return hipErrorInvalidValue;
+  const bool hz = ka.zeros != nullptr;
+  const int sb = ka.scale_bf16 ? 1 : 0;
+#define WQ_QFN(L, Z, S) reinterpret_cast<const void*>(&k_gemv_w4_quad<C, L, D, Z, S>)
+  const void* fns[2][2][2] = {{{WQ_QFN(0, false, false), WQ_QFN(0, false, true)},
+                               {WQ_QFN(0, true, false), WQ_QFN(0, true, true)}},
+                              {{WQ_QFN(1, false, false), WQ_QFN(1, false, true)},
+                               {WQ_QFN(1, true, false), WQ_QFN(1, true, true)}}};
+#undef WQ_QFN
+  const void* fn = fns[layout][hz][sb];
+  static std::atomic<uint64_t> lds_ok[2][2][2];  // devices where fn may use all of the LDS
+  const hipError_t e = allow_dynamic_lds(fn, lds_ok[layout][hz][sb], PERSIST_LDS_MAX);
+  if (e != hipSuccess) return e;
+  int spw_arg = spw;
+  void* args[] = {const_cast<KArgs*>(&ka), &spw_arg};
+  return hipLaunchKernel(fn, dim3(grid), dim3(QK_NT), args, (size_t)lds, s);
+}
+
+// bf16 x, c <= 4: the persistent kernels when all of x fits in LDS (one
+// column: two rows per lane, x from LDS per lane; two to four columns: x
+// shared by lane quads), else the streaming kernel.
 template <int C>
 hipError_t launch_stream_c(const KArgs& ka, int layout, hipStream_t s) {
-#ifndef WQ_NO_PERSIST
-  if constexpr (C <= 4) {
-    hipError_t e = launch_persist<C>(ka, layout, s);
-    if (e != hipErrorInvalidValue) return e;
-  }
-#endif
-  constexpr int D = C <= 4 ? 4 : (C <= 8 ? 2 : 1);
+  static_assert(C <= 4, "decode batches");
+  hipError_t e;
+  if constexpr (C == 1) e = launch_persist<C>(ka, layout, s);
+  else e = launch_quad<C>(ka, layout, s);
+  if (e != hipErrorInvalidValue) return e;
   // rows per half-wave: 2 when that still leaves >= 4 workgroups per CU
-  if (WQ_STREAM_ROWS == 2 || (WQ_STREAM_ROWS == 0 && C <= 4 && ka.n >= 16 * 1024))
-    return launch_stream<2, C, D>(ka, layout, s);
-  return launch_stream<1, C, D>(ka, layout, s);
+  if (ka.n >= 16 * 1024) return launch_stream<2, C, 4>(ka, layout, s);
+  return launch_stream<1, C, 4>(ka, layout, s);
 }
 
 template <int R, int C, bool XBF16>
@@ -1168,9 +1518,6 @@ hipError_t launch_c(const KArgs& ka, int layout, hipStream_t s) {
   return launch_rc<1, C, XBF16>(ka, layout, s);
 }
 
-#ifndef WQ_B_CS16
-#define WQ_B_CS16 2  // column sets per workgroup for 16-column passes
-#endif
 
 template <int C, int CS>
 hipError_t launch_batch_cs(const KArgs& ka, int layout, hipStream_t s, int64_t nrg) {
@@ -1202,7 +1549,7 @@ template <int C>
 hipError_t launch_batch(const KArgs& ka, int layout, hipStream_t s) {
   const int64_t nrg = (ka.n + 4 * BT_RW - 1) / (4 * BT_RW);
   if constexpr (C > 8) {
-    return launch_batch_cs<C, WQ_B_CS16>(ka, layout, s, nrg);
+    return launch_batch_cs<C, 2>(ka, layout, s, nrg);  // two column sets per workgroup
   } else {
     // 8 columns: two 256-lane workgroups per CU when there are row-groups
     // for them, else one 512-lane workgroup whose two column sets give each
@@ -1241,8 +1588,16 @@ hipError_t launch_f32(const KArgs& ka, int layout, hipStream_t s) {
     default: break;
   }
   if (ka.c <= 8) return launch_c<8, false>(ka, layout, s);
-  if (ka.c <= 16) return launch_c<16, false>(ka, layout, s);
-  return launch_c<32, false>(ka, layout, s);
+  // wider batches: passes of at most 16 columns over x[c0:c0+16] -> out[c0:c0+16]
+  for (int64_t c0 = 0; c0 < ka.c; c0 += 16) {
+    KArgs kp = ka;
+    kp.c = std::min<int64_t>(16, ka.c - c0);
+    kp.x = reinterpret_cast<const float*>(ka.x) + c0 * ka.k;
+    kp.out = reinterpret_cast<char*>(ka.out) + c0 * ka.n * (ka.out_bf16 ? 2 : 4);
+    const hipError_t e = kp.c <= 8 ? launch_c<8, false>(kp, layout, s) : launch_c<16, false>(kp, layout, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

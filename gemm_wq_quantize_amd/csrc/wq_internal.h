@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace wq {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -28,6 +30,37 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
 // float32 -> fp16 bit pattern, round to nearest even.
 __device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Host-side per-device caches.  Each entry is an atomic, so concurrent first
+// calls from several host threads are well defined (at worst both query the
+// runtime and store the same value).
+constexpr int kMaxDevices = 64;
+
+// Compute-unit count of the current device (256 if the runtime cannot say).
+inline int device_cu_count() {
+  static std::atomic<int> cached[kMaxDevices];  // static storage: zero-initialised
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Lets kernel `fn` use up to `bytes` of dynamic LDS on the current device,
+// once per device: `done` is the caller's per-kernel bit set of devices.
+inline hipError_t allow_dynamic_lds(const void* fn, std::atomic<uint64_t>& done, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  const uint64_t bit = uint64_t(1) << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
 }
 
 // Launchers: validated arguments only.  Each returns hipSuccess or the

@@ -101,7 +101,10 @@ def test_gemm_8192_group128_sampled_rows():
     got = c.index_select(0, torch.from_numpy(rows).cuda()).float().cpu().numpy()
     a = fpformat.bf16_bits_to_f32(p.a_bits[rows])
     s = fpformat.bf16_bits_to_f32(p.scale_bits)
-    check_bf16_rows(got, o4.gemm_w4a16_rows_bf16w(a, o4.pack(p.codes, 1), 1, s, 8.0, 128))
+    packed = o4.pack(p.codes, 1)
+    check_bf16_rows(got, o4.gemm_w4a16_rows_bf16w(a, packed, 1, s, 8.0, 128))
+    # and against the plain product (no rounding of the weights), normwise
+    check_bf16_rownorm(got, o4.gemm_w4a16_rows(a, packed, 1, s, 8.0, 128))
     assert torch.isfinite(c.float()).all()
 
 
@@ -161,7 +164,9 @@ def test_gemm_on_quantiser_output():
     assert np.array_equal(packed.cpu().numpy(), o4.pack(codes, 1))
     a = fpformat.bf16_bits_to_f32(a_bits)
     got = c.float().cpu().numpy()
-    check_bf16_rows(got, o4.gemm_w4a16_rows_bf16w(a, o4.pack(codes, 1), 1, s, 8.0, 128))
+    packed_ref = o4.pack(codes, 1)
+    check_bf16_rows(got, o4.gemm_w4a16_rows_bf16w(a, packed_ref, 1, s, 8.0, 128))
+    check_bf16_rownorm(got, o4.gemm_w4a16_rows(a, packed_ref, 1, s, 8.0, 128))
 
 
 # ---- stored zero points (wq_gemm_w4a16_zp)

@@ -223,6 +223,28 @@ def test_gemv_ragged_and_dtypes(case):
         check_bf16_rows(got, ref)
 
 
+# One case per launch path of wq_gemv_w4 that the workloads above do not
+# reach: bf16 x too large for the persistent kernel's LDS (the streaming
+# kernel, c = 3 and 4 at K = 28672), the persistent kernel on plain-layout
+# weights with stored bf16 zeros, fp32 x with N >= 16384 (two rows per
+# half-wave), and fp32 x wider than 16 columns (passes of 16).
+PATHS = [
+    # n, k, group, c, x dtype, scale dtype, zeros, out dtype, layout
+    (2048, 28672, 128, 3, "bf16", "bf16", False, torch.bfloat16, 1),
+    (2048, 28672, 128, 4, "bf16", "bf16", False, torch.bfloat16, 1),
+    (500, 2048, 128, 2, "bf16", "bf16", True, torch.bfloat16, 0),
+    (16400, 1024, 128, 3, "f32", "f32", False, torch.float32, 1),
+    (16400, 1024, 64, 8, "f32", "bf16", True, torch.float32, 0),
+    (300, 1024, 64, 24, "f32", "f32", True, torch.float32, 1),
+    (131, 2048, 2048, 32, "f32", "bf16", False, torch.bfloat16, 1),
+]
+
+
+@pytest.mark.parametrize("case", PATHS, ids=[f"n{c[0]}k{c[1]}g{c[2]}c{c[3]}{c[4]}l{c[8]}" for c in PATHS])
+def test_gemv_launch_paths(case):
+    test_gemv_ragged_and_dtypes(case)
+
+
 @pytest.mark.parametrize("xdt,c", [("bf16", 4), ("f32", 4), ("bf16", 16)])
 def test_gemv_integer_exact(xdt, c):
     say("gemv integer exact", xdt, c)
