@@ -33,6 +33,7 @@ BF16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
+SETTLE_S = 0.4              # seconds of step replays before the warm-up steps
 
 
 def log(*a):
@@ -66,9 +67,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    # about 0.3 s of steps: the device settles at its loaded clock (with 10
-    # warmup steps the timed steps ran 10-15% slower than in steady state)
-    ap.add_argument("--warmup", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the secondary rows")
     ap.add_argument("--rows", default="small,gemm,ternary",
@@ -143,11 +142,22 @@ def main():
         graphs.append(gr)
     torch.cuda.synchronize()
 
+    # Settle: the device needs a few tenths of a second of sustained work to
+    # reach its loaded clock (with a handful of warm-up steps the timed steps
+    # ran 10-15% slower), so graph replays of the step run for SETTLE_S
+    # seconds whatever --warmup says; then the W counted warm-up steps.
+    t_settle = time.perf_counter()
+    j = 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(50):
+            graphs[j % ncopy].replay()
+            j += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         graphs[i % ncopy].replay()
         step_eager(i)
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
+    log(f"settled for {time.perf_counter() - t_settle:.2f} s ({j} replays), warmup {args.warmup} steps done")
 
     # The timed region: K steps launched back to back on the current stream
     # (what a caller sees), bracketed by events and synchronisations.
@@ -246,6 +256,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -451,13 +462,45 @@ def ternary_rows(g, torch, wq_inputs, dev, log):
 
 def cpu_baseline(np, wq_inputs, log):
     """The oracle, untouched, on whole steps of the same workload (the 6
-    GEMVs), repeated until at least 10 s of CPU time have been timed."""
+    GEMVs), repeated until at least 10 s of CPU time have been timed, with
+    its BLAS pool set to the host cores this process may run on; plus the
+    tiny int4 GEMV (256 x 512, one column) on one thread."""
     from oracle import int4 as o4
+    threads = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+        from threadpoolctl import threadpool_limits
+    except Exception:  # no pool control: the BLAS default (reported as is)
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=threads) if threadpool_limits else _nullcontext()
+    with ctx:
+        out = _cpu_steps(np, o4, wq_inputs, log, threads)
+    # the tiny per-row fp32 GEMV on one thread
+    p = wq_inputs.tiny_int4()
+    packed = o4.pack(p.codes, 0)
+    ctx1 = threadpool_limits(limits=1) if threadpool_limits else _nullcontext()
+    with ctx1:
+        reps, t1 = 0, 0.0
+        while t1 < 1.0:
+            t0 = time.perf_counter()
+            o4.gemv_w4(packed, 0, p.scales, p.zeros, 0.0, p.k, p.x)
+            t1 += time.perf_counter() - t0
+            reps += 1
+    tiny_bytes = packed.nbytes + p.scales.nbytes + p.zeros.nbytes
+    out["tiny_int4_gemv_1_thread"] = {"us_per_call": round(t1 / reps * 1e6, 1),
+                                      "GBs": round(tiny_bytes * reps / t1 / 1e9, 4), "calls": reps}
+    log(f"cpu oracle, tiny GEMV on 1 thread: {t1 / reps * 1e6:.1f} us per call")
+    return out
+
+
+class _nullcontext:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+def _cpu_steps(np, o4, wq_inputs, log, threads):
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
@@ -477,7 +520,7 @@ def cpu_baseline(np, wq_inputs, log):
                 total_bytes += packed.nbytes + p.scale_bits.nbytes
         steps += 1
     v = total_bytes / total_s / 1e9
-    log(f"cpu oracle: {steps} steps in {total_s:.2f} s, {v:.3f} GB/s, {threads} threads ({model})")
+    log(f"cpu oracle: {steps} steps in {total_s:.2f} s, {v:.3f} GB/s, {threads} cores ({model})")
     return {"value": round(v, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "cpu": model,
             "sample": f"{steps} full steps of the 6 decode GEMVs (both shapes, c = 1, 2, 4), "

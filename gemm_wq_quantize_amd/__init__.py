@@ -202,7 +202,8 @@ def wq_pack_ptq1_0(trits, d, blocks, stream=None):
     """trits int8 [n][k], d fp16 [n][k/128] -> PTQ1_0 blocks uint8 [n][k/128][28]."""
     n, k = trits.shape
     _require(trits.dtype == torch.int8 and blocks.dtype == torch.uint8, "trits int8, blocks uint8")
-    _require(d.element_size() == 2 and d.numel() == n * (k // 128), "d holds n * k / 128 fp16 values")
+    _require(d.dtype in (torch.float16, torch.int16, torch.uint16), "d is fp16 (or its bits)")
+    _require(d.numel() == n * (k // 128), "d holds n * k / 128 fp16 values")
     _require(blocks.numel() == n * (k // 128) * 28, "blocks hold n * k / 128 * 28 bytes")
     st = _stream(stream)
     dv = st.device

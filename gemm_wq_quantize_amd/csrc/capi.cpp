@@ -173,8 +173,8 @@ int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int
   if (n < 0 || k < 0 || c < 0) return WQ_EINVAL;
   if (n == 0 || c == 0) return WQ_OK;
   if (!w_blocks || !x_q8 || !out) return WQ_EINVAL;
-  // up to 16 columns on the vector units; 64 or more on the int8 matrix cores
-  if (k == 0 || k % 128 != 0 || (c > 16 && c < 64)) return WQ_ESHAPE;
+  // up to 16 columns per pass on the vector units; 64 or more on the int8 matrix cores
+  if (k == 0 || k % 128 != 0) return WQ_ESHAPE;
   if (!aligned(w_blocks, 4) || !aligned(x_q8, 4) || !aligned(out, c >= 64 ? 16 : 4)) return WQ_EALIGN;
   if (n / 32 + 1 > kMaxGrid) return WQ_ESHAPE;
   if (c >= 64) {  // 32-bit buffer offsets and the tile grid

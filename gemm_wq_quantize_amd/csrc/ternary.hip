@@ -262,16 +262,8 @@ constexpr uint32_t T_OOB = 0x80000000u;
 // four lanes that share a copy are the only ones that can collide; x blocks
 // of 128 int8 are padded to 144 bytes so that the 8 blocks a wave reads at
 // once start in 8 different bank quads.
-#ifndef WQ_T_LPR
-#define WQ_T_LPR 8  // lanes per row in the persistent ternary GEMV
-#endif
-#ifndef WQ_T_PRIO
-#define WQ_T_PRIO 1  // progress-based issue priority in the persistent loop
-#endif
-#ifndef WQ_T_WAVES
-#define WQ_T_WAVES 5  // waves per SIMD the register budget is sized for
-#endif
-constexpr int TP_LPR = WQ_T_LPR;
+constexpr int TP_LPR = 8;     // lanes per row in the persistent ternary GEMV
+constexpr int TP_WAVES = 5;   // waves per SIMD the register budget is sized for
 constexpr int LUT_COPIES = 16;
 constexpr int XB_WORDS = 36;  // words per padded 128-element x block
 
@@ -388,7 +380,7 @@ __device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_
 // LPR lanes per row (8 or 16): a wave holds 64 / LPR rows, a lane one block
 // of its row per item (an item = LPR consecutive blocks of each row).
 template <int C, int D, int LPR>
-__global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const uint32_t* __restrict__ w,
+__global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_persist(const uint32_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
                                                               float* __restrict__ out, int n, int k,
                                                               int c) {
@@ -460,7 +452,7 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
   };
   // groups of D items keep the ring slot a compile-time constant
   for (int i = 0; i < nitems; i += D) {
-    if constexpr (WQ_T_PRIO && C <= 4) {
+    if constexpr (C <= 4) {
       // issue priority from the share of items still to do (waves that fall
       // behind are served first; 4-5% at 2 and 4 columns, a loss at 8)
       if (4 * (nitems - i) > 3 * nitems) __builtin_amdgcn_s_setprio(3);
@@ -481,7 +473,7 @@ __global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_persist(const 
 // S times more waves run, and the S partial sums of a row are added in LDS in
 // part order.
 template <int C, int D, int S>
-__global__ __launch_bounds__(256, WQ_T_WAVES) void k_gemv_ternary_ksplit(const uint32_t* __restrict__ w,
+__global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_ksplit(const uint32_t* __restrict__ w,
                                                              const uint8_t* __restrict__ xq,
                                                              float* __restrict__ out, int n, int k,
                                                              int c) {
@@ -775,29 +767,12 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x
   return hipGetLastError();
 }
 
-int cu_count_t() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
-
 // Items in flight per lane.  Two (with registers for five waves per SIMD)
 // ran c = 2 and 4 14-15% faster than four with four waves (K=5120,
 // N=17280: 14.0 -> 11.9 and 18.4 -> 15.8 us), c = 1 and 8 the same: the
 // shorter ring leaves the registers for a fifth wave, and more waves hide
 // the table-read and permute latencies better than deeper prefetch.
 constexpr int TP_D = 2;
-
-#ifndef WQ_T_KSPLIT_CMAX
-#define WQ_T_KSPLIT_CMAX 1  // widest batch routed to the K-split kernel
-#endif
 
 // K-split launch (S = 2) when x fits in LDS; returns hipErrorInvalidValue (no
 // launch) otherwise.
@@ -809,15 +784,10 @@ hipError_t launch_ternary_ksplit(const uint32_t* wp, const uint8_t* xq, int64_t 
                       4 * 8 * C * 4;
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
-  static bool attr_set[64] = {};  // per instantiation and device
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set[dev] = true;
-  }
+  static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S>),
+                                         lds_ok, 160 * 1024);
+  if (e != hipSuccess) return e;
   const int64_t nrg = (n + 7) / 8;
   const int64_t grid = (nrg + (4 / S) - 1) / (4 / S);
   hipLaunchKernelGGL((k_gemv_ternary_ksplit<C, TP_D, S>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
@@ -833,50 +803,31 @@ hipError_t launch_ternary_persist(const uint32_t* wp, const uint8_t* xq, int64_t
   const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8;
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
-  static bool attr_set[64] = {};  // per instantiation and device
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set[dev] = true;
-  }
+  static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR>),
+                                         lds_ok, 160 * 1024);
+  if (e != hipSuccess) return e;
   const int64_t nrg = (n + 64 / TP_LPR - 1) / (64 / TP_LPR);
   // workgroups resident at once: LDS and the waves per SIMD the register
   // budget allows
-  const int per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(WQ_T_WAVES, (160 * 1024) / lds));
-  const int64_t grid = std::min<int64_t>((nrg + 3) / 4, (int64_t)cu_count_t() * per_cu);
+  const int per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(TP_WAVES, (160 * 1024) / lds));
+  const int64_t grid = std::min<int64_t>((nrg + 3) / 4, (int64_t)device_cu_count() * per_cu);
   hipLaunchKernelGGL((k_gemv_ternary_persist<C, TP_D, TP_LPR>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
                      wp, xq, out, (int)n, (int)k, (int)c);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
-                               int64_t c, float* out, hipStream_t s) {
+// Up to 16 columns on the vector units.
+hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
+                                 int64_t c, float* out, hipStream_t s) {
   const uint32_t* wp0 = reinterpret_cast<const uint32_t*>(w);
-  if (c >= 64) {  // a batch wide enough for the int8 matrix cores
-    const int tiles_m = (int)((c + TG_BM - 1) / TG_BM), tiles_n = (int)((n + TG_BN - 1) / TG_BN);
-    hipLaunchKernelGGL(k_gemm_ternary, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s, wp0, xq,
-                       out, (int)n, (int)k, (int)c, tiles_m);
-    return hipGetLastError();
-  }
   {
     // (a single column runs slightly faster on the tiled kernel below, whose
     // per-tile staging is small at c = 1)
+    // one column: the K-split kernel (wider splits spilled registers)
     hipError_t e = hipErrorInvalidValue;
-    if (c <= WQ_T_KSPLIT_CMAX) {
-      switch (c) {
-        case 1: e = launch_ternary_ksplit<1>(wp0, xq, n, k, c, out, s); break;
-#if WQ_T_KSPLIT_CMAX >= 2
-        case 2: e = launch_ternary_ksplit<2>(wp0, xq, n, k, c, out, s); break;
-#endif
-#if WQ_T_KSPLIT_CMAX >= 3
-        default: e = launch_ternary_ksplit<4>(wp0, xq, n, k, c, out, s); break;
-#else
-        default: break;
-#endif
-      }
+    if (c == 1) {
+      e = launch_ternary_ksplit<1>(wp0, xq, n, k, c, out, s);
       if (e != hipErrorInvalidValue) return e;
     }
     switch (c) {
@@ -901,6 +852,24 @@ hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, i
   }
 #undef WQ_TG
   return hipGetLastError();
+}
+
+
+hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
+                               int64_t c, float* out, hipStream_t s) {
+  if (c >= 64) {  // a batch wide enough for the int8 matrix cores
+    const int tiles_m = (int)((c + TG_BM - 1) / TG_BM), tiles_n = (int)((n + TG_BN - 1) / TG_BN);
+    hipLaunchKernelGGL(k_gemm_ternary, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s,
+                       reinterpret_cast<const uint32_t*>(w), xq, out, (int)n, (int)k, (int)c, tiles_m);
+    return hipGetLastError();
+  }
+  // 17..63 columns: passes of at most 16 over x[c0:c0+16] -> out[c0:c0+16]
+  for (int64_t c0 = 0; c0 < c; c0 += 16) {
+    const hipError_t e = launch_ternary_narrow(w, xq + c0 * (k / 32) * Q8_BYTES, n, k,
+                                               std::min<int64_t>(16, c - c0), out + c0 * n, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace wq

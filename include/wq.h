@@ -204,12 +204,13 @@ int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* 
  *   w_blocks  [n][k/128] PTQ1_0 blocks.
  *   x_q8      [c][k/32] block_q8_1.
  *   out       [c][n] float32.
- * Requires 1 <= c <= 16 or c >= 64 (0 is a no-op), k % 128 == 0, w_blocks
- * and x_q8 4-byte aligned, out 4-byte aligned (16-byte for c >= 64).
+ * Requires c >= 0 (0 is a no-op), k % 128 == 0, w_blocks and x_q8 4-byte
+ * aligned, out 4-byte aligned (16-byte for c >= 64).  Up to 16 columns run
+ * on the vector units; 17 <= c <= 63 runs as passes of at most 16 columns.
  * c >= 64 (a prefill batch) runs on the int8 matrix cores
  * (v_mfma_i32_32x32x32_i8: one product per 32-k activation block, so S is
  * still exact in int32); it also requires n * k / 128 * 28 and c * k / 32 * 36
- * below 2^31 (32-bit offsets).  17 <= c <= 63 is WQ_ESHAPE.
+ * below 2^31 (32-bit offsets).
  */
 int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k,
                     int64_t c, float* out, void* stream);

@@ -106,6 +106,22 @@ def test_ternary_special_cases():
             check_f32(got, ref)
 
 
+@pytest.mark.parametrize("k,n,c", [(1024, 300, 24), (5120, 2000, 40), (384, 77, 63)])
+def test_ternary_gemv_passes_of_16(k, n, c):
+    # 17..63 columns run as passes of at most 16 columns (the last one ragged)
+    say("ternary gemv in passes", k, n, c)
+    p = wq_inputs.ternary_gemv(k, n, cmax=c, seed=c + k)
+    wb = gpu_blocks(p.trits, p.d_bits)
+    xq = gpu_q8(p.x)
+    xref = ot.quantize_q8_1(p.x)
+    assert np.array_equal(xq.cpu().numpy(), xref)
+    check_f32(gpu_gemv(wb, xq, k), ot.gemv_ternary(ot.encode_ptq1_0(p.trits, p.d_bits), xref))
+    u = wq_inputs.ternary_gemv(k, n, cmax=c, seed=c, unit_scale=True)
+    got = gpu_gemv(gpu_blocks(u.trits, u.d_bits), gpu_q8(u.x), k)
+    exact = u.x.astype(np.int64) @ u.trits.astype(np.int64).T
+    assert np.array_equal(got, exact.astype(np.float64))
+
+
 # ---- 64 or more columns: the int8 matrix-core kernel
 @pytest.mark.parametrize("k,n,c", [(1024, 256, 64), (640, 333, 200), (5120, 2048, 128),
                                    (384, 77, 130)])
