@@ -22,6 +22,7 @@ Pages cited (short names used in docstrings):
 Parity pins live in ``tests/test_oracle_*.py``.  Functions whose reading is
 pinned only by invariants (not by a value printed on the pages) say
 "parity unpinned" in their docstring: the int4 quantiser formula, the gfx950
-nibble order and the ternary digit encoding.
+nibble order, the ternary digit encoding and the PTQ1_1 bit positions and
+codebook order (pinned by round trips, sizes and hand-worked bytes only).
 """
 from . import fpformat, int4, ternary  # noqa: F401

@@ -31,6 +31,37 @@ two; they are pinned by round trips and by the post's byte-0 example only):
            S[r, c, b] = sum_i t * q over each block of 32 (s is stored for
            fidelity; the exact path never uses it):
            y[c, r] = sum_b d_w[r, b // 4] * d_x[c, b] * S[r, c, b].
+
+PTQ1_1 superblock (section 2, struct ptq1_1; section 3.1, sb = kbx >> 3,
+sub = kbx & 7): eight consecutive PTQ1_0 blocks of a row in 216 bytes --
+qs[192], qh[13], eight 10-bit mantissas, one exponent byte.  The post fixes
+the sizes and the idea (the sign of d is always +; the eight 5-bit exponents
+become an index into 768 patterns made of the exponent byte and the free
+trit of qh, 767 meaning "look the superblock up in an external table"),
+not the bit positions.  Readings (parity unpinned beyond the round trips,
+sizes and hand-worked bytes of the tests):
+  R-sb     A row's K/128 blocks form K/1024 superblocks of 8 consecutive
+           blocks (block kbx is sub-block kbx & 7 of superblock kbx >> 3);
+           K must be a multiple of 1024.  Superblocks are [N][K/1024].
+  R-sbqs   Bytes 0..191: the qs[24] of sub-blocks 0..7 in order, unchanged
+           (section 3.1 reads qs of sub-block sub as a uint8_t[24] at sub).
+  R-sbqh   Bytes 192..204 (qh[13]): the 64 tail trits (elements 120..127 of
+           each sub-block, digit u = t + 1) in sub-block order, tail trit
+           8 sub + e in byte (8 sub + e) // 5 at base-3 digit
+           (8 sub + e) % 5, digit 0 least significant -- five to a byte as in
+           qs; digit 4 of qh[12] is the free trit.
+  R-sbm    Bytes 205..214: the ten bytes of an 80-bit little-endian field
+           holding mantissa sub (the low 10 bits of d) at bits 10 sub.
+  R-sbe    Byte 215 and the free trit: pattern index P = byte + 256 * free
+           digit (0..767).  P < 767 selects row P of a 767 x 8 codebook of
+           exponent fields; P = 767 means the superblock's 8 exponents come
+           from the escape table (superblock indices row * K/1024 + sb in
+           ascending order, with their 8 exponents).  d = (e << 10) | m.
+  R-sbcb   Codebook (the encoder's choice; the post builds it from the
+           statistics of trained weights): the exponent patterns of the
+           tensor by decreasing count, ties by increasing pattern (e_0..e_7
+           compared in order), the first min(767, #patterns) of them; unused
+           rows are zero; every other superblock escapes.
 """
 from __future__ import annotations
 
@@ -158,3 +189,171 @@ def gemv_ternary(w_blocks: np.ndarray, x_blocks: np.ndarray) -> np.ndarray:
     dw32 = np.repeat(dw, QK // Q8_QK, axis=1)                       # [N][K/32]
     y = np.einsum("rcb,rb,cb->cr", S, dw32, dx)
     return y
+
+
+# --------------------------------------------------------------------------
+# PTQ1_1 superblocks
+# --------------------------------------------------------------------------
+SB_BLOCKS = 8        # PTQ1_0 blocks per superblock
+SB_BYTES = 216       # 192 qs + 13 qh + 10 mantissa + 1 exponent byte
+SB_QH = 192          # byte offset of qh[13]
+SB_MANT = 205        # byte offset of the 80-bit mantissa field
+SB_EXP = 215         # byte offset of the exponent (pattern) byte
+CODEBOOK_ROWS = 767  # pattern indices 0..766; 767 is the escape
+ESCAPE = 767
+
+
+def tail_position(t: int):
+    """Tail trit t (0..63, = 8 sub + e) of a superblock -> (qh byte, digit).
+    Position 64 (byte 12, digit 4) is the free trit."""
+    return t // 5, t % 5
+
+
+def pattern_fields(p: int):
+    """Pattern index (0..767) -> (exponent byte, free-trit digit)."""
+    return p & 0xFF, p >> 8
+
+
+def pattern_index(byte: int, digit: int) -> int:
+    """(exponent byte, free-trit digit) -> pattern index; inverse of
+    ``pattern_fields``."""
+    return byte + 256 * digit
+
+
+def mantissa_bytes(mant) -> np.ndarray:
+    """Eight 10-bit mantissas -> the 10 bytes of the little-endian 80-bit
+    field, mantissa sub at bit 10 sub."""
+    field = 0
+    for sub, m in enumerate(mant):
+        field |= (int(m) & 0x3FF) << (10 * sub)
+    return np.frombuffer(field.to_bytes(10, "little"), dtype=np.uint8).copy()
+
+
+def mantissas(field_bytes) -> list:
+    """Inverse of ``mantissa_bytes``."""
+    field = int.from_bytes(bytes(np.asarray(field_bytes, dtype=np.uint8)), "little")
+    return [(field >> (10 * sub)) & 0x3FF for sub in range(SB_BLOCKS)]
+
+
+def superblock_index(row: int, sb: int, nsb: int) -> int:
+    """Global index of superblock sb of a row (the key of the escape table)."""
+    return row * nsb + sb
+
+
+def exponent_patterns(d_bits: np.ndarray) -> np.ndarray:
+    """fp16 scale bits [N][K/128] -> exponent fields [N][K/1024][8].  The sign
+    must be 0 (the post drops it: d is always positive)."""
+    d = np.asarray(d_bits, dtype=np.uint16)
+    n, nb = d.shape
+    assert nb % SB_BLOCKS == 0, "K must be a multiple of 1024"
+    assert not np.any(d >> 15), "PTQ1_1 stores no sign: every d must be >= +0"
+    return ((d >> 10) & 0x1F).astype(np.int64).reshape(n, nb // SB_BLOCKS, SB_BLOCKS)
+
+
+def codebook_order(counts: dict) -> list:
+    """Reading R-sbcb: patterns by decreasing count, ties by increasing
+    pattern."""
+    return [pat for pat, _ in sorted(counts.items(), key=lambda kv: (-kv[1], kv[0]))]
+
+
+def build_codebook(patterns: np.ndarray):
+    """The 767 first patterns of ``codebook_order``.  Returns (codebook uint8
+    [767][8], {pattern: row})."""
+    counts = {}
+    for row in np.asarray(patterns).reshape(-1, SB_BLOCKS):
+        pat = tuple(int(v) for v in row)
+        counts[pat] = counts.get(pat, 0) + 1
+    book = np.zeros((CODEBOOK_ROWS, SB_BLOCKS), dtype=np.uint8)
+    index = {}
+    for row, pat in enumerate(codebook_order(counts)[:CODEBOOK_ROWS]):
+        book[row] = pat
+        index[pat] = row
+    return book, index
+
+
+def encode_ptq1_1(blocks: np.ndarray):
+    """PTQ1_0 blocks uint8 [N][K/128][28] -> (superblocks uint8
+    [N][K/1024][216], codebook uint8 [767][8], escape indices int64 [n_esc],
+    escape patterns uint8 [n_esc][8])."""
+    b = np.asarray(blocks, dtype=np.uint8)
+    n, nb, _ = b.shape
+    assert nb % SB_BLOCKS == 0, "K must be a multiple of 1024"
+    nsb = nb // SB_BLOCKS
+    d = (b[:, :, 26].astype(np.int64) | (b[:, :, 27].astype(np.int64) << 8))
+    pats = exponent_patterns(d.astype(np.uint16))
+    book, index = build_codebook(pats)
+    out = np.zeros((n, nsb, SB_BYTES), dtype=np.uint8)
+    esc = []
+    for r in range(n):
+        for sb in range(nsb):
+            blk = b[r, sb * SB_BLOCKS:(sb + 1) * SB_BLOCKS]
+            dd = d[r, sb * SB_BLOCKS:(sb + 1) * SB_BLOCKS]
+            sup = out[r, sb]
+            # qs: the eight qs[24] arrays in sub-block order
+            sup[:SB_QH] = blk[:, :24].reshape(-1)
+            # tail trits: element 120 + e of sub-block sub is qh[e & 1] bits
+            # 2 (e >> 1) of that block (reading R-qh); it is tail trit 8 sub + e
+            qh = [0] * 13
+            for sub in range(SB_BLOCKS):
+                for e in range(8):
+                    u = (int(blk[sub, 24 + (e & 1)]) >> (2 * (e >> 1))) & 3
+                    byte, digit = tail_position(8 * sub + e)
+                    qh[byte] += u * 3 ** digit
+            pat = tuple(int(v) for v in pats[r, sb])
+            p = index.get(pat, ESCAPE)
+            ebyte, free = pattern_fields(p)
+            byte, digit = tail_position(64)
+            qh[byte] += free * 3 ** digit
+            sup[SB_QH:SB_MANT] = qh
+            sup[SB_MANT:SB_EXP] = mantissa_bytes(dd & 0x3FF)
+            sup[SB_EXP] = ebyte
+            if p == ESCAPE:
+                esc.append((superblock_index(r, sb, nsb), pat))
+    esc.sort()
+    return (out, book, np.array([g for g, _ in esc], dtype=np.int64),
+            np.array([pt for _, pt in esc], dtype=np.uint8).reshape(-1, SB_BLOCKS))
+
+
+def superblock_pattern(sup: np.ndarray, gidx: int, codebook, esc_idx, esc_pat):
+    """The eight exponent fields of superblock ``sup`` (216 bytes), global
+    index gidx (section 3.1: the pattern lookup takes the superblock's index,
+    the codebook and the escape table)."""
+    byte, digit = tail_position(64)
+    free = (int(sup[SB_QH + byte]) // 3 ** digit) % 3
+    p = pattern_index(int(sup[SB_EXP]), free)
+    if p < ESCAPE:
+        return [int(v) for v in codebook[p]]
+    j = int(np.searchsorted(esc_idx, gidx))
+    assert j < len(esc_idx) and int(esc_idx[j]) == gidx, "escaped superblock missing from the table"
+    return [int(v) for v in esc_pat[j]]
+
+
+def decode_ptq1_1(sup: np.ndarray, codebook, esc_idx, esc_pat) -> np.ndarray:
+    """Superblocks uint8 [N][K/1024][216] -> the PTQ1_0 blocks uint8
+    [N][K/128][28] they hold (section 3.1: qs of sub-block sub, its eight
+    tail trits, its scale -- "the same as the PTQ1_0 format")."""
+    s = np.asarray(sup, dtype=np.uint8)
+    n, nsb, _ = s.shape
+    out = np.zeros((n, nsb * SB_BLOCKS, BLOCK_BYTES), dtype=np.uint8)
+    for r in range(n):
+        for sb in range(nsb):
+            x = s[r, sb]
+            exps = superblock_pattern(x, superblock_index(r, sb, nsb), codebook, esc_idx, esc_pat)
+            mant = mantissas(x[SB_MANT:SB_EXP])
+            for sub in range(SB_BLOCKS):
+                blk = out[r, sb * SB_BLOCKS + sub]
+                blk[:24] = x[24 * sub:24 * sub + 24]
+                qh = [0, 0]
+                for e in range(8):
+                    byte, digit = tail_position(8 * sub + e)
+                    u = (int(x[SB_QH + byte]) // 3 ** digit) % 3
+                    qh[e & 1] |= u << (2 * (e >> 1))
+                blk[24], blk[25] = qh
+                dbits = (exps[sub] << 10) | mant[sub]
+                blk[26], blk[27] = dbits & 0xFF, dbits >> 8
+    return out
+
+
+def gemv_ternary_ptq1_1(sup, codebook, esc_idx, esc_pat, x_blocks) -> np.ndarray:
+    """y[c, r] for PTQ1_1 weights: the PTQ1_0 GEMV of the decoded blocks."""
+    return gemv_ternary(decode_ptq1_1(sup, codebook, esc_idx, esc_pat), x_blocks)

@@ -26,8 +26,11 @@ def _int4_pins():
 
 
 def _ternary_pins():
-    return [f for name, f in sorted(vars(pins_ternary).items())
-            if name.startswith("test_") and f.__code__.co_argcount == 0]
+    out = [f for name, f in sorted(vars(pins_ternary).items())
+           if name.startswith("test_") and f.__code__.co_argcount == 0]
+    out.append(lambda: pins_ternary.test_ptq1_1_round_trip(False, 40, 5120))
+    out.append(lambda: pins_ternary.test_ptq1_1_round_trip(True, 240, 8192))
+    return out
 
 
 # ------------------------------------------------------------ planted mistakes
@@ -160,6 +163,41 @@ def _subblock_off_by_one(mp):
     mp.setattr(ternary, "subblock_sums", subblock_sums)
 
 
+def _sb_tail_strided(mp):
+    # the stride of the PTQ1_0 sections (byte t % 13, digit t // 13) instead
+    # of five consecutive tail trits per byte
+    mp.setattr(ternary, "tail_position", lambda t: (t % 13, t // 13))
+
+
+def _sb_pattern_3b(mp):
+    # pattern index 3 * byte + digit instead of byte + 256 * digit
+    mp.setattr(ternary, "pattern_fields", lambda p: (p // 3, p % 3))
+    mp.setattr(ternary, "pattern_index", lambda byte, digit: 3 * byte + digit)
+
+
+def _sb_mantissa_big_endian(mp):
+    def mantissa_bytes(mant):
+        field = 0
+        for sub, m in enumerate(mant):
+            field |= (int(m) & 0x3FF) << (10 * sub)
+        return np.frombuffer(field.to_bytes(10, "big"), dtype=np.uint8).copy()
+
+    def mantissas(field_bytes):
+        field = int.from_bytes(bytes(np.asarray(field_bytes, dtype=np.uint8)), "big")
+        return [(field >> (10 * sub)) & 0x3FF for sub in range(8)]
+    mp.setattr(ternary, "mantissa_bytes", mantissa_bytes)
+    mp.setattr(ternary, "mantissas", mantissas)
+
+
+def _sb_ties_descending(mp):
+    mp.setattr(ternary, "codebook_order",
+               lambda counts: [pat for pat, _ in sorted(counts.items(), key=lambda kv: (-kv[1], tuple(-v for v in kv[0])))])
+
+
+def _sb_escape_key_without_row(mp):
+    mp.setattr(ternary, "superblock_index", lambda row, sb, nsb: sb)
+
+
 CASES = {
     "int4: low nibble holds the odd k": (_swap_nibbles, _int4_pins),
     "int4: gfx950 order replaced by its inverse": (_inverse_interleave, _int4_pins),
@@ -175,6 +213,11 @@ CASES = {
     "ternary: weight scale paired with the wrong sub-blocks": (_weight_scale_per_32, _ternary_pins),
     "ternary: q8_1 scale amax / 128": (_q8_divisor_128, _ternary_pins),
     "ternary: sub-block sum off by one": (_subblock_off_by_one, _ternary_pins),
+    "ptq1_1: tail trits strided over qh": (_sb_tail_strided, _ternary_pins),
+    "ptq1_1: pattern index 3 * byte + free digit": (_sb_pattern_3b, _ternary_pins),
+    "ptq1_1: mantissa field big-endian": (_sb_mantissa_big_endian, _ternary_pins),
+    "ptq1_1: codebook ties by decreasing pattern": (_sb_ties_descending, _ternary_pins),
+    "ptq1_1: escape table keyed by the superblock within its row": (_sb_escape_key_without_row, _ternary_pins),
 }
 
 

@@ -1,5 +1,6 @@
 """Pins of the ternary oracle against the Ternary post and closed forms."""
 import numpy as np
+import pytest
 
 from oracle import fpformat, ternary
 from conftest import load_golden
@@ -144,3 +145,109 @@ def test_ternary_special_cases():
     for c in range(2):
         assert y[c, 2] == -dwf[2, 0] * dx[c, 77] * q[c, 77]
         assert np.all(np.delete(y[c], 2) == 0)
+
+
+# ---- PTQ1_1 superblocks (Ternary post, section 2 struct ptq1_1; section 3.1)
+def test_ptq1_1_sizes_match_post():
+    g = load_golden("ptq1_0_layout.txt")
+    assert ternary.SB_BYTES == int(g["superblock_bytes"][0])
+    # trits: qs + qh = 205 bytes against 8 * (24 + 2) = 208
+    assert ternary.SB_MANT == int(g["superblock_trit_bytes"][0])
+    assert 8 * 26 == int(g["plain_trit_bytes_per_1024"][0])
+    # scales: 10 mantissa bytes + 1 exponent byte = 11 against 8 * 2 = 16
+    assert ternary.SB_BYTES - ternary.SB_MANT == int(g["superblock_scale_bytes"][0])
+    assert 8 * 2 == int(g["plain_scale_bytes_per_8"][0])
+    # 256 exponent-byte values x 3 free-trit digits; the last is the escape
+    assert 256 * 3 == int(g["superblock_patterns"][0])
+    assert ternary.ESCAPE == int(g["superblock_escape_index"][0]) == ternary.CODEBOOK_ROWS
+    # 13 bytes hold 65 trits: the 64 tail trits and one free trit
+    assert 13 * 5 == 8 * 8 + 1 and ternary.tail_position(64) == (12, 4)
+    sup, _, _, _ = ternary.encode_ptq1_1(ternary.encode_ptq1_0(np.zeros((2, 2048), np.int8),
+                                                               np.full((2, 16), 0x3C00, np.uint16)))
+    assert sup.shape == (2, 2, 216)
+
+
+def test_ptq1_1_handworked_single_superblock():
+    g = load_golden("ptq1_1_handworked.txt")
+    t = np.zeros((1, 1024), np.int8)
+    t[0, 128 + 121] = 1                     # sub-block 1, element 121
+    d = np.full((1, 8), 0x3C00, np.uint16)
+    d[0, 7] = 0x3801
+    sup, book, ei, ep = ternary.encode_ptq1_1(ternary.encode_ptq1_0(t, d))
+    s = sup[0, 0]
+    assert all(int(v) == 121 for v in s[:192])
+    assert _ints(s[192:205]) == _ints(g["a_qh"])
+    assert _ints(s[205:215]) == _ints(g["a_mantissa_bytes"])
+    assert int(s[215]) == int(g["a_exponent_byte"][0])
+    assert _ints(book[0]) == _ints(g["a_codebook_row0"]) and not book[1:].any()
+    assert len(ei) == 0 and ep.shape == (0, 8)
+
+
+def test_ptq1_1_handworked_escape():
+    g = load_golden("ptq1_1_handworked.txt")
+    nsb = 768
+    e = np.zeros((nsb, 8), np.int64)
+    j = np.arange(767)
+    e[:767, 6] = j // 31
+    e[:767, 7] = j % 31
+    e[767, :] = 30
+    d = (e.reshape(1, nsb * 8) << 10).astype(np.uint16)
+    t = np.zeros((1, nsb * 1024), np.int8)
+    sup, book, ei, ep = ternary.encode_ptq1_1(ternary.encode_ptq1_0(t, d))
+    esc = sup[0, 767]
+    assert int(esc[204]) == int(g["b_escape_qh12"][0])
+    assert int(esc[215]) == int(g["b_escape_exponent_byte"][0])
+    assert _ints(ei) == _ints(g["b_escape_index"])
+    assert _ints(ep[0]) == _ints(g["b_escape_pattern"])
+    assert _ints(book[5]) == _ints(g["b_row5_pattern"])
+    assert int(sup[0, 5, 215]) == int(g["b_sb5_exponent_byte"][0])
+    assert int(sup[0, 5, 204]) == int(g["b_sb5_qh12"][0])
+    # and the decoder finds the escaped scales again
+    blocks = ternary.decode_ptq1_1(sup, book, ei, ep)
+    _, d2 = ternary.decode_ptq1_0(blocks)
+    assert np.array_equal(d2, d)
+
+
+def test_ptq1_1_tail_positions_exhaustive():
+    # each of the 64 tail trits set alone to +1 (digit 2, the rest digit 1)
+    # raises exactly one qh byte by 3^digit at the reading's position
+    for tt in range(64):
+        sub, e = divmod(tt, 8)
+        t = np.zeros((1, 1024), np.int8)
+        t[0, 128 * sub + 120 + e] = 1
+        sup, _, _, _ = ternary.encode_ptq1_1(ternary.encode_ptq1_0(t, np.full((1, 8), 0x3C00, np.uint16)))
+        qh = sup[0, 0, 192:205].astype(int)
+        byte, digit = ternary.tail_position(tt)
+        base = np.array([121] * 12 + [40])
+        base[byte] += 3 ** digit
+        assert np.array_equal(qh, base), tt
+        assert qh.max() <= 242
+
+
+@pytest.mark.parametrize("independent,n,k", [(False, 40, 5120), (True, 240, 8192)])
+def test_ptq1_1_round_trip(independent, n, k):
+    # correlated scales (few patterns, no escape) and independent exponents
+    # (many more patterns than codebook rows: most superblocks escape)
+    p = wq_inputs.ternary_correlated_scales(k, n, 1, seed=n)
+    d = p.d_bits
+    if independent:
+        rng = np.random.default_rng(k)
+        d = ((rng.integers(5, 13, d.shape) << 10) | rng.integers(0, 1024, d.shape)).astype(np.uint16)
+    blocks = ternary.encode_ptq1_0(p.trits, d)
+    sup, book, ei, ep = ternary.encode_ptq1_1(blocks)
+    if independent:
+        assert len(ei) >= n * k // 1024 - 2 * 767  # (a few patterns repeat)
+    assert np.array_equal(ternary.decode_ptq1_1(sup, book, ei, ep), blocks)
+    assert sup[:, :, 192:205].max() <= 242
+    assert np.all(np.diff(ei) > 0)
+    # the GEMV of the superblocks is the GEMV of the blocks they hold
+    xq = ternary.quantize_q8_1(p.x)
+    assert np.array_equal(ternary.gemv_ternary_ptq1_1(sup, book, ei, ep, xq),
+                          ternary.gemv_ternary(blocks, xq))
+
+
+def test_ptq1_1_rejects_negative_scale():
+    d = np.full((1, 8), 0x3C00, np.uint16)
+    d[0, 3] = 0xBC00
+    with pytest.raises(AssertionError):
+        ternary.encode_ptq1_1(ternary.encode_ptq1_0(np.zeros((1, 1024), np.int8), d))

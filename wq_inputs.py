@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "to_bf16_bits", "to_f16_bits", "bf16_bits_to_f32", "f16_bits_to_f32",
     "tiny_int4", "decode_int4", "small_batch_int4", "large_gemm", "grouped_gemm",
-    "ternary_gemv", "DECODE_SHAPES", "SMALL_BATCH_SHAPES",
+    "ternary_gemv", "ternary_correlated_scales", "DECODE_SHAPES", "SMALL_BATCH_SHAPES",
 ]
 
 # (K, N) pairs: the two projections of one transformer layer at these widths.
@@ -183,4 +183,33 @@ def ternary_gemv(k: int = 5120, n: int = 17280, cmax: int = 8, seed: int = 0,
     else:
         d_bits = to_f16_bits(rng.uniform(0.01, 0.05, (n, k // 128)))
         x = rng.standard_normal((cmax, k)).astype(np.float32)
+    return TernaryProblem(n, k, trits, d_bits, x)
+
+
+def ternary_correlated_scales(k: int = 5120, n: int = 17280, cmax: int = 8, seed: int = 0,
+                              p_change: float = 0.075) -> TernaryProblem:
+    """Ternary GEMV whose block scales have the exponent statistics the
+    ternary post reports for trained weights (section 2: the sign is always
+    positive, the exponents of neighbouring blocks rarely differ, and eight
+    consecutive blocks almost never leave a set of 768 exponent patterns).
+
+    Draws: trits U{-1,0,1} [N][K]; per row a starting fp16 exponent field
+    U{8, 9, 10} (scales in [2^-7, 2^-4), the range of the U(0.01, 0.05)
+    scales of the plain ternary workload); along the row, each next block's
+    exponent moves by -1 or +1 with probability p_change / 2 each (a running
+    sum, clipped to [7, 11]); a 10-bit mantissa U{0..1023} per block; fp32
+    x ~ N(0,1).  The fp16 scale bits are (exponent << 10) | mantissa.
+    p_change = 0.075 leaves about 3 in 10^4 superblocks outside the 767 most
+    common patterns at K=5120, N=17280 (the post: about 1 in 10^4)."""
+    rng = np.random.default_rng(seed)
+    trits = rng.integers(-1, 2, (n, k), dtype=np.int8)
+    nb = k // 128
+    e0 = rng.integers(8, 11, n)
+    u = rng.random((n, max(nb - 1, 0)))
+    step = np.where(u < p_change / 2, -1, np.where(u < p_change, 1, 0))
+    e = np.concatenate([e0[:, None], e0[:, None] + np.cumsum(step, axis=1)], axis=1)
+    e = np.clip(e, 7, 11)
+    mant = rng.integers(0, 1024, (n, nb))
+    d_bits = ((e << 10) | mant).astype(np.uint16)
+    x = rng.standard_normal((cmax, k)).astype(np.float32)
     return TernaryProblem(n, k, trits, d_bits, x)
