@@ -445,6 +445,29 @@ def ternary_rows(g, torch, wq_inputs, dev, log):
             "Mrows_per_s": round(17280 * cc / (ms * 1e-3) / 1e6, 1)}
     rows["gemv_ternary"] = trow
     log("ternary:", json.dumps(trow))
+    # the same GEMV on PTQ1_1 superblocks (216 bytes per 1024 trits), with
+    # block scales that have the exponent statistics of trained weights
+    tc = wq_inputs.ternary_correlated_scales(5120, 17280, cmax=8)
+    blk = torch.empty((17280, 40, 28), dtype=torch.uint8, device=dev)
+    g.wq_pack_ptq1_0(torch.from_numpy(tc.trits).to(dev),
+                     torch.from_numpy(tc.d_bits).view(torch.int16).to(dev), blk)
+    sup, book, ei, ep = g.wq_ptq1_1_encode(blk.cpu().numpy())
+    sup_d = torch.from_numpy(sup).to(dev)
+    tabs = [torch.from_numpy(a).to(dev) for a in (book, ei, ep)]
+    nc1 = copies_for(sup_d.numel())
+    scs = [sup_d] + [sup_d.clone() for _ in range(nc1 - 1)]
+    xq1 = torch.empty((8, 160, 36), dtype=torch.uint8, device=dev)
+    g.wq_quantize_q8_1(torch.from_numpy(tc.x).to(dev), xq1)
+    srow = {"escaped_superblocks": int(len(ei))}
+    for cc in (1, 4, 8):
+        ms = timed(torch, lambda i: g.wq_gemv_ternary_ptq1_1(scs[i % nc1], *tabs, xq1[:cc], 5120, y[:cc]), 50)
+        srow[f"K5120_N17280_c{cc}"] = {
+            "us": round(ms * 1e3, 2), "weight_GBs": round(sup_d.numel() / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(sup_d.numel() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "Mrows_per_s": round(17280 * cc / (ms * 1e-3) / 1e6, 1)}
+    rows["gemv_ternary_ptq1_1"] = srow
+    log("ternary ptq1_1:", json.dumps(srow))
+    del scs, sup_d
     # 4096 activation columns: the int8 matrix-core path (2 int8 ops per MAC)
     gen = torch.Generator(device="cpu").manual_seed(0)
     mg = 4096

@@ -33,6 +33,8 @@ _SIGS = {
     "wq_pack_ptq1_0": ([_p, _p, _i64, _i64, _p, _p], _i),
     "wq_quantize_q8_1": ([_p, _i64, _i64, _p, _p], _i),
     "wq_gemv_ternary": ([_p, _p, _i64, _i64, _i64, _p, _p], _i),
+    "wq_ptq1_1_encode": ([_p, _i64, _i64, _p, _p, _p, _p, _i64, _p], _i),
+    "wq_gemv_ternary_ptq1_1": ([_p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _p], _i),
     # calibration kernels (include/wq_peaks.h)
     "wq_peak_read_sink_words": ([], _i64),
     "wq_peak_read": ([_p, _i64, _p, _i64, _p], _i),
@@ -233,6 +235,53 @@ def wq_gemv_ternary(w_blocks, x_q8, k, out, stream=None):
     d = st.device
     _check("wq_gemv_ternary",
            lib.wq_gemv_ternary(_ptr(w_blocks, d), _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
+
+
+def wq_ptq1_1_encode(blocks):
+    """PTQ1_0 blocks (host numpy uint8 [n][k/128][28]) -> PTQ1_1 superblocks
+    on the host: (superblocks uint8 [n][k/1024][216], codebook uint8 [767][8],
+    escape indices int32 [n_esc], escape patterns uint8 [n_esc][8])."""
+    import numpy as np
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    _require(b.ndim == 3 and b.shape[2] == 28, "blocks are [n][k/128][28]")
+    n, nb = b.shape[0], b.shape[1]
+    k = nb * 128
+    _require(nb % 8 == 0, "k is a multiple of 1024")
+    sup = np.empty((n, nb // 8, 216), dtype=np.uint8)
+    book = np.empty((767, 8), dtype=np.uint8)
+    n_esc = ctypes.c_int64(0)
+    cap = n * (nb // 8)
+    idx = np.empty(max(cap, 1), dtype=np.int32)
+    patt = np.empty((max(cap, 1), 8), dtype=np.uint8)
+    _check("wq_ptq1_1_encode",
+           lib.wq_ptq1_1_encode(b.ctypes.data_as(_p), n, k, sup.ctypes.data_as(_p),
+                                book.ctypes.data_as(_p), idx.ctypes.data_as(_p),
+                                patt.ctypes.data_as(_p), cap, ctypes.byref(n_esc)))
+    m = n_esc.value
+    return sup, book, idx[:m].copy(), patt[:m].copy()
+
+
+def wq_gemv_ternary_ptq1_1(superblocks, codebook, esc_idx, esc_patt, x_q8, k, out, stream=None):
+    """out fp32 [c][n] from PTQ1_1 superblocks [n][k/1024][216] (device), the
+    codebook [767][8] and escape table (device), and q8_1 x [c][k/32][36]."""
+    n = superblocks.shape[0]
+    c = x_q8.shape[0]
+    n_esc = esc_idx.numel()
+    _require(superblocks.dtype == torch.uint8 and codebook.dtype == torch.uint8 and
+             x_q8.dtype == torch.uint8 and esc_patt.dtype == torch.uint8, "byte tensors are uint8")
+    _require(esc_idx.dtype == torch.int32, "escape indices are int32")
+    _require(superblocks.numel() == n * (k // 1024) * 216, "superblocks [n][k/1024][216]")
+    _require(codebook.numel() == 767 * 8, "codebook [767][8]")
+    _require(esc_patt.numel() == n_esc * 8, "escape patterns [n_esc][8]")
+    _require(x_q8.numel() == c * (k // 32) * 36, "x_q8 [c][k/32][36]")
+    _require(out.dtype == torch.float32 and out.numel() == c * n, "out is fp32 [c][n]")
+    st = _stream(stream)
+    d = st.device
+    _check("wq_gemv_ternary_ptq1_1",
+           lib.wq_gemv_ternary_ptq1_1(_ptr(superblocks, d), _ptr(codebook, d),
+                                      _ptr(esc_idx, d) if n_esc else None,
+                                      _ptr(esc_patt, d) if n_esc else None, n_esc,
+                                      _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
 
 
 # ---- calibration kernels (include/wq_peaks.h): practical ceilings of the

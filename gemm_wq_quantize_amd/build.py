@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwq.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["capi.cpp", "quantize_pack.hip", "gemv_w4.hip", "gemm_w4a16.hip", "ternary.hip", "peaks.hip"]
+SOURCES = ["capi.cpp", "ptq1_1.cpp", "quantize_pack.hip", "gemv_w4.hip", "gemm_w4a16.hip", "ternary.hip",
+           "peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -186,4 +186,24 @@ int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int
   return hip_status(wq::launch_gemv_ternary(w_blocks, x_q8, n, k, c, out, as_stream(stream)));
 }
 
+int wq_gemv_ternary_ptq1_1(const uint8_t* superblocks, const uint8_t* codebook,
+                           const int32_t* esc_idx, const uint8_t* esc_patt, int64_t n_esc,
+                           const uint8_t* x_q8, int64_t n, int64_t k, int64_t c, float* out,
+                           void* stream) {
+  if (n < 0 || k < 0 || c < 0 || n_esc < 0) return WQ_EINVAL;
+  if (n == 0 || c == 0) return WQ_OK;
+  if (!superblocks || !codebook || !x_q8 || !out || (n_esc > 0 && (!esc_idx || !esc_patt)))
+    return WQ_EINVAL;
+  // superblocks of 8 blocks; x of one column must fit in LDS beside the tables
+  if (k == 0 || k % 1024 != 0 || k > 65536) return WQ_ESHAPE;
+  if (n_esc > 2048) return WQ_EUNSUPPORTED;  // escape table staged in LDS
+  if (n >= (int64_t(1) << 30) || mul_sat(mul_sat(n, k / 128), 28) >= (int64_t(1) << 31))
+    return WQ_ESHAPE;
+  if (!aligned(superblocks, 4) || !aligned(codebook, 4) || !aligned(x_q8, 4) || !aligned(out, 4) ||
+      (n_esc > 0 && (!aligned(esc_idx, 4) || !aligned(esc_patt, 4))))
+    return WQ_EALIGN;
+  return hip_status(wq::launch_gemv_ternary_sb(superblocks, codebook, esc_idx, esc_patt, n_esc, x_q8,
+                                               n, k, c, out, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -264,6 +264,7 @@ constexpr uint32_t T_OOB = 0x80000000u;
 // once start in 8 different bank quads.
 constexpr int TP_LPR = 8;     // lanes per row in the persistent ternary GEMV
 constexpr int TP_WAVES = 5;   // waves per SIMD the register budget is sized for
+constexpr int TP_WAVES_SB = 4;  // the same with PTQ1_1 superblocks (12 words per item)
 constexpr int LUT_COPIES = 16;
 constexpr int XB_WORDS = 36;  // words per padded 128-element x block
 
@@ -347,13 +348,12 @@ __device__ __forceinline__ void tern_decode(const uint32_t (&v)[7], const uint32
   }
 }
 
+// acc[col] += d_w * sum_s4 d_x * (sum u q - sum q) for one block's 128
+// digits dg against the staged activations of block bx of the row.
 template <int C>
-__device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_t* lt,
-                                           const uint32_t* xs, const int* xsum, const float* xd,
-                                           int bx, int bpr, int nsb, float (&acc)[C]) {
-  uint32_t dg[32];
-  tern_decode(v, lt, dg);
-  const float dw = f16_to_f32(v[6] >> 16);  // 0 for blocks past the end
+__device__ __forceinline__ void tern_products(const uint32_t (&dg)[32], float dw, const uint32_t* xs,
+                                              const int* xsum, const float* xd, int bx, int bpr,
+                                              int nsb, float (&acc)[C]) {
 #pragma unroll
   for (int col = 0; col < C; ++col) {
     const uint4* xv = reinterpret_cast<const uint4*>(xs + (col * bpr + bx) * XB_WORDS);
@@ -376,14 +376,127 @@ __device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_
   }
 }
 
+// One PTQ1_0 block (its 7 words in v) against the staged activations.
+template <int C>
+__device__ __forceinline__ void tern_block(const uint32_t (&v)[7], const uint32_t* lt,
+                                           const uint32_t* xs, const int* xsum, const float* xd,
+                                           int bx, int bpr, int nsb, float (&acc)[C]) {
+  uint32_t dg[32];
+  tern_decode(v, lt, dg);
+  tern_products<C>(dg, f16_to_f32(v[6] >> 16), xs, xsum, xd, bx, bpr, nsb, acc);  // d = 0 past the end
+}
+
+// ---- PTQ1_1 superblocks (Ternary post, section 2 struct ptq1_1; section
+// 3.1: sub-block sub = kbx & 7 of superblock kbx >> 3).  216 bytes: qs[192]
+// (the qs[24] of sub-blocks 0..7), qh[13] (the 64 tail trits, five per byte
+// in sub-block order, tail trit 8 sub + e at digit (8 sub + e) % 5 of byte
+// (8 sub + e) / 5; digit 4 of qh[12] is the free trit), an 80-bit
+// little-endian field of eight 10-bit mantissas (mantissa sub at bit 10 sub),
+// and the exponent byte.  Pattern index P = exponent byte + 256 * free digit:
+// P < 767 is a row of the 767 x 8 exponent codebook, P = 767 sends the
+// superblock to the escape table (ascending superblock indices row * K/1024 +
+// sb, eight exponents each).  d = (exponent << 10) | mantissa (sign +).
+constexpr int SB_BYTES = 216;
+constexpr int SB_CODEBOOK_ROWS = 767;
+constexpr int SB_ESC_MAX = 2048;  // escaped superblocks staged in LDS per call
+
+struct SbTables {
+  const uint8_t* codebook;  // [767][8] exponent fields
+  const int32_t* esc_idx;   // [n_esc] ascending superblock indices
+  const uint8_t* esc_patt;  // [n_esc][8] their exponent fields
+  int n_esc;
+};
+
+// LDS words the superblock tables take: codebook (767 x 8 bytes) + escape
+// indices + escape patterns
+__host__ __device__ constexpr int sb_lds_words(int n_esc) { return 1534 + n_esc + 2 * n_esc; }
+
+// Codebook and escape table into LDS (256 threads; one-time per workgroup).
+__device__ __forceinline__ void tern_stage_sb(uint32_t* dst, const SbTables& t) {
+  const int tid = threadIdx.x;
+  const uint32_t* cb = reinterpret_cast<const uint32_t*>(t.codebook);
+  for (int i = tid; i < 1534; i += 256) dst[i] = cb[i];
+  const int ne = t.n_esc;
+  for (int i = tid; i < ne; i += 256) dst[1534 + i] = (uint32_t)t.esc_idx[i];
+  const uint32_t* ep = reinterpret_cast<const uint32_t*>(t.esc_patt);
+  for (int i = tid; i < 2 * ne; i += 256) dst[1534 + ne + i] = ep[i];
+}
+
+// The 128 digits and the scale of sub-block sub (= this lane's block within
+// the superblock) from its 12 words: v[0..5] its qs bytes 24 sub .. 24 sub +
+// 23, v[6..11] the superblock's bytes 192..215.  gidx: the superblock's
+// index (the escape key); tbl: the staged tables (codebook bytes, then the
+// escape indices and patterns).
+__device__ __forceinline__ void tern_decode_sb(const uint32_t (&v)[12], const uint32_t* lt,
+                                               const uint32_t* tbl, int n_esc, int gidx, int sub,
+                                               uint32_t (&dg)[32], float& dw) {
+  // qs: exactly the PTQ1_0 sections
+  uint32_t v7[7] = {v[0], v[1], v[2], v[3], v[4], v[5], 0u};
+  tern_decode(v7, lt, dg);
+  // tail: the 8 digits from digit d0 of qh byte b0 on (b0 = 8 sub / 5,
+  // d0 = 8 sub % 5), out of the three bytes b0 .. b0 + 2
+  // (word selection by lane masks: a select chain on the array makes the
+  // compiler index a private copy of it in scratch memory)
+  const int b0 = (8 * sub) / 5, d0 = (8 * sub) % 5, w = b0 >> 2;
+  const uint32_t w0 = 0u - (uint32_t)(w == 0), w1 = 0u - (uint32_t)(w == 1), w2 = 0u - (uint32_t)(w == 2);
+  const uint32_t lo = (v[6] & w0) | (v[7] & w1) | (v[8] & w2);
+  const uint32_t hi = (v[7] & w0) | (v[8] & w1) | (v[9] & w2);
+  const uint32_t three = __builtin_amdgcn_alignbit(hi, lo, 8 * (b0 & 3));
+  const uint32_t l0 = lt[(three & 0xFF) * LUT_COPIES];
+  const uint32_t l1 = lt[((three >> 8) & 0xFF) * LUT_COPIES];
+  const uint32_t l2 = lt[((three >> 16) & 0xFF) * LUT_COPIES];
+  // the digit sequence of the three bytes, one digit per byte: table entry =
+  // digits 0..3 in bytes 0..3 (two bits each) and digit 4 in bits 4..5
+  const uint32_t s0 = l0 & 0x03030303u;
+  const uint32_t s1 = ((l0 >> 4) & 3u) | ((l1 & 0x00030303u) << 8);
+  const uint32_t s2 = ((l1 >> 24) & 3u) | (((l1 >> 4) & 3u) << 8) | ((l2 & 0x0303u) << 16);
+  // digits d0 .. d0 + 7 of the sequence s0 s1 s2 (v_alignbyte shifts by 0..3
+  // bytes, so d0 = 4 starts one word later)
+  const bool d4 = d0 == 4;
+  dg[30] = __builtin_amdgcn_alignbyte(d4 ? s2 : s1, d4 ? s1 : s0, d0 & 3);  // elements 120..123
+  dg[31] = d4 ? s2 : __builtin_amdgcn_alignbyte(s2, s1, d0 & 3);            // elements 124..127
+  // scale: pattern index from the exponent byte and the free trit
+  const uint32_t free = (lt[(v[9] & 0xFF) * LUT_COPIES] >> 4) & 3u;
+  const int pat = (int)((v[11] >> 24) | (free << 8));
+  uint32_t e;
+  if (pat < SB_CODEBOOK_ROWS) {
+    e = (tbl[pat * 2 + (sub >> 2)] >> (8 * (sub & 3))) & 0xFFu;
+  } else {  // escape: binary search of the superblock index (LDS only)
+    const uint32_t* idx = tbl + 1534;
+    int a = 0, z = n_esc;
+    while (a < z) {
+      const int m = (a + z) >> 1;
+      if ((int)idx[m] < gidx) a = m + 1;
+      else z = m;
+    }
+    a = min(a, max(n_esc - 1, 0));
+    e = n_esc > 0 ? (tbl[1534 + n_esc + 2 * a + (sub >> 2)] >> (8 * (sub & 3))) & 0xFFu : 0u;
+  }
+  // mantissa sub: bits 10 sub .. + 9 of the field at bytes 205..214
+  const uint32_t f0 = __builtin_amdgcn_alignbit(v[10], v[9], 8);   // field bits 0..31
+  const uint32_t f1 = __builtin_amdgcn_alignbit(v[11], v[10], 8);  // bits 32..63
+  const uint32_t f2 = v[11] >> 8;                                  // bits 64..87
+  const int mb = 10 * sub, mw = mb >> 5;
+  const uint32_t m0 = 0u - (uint32_t)(mw == 0), m1 = 0u - (uint32_t)(mw == 1), m2 = 0u - (uint32_t)(mw == 2);
+  const uint32_t mlo = (f0 & m0) | (f1 & m1) | (f2 & m2);
+  const uint32_t mhi = (f1 & m0) | (f2 & (m1 | m2));
+  const uint32_t m = __builtin_amdgcn_alignbit(mhi, mlo, mb & 31) & 0x3FFu;
+  dw = f16_to_f32((e << 10) | m);
+}
+
 // dynamic LDS: table [256][16], x [C][bpr][36 words], sum q [C][k/32], d [C][k/32]
 // LPR lanes per row (8 or 16): a wave holds 64 / LPR rows, a lane one block
 // of its row per item (an item = LPR consecutive blocks of each row).
-template <int C, int D, int LPR>
-__global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_persist(const uint32_t* __restrict__ w,
+// SB: the weights are PTQ1_1 superblocks (LPR = 8: an item is one superblock
+// of each row, lane sub its sub-block), with the codebook and the escape
+// table staged in LDS after the activations.
+template <int C, int D, int LPR, bool SB>
+__global__ __launch_bounds__(256, SB ? TP_WAVES_SB : TP_WAVES) void k_gemv_ternary_persist(const uint32_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
                                                               float* __restrict__ out, int n, int k,
-                                                              int c) {
+                                                              int c, SbTables sbt) {
+  static_assert(!SB || LPR == 8, "a superblock is 8 blocks");
+  constexpr int W = SB ? 12 : 7;                          // words a lane loads per item
   extern __shared__ uint32_t tsm[];
   const int nsb = k / 32;
   const int bpr = k / 128;                                // blocks per row
@@ -391,6 +504,7 @@ __global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_persist(const ui
   uint32_t* xs = tsm + 256 * LUT_COPIES;                  // [C][bpr][XB_WORDS]
   int* xsum = reinterpret_cast<int*>(xs + C * bpr * XB_WORDS);  // [C][nsb]
   float* xd = reinterpret_cast<float*>(xsum + C * nsb);   // [C][nsb]
+  uint32_t* tbl = reinterpret_cast<uint32_t*>(xd + C * nsb);  // superblock tables
 
   constexpr int RPW = 64 / LPR;  // rows per wave (one row group)
   const int tid = threadIdx.x, lane = tid & 63, sub = lane & (LPR - 1);
@@ -400,24 +514,37 @@ __global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_persist(const ui
   const int nrg = (n + RPW - 1) / RPW;
   const int nitems = (nrg > gw ? (nrg - gw + nw - 1) / nw : 0) * ntiles;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)w, 0, (int)((int64_t)n * bpr * PT_BYTES), 0x00020000);
+      (void*)w, 0, (int)((int64_t)n * bpr * (SB ? SB_BYTES / 8 : PT_BYTES)), 0x00020000);
 
   // ---- weight ring: item i = (row group gw + (i / ntiles) nw, tile i % ntiles)
-  uint32_t wd[D][7];
+  uint32_t wd[D][W];
   auto issue = [&](int slot, int i) {
     const int t = i % ntiles, rg = gw + (i / ntiles) * nw;
     const int row = rg * RPW + lane / LPR, blk = t * LPR + sub;
     const bool ok = i < nitems && row < n && blk < bpr;
-    const uint32_t o = ok ? (uint32_t)((row * bpr + blk) * PT_BYTES) : T_OOB;
+    if constexpr (SB) {
+      // this sub-block's qs words, then the superblock's last 24 bytes
+      const uint32_t o = ok ? (uint32_t)((row * ntiles + t) * SB_BYTES) : T_OOB;
 #pragma unroll
-    for (int q = 0; q < 7; ++q)
-      wd[slot][q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * q), 0, 0);
+      for (int q = 0; q < 6; ++q)
+        wd[slot][q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 24 * sub + 4 * q), 0, 0);
+#pragma unroll
+      for (int q = 0; q < 6; ++q)
+        wd[slot][6 + q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 192 + 4 * q), 0, 0);
+    } else {
+      const uint32_t o = ok ? (uint32_t)((row * bpr + blk) * PT_BYTES) : T_OOB;
+#pragma unroll
+      for (int q = 0; q < 7; ++q)
+        wd[slot][q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * q), 0, 0);
+    }
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
 
-  // ---- one-time staging: digit table and the activations
+  // ---- one-time staging: digit table and the activations (and the
+  // superblock tables)
   tern_stage<C>(lut, xs, xsum, xd, xq, bpr, nsb, c);
+  if constexpr (SB) tern_stage_sb(tbl, sbt);
   __syncthreads();
 
   float acc[C];
@@ -429,13 +556,22 @@ __global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_persist(const ui
   auto item = [&](const int i, const int slot) {
     const int t = i % ntiles;
     const int blk = t * LPR + sub;
-    uint32_t v[7];
+    uint32_t v[W];
 #pragma unroll
-    for (int q = 0; q < 7; ++q) v[q] = wd[slot][q];
+    for (int q = 0; q < W; ++q) v[q] = wd[slot][q];
     issue(slot, i + D);  // the slot is free once copied out
     if (i >= nitems) return;  // uniform; no load below
-    // blocks past the end loaded zeros (scale 0); x reads stay in the staged range
-    tern_block<C>(v, lut + (lane & (LUT_COPIES - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
+    if constexpr (SB) {
+      // (rows past n decode garbage that is never stored)
+      const int row = (gw + (i / ntiles) * nw) * RPW + lane / LPR;
+      uint32_t dg[32];
+      float dw;
+      tern_decode_sb(v, lut + (lane & (LUT_COPIES - 1)), tbl, sbt.n_esc, row * ntiles + t, sub, dg, dw);
+      tern_products<C>(dg, dw, xs, xsum, xd, blk, bpr, nsb, acc);
+    } else {
+      // blocks past the end loaded zeros (scale 0); x reads stay in the staged range
+      tern_block<C>(v, lut + (lane & (LUT_COPIES - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
+    }
     if (t == ntiles - 1) {  // uniform: the wave leaves its 8-row group
       const int row = (gw + (i / ntiles) * nw) * RPW + lane / LPR;
 #pragma unroll
@@ -472,12 +608,13 @@ __global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_persist(const ui
 // one workgroup (4 / S row groups per 256-lane workgroup, not persistent), so
 // S times more waves run, and the S partial sums of a row are added in LDS in
 // part order.
-template <int C, int D, int S>
-__global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_ksplit(const uint32_t* __restrict__ w,
+template <int C, int D, int S, bool SB>
+__global__ __launch_bounds__(256, SB ? TP_WAVES_SB : TP_WAVES) void k_gemv_ternary_ksplit(const uint32_t* __restrict__ w,
                                                              const uint8_t* __restrict__ xq,
                                                              float* __restrict__ out, int n, int k,
-                                                             int c) {
+                                                             int c, SbTables sbt) {
   constexpr int LPR = 8, RPW = 64 / LPR;
+  constexpr int W = SB ? 12 : 7;                          // words a lane loads per item
   extern __shared__ uint32_t tsm[];
   const int nsb = k / 32;
   const int bpr = k / 128;
@@ -486,6 +623,7 @@ __global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_ksplit(const uin
   int* xsum = reinterpret_cast<int*>(xs + C * bpr * XB_WORDS);  // [C][nsb]
   float* xd = reinterpret_cast<float*>(xsum + C * nsb);   // [C][nsb]
   float* psum = xd + C * nsb;                             // [4 waves][RPW rows][C]
+  uint32_t* tbl = reinterpret_cast<uint32_t*>(psum + 4 * RPW * C);  // superblock tables
 
   const int tid = threadIdx.x, lane = tid & 63, sub = lane & (LPR - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -497,35 +635,54 @@ __global__ __launch_bounds__(256, TP_WAVES) void k_gemv_ternary_ksplit(const uin
   const int t0 = part * tps;
   const int nitems = max(0, min(ntiles, t0 + tps) - t0);  // this wave's tiles
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)w, 0, (int)((int64_t)n * bpr * PT_BYTES), 0x00020000);
+      (void*)w, 0, (int)((int64_t)n * bpr * (SB ? SB_BYTES / 8 : PT_BYTES)), 0x00020000);
 
-  // weight ring: item i = tile t0 + i of the row group
-  uint32_t wd[D][7];
+  // weight ring: item i = tile t0 + i of the row group (with superblocks: its
+  // superblock t0 + i, this lane's sub-block sub)
+  uint32_t wd[D][W];
   auto issue = [&](int slot, int i) {
     const int blk = (t0 + i) * LPR + sub;
     const bool ok = i < nitems && row < n && blk < bpr;
-    const uint32_t o = ok ? (uint32_t)((row * bpr + blk) * PT_BYTES) : T_OOB;
+    if constexpr (SB) {
+      const uint32_t o = ok ? (uint32_t)((row * ntiles + t0 + i) * SB_BYTES) : T_OOB;
 #pragma unroll
-    for (int q = 0; q < 7; ++q)
-      wd[slot][q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * q), 0, 0);
+      for (int q = 0; q < 6; ++q)
+        wd[slot][q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 24 * sub + 4 * q), 0, 0);
+#pragma unroll
+      for (int q = 0; q < 6; ++q)
+        wd[slot][6 + q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 192 + 4 * q), 0, 0);
+    } else {
+      const uint32_t o = ok ? (uint32_t)((row * bpr + blk) * PT_BYTES) : T_OOB;
+#pragma unroll
+      for (int q = 0; q < 7; ++q)
+        wd[slot][q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * q), 0, 0);
+    }
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
 
   tern_stage<C>(lut, xs, xsum, xd, xq, bpr, nsb, c);
+  if constexpr (SB) tern_stage_sb(tbl, sbt);
   __syncthreads();
 
   float acc[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) acc[j] = 0.f;
   auto item = [&](const int i, const int slot) {
-    uint32_t v[7];
+    uint32_t v[W];
 #pragma unroll
-    for (int q = 0; q < 7; ++q) v[q] = wd[slot][q];
+    for (int q = 0; q < W; ++q) v[q] = wd[slot][q];
     issue(slot, i + D);       // the slot is free once copied out
     if (i >= nitems) return;  // uniform; no load below
     const int blk = (t0 + i) * LPR + sub;
-    tern_block<C>(v, lut + (lane & (LUT_COPIES - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
+    if constexpr (SB) {
+      uint32_t dg[32];
+      float dw;
+      tern_decode_sb(v, lut + (lane & (LUT_COPIES - 1)), tbl, sbt.n_esc, row * ntiles + t0 + i, sub, dg, dw);
+      tern_products<C>(dg, dw, xs, xsum, xd, blk, bpr, nsb, acc);
+    } else {
+      tern_block<C>(v, lut + (lane & (LUT_COPIES - 1)), xs, xsum, xd, blk < bpr ? blk : 0, bpr, nsb, acc);
+    }
   };
   for (int i = 0; i < nitems; i += D) {
 #pragma unroll
@@ -775,45 +932,46 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x
 constexpr int TP_D = 2;
 
 // K-split launch (S = 2) when x fits in LDS; returns hipErrorInvalidValue (no
-// launch) otherwise.
-template <int C>
+// launch) otherwise.  SB: PTQ1_1 superblocks with their tables.
+template <int C, bool SB>
 hipError_t launch_ternary_ksplit(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k,
-                                 int64_t c, float* out, hipStream_t s) {
+                                 int64_t c, float* out, const SbTables& sbt, hipStream_t s) {
   constexpr int S = 2;
   const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8 +
-                      4 * 8 * C * 4;
+                      4 * 8 * C * 4 + (SB ? sb_lds_words(sbt.n_esc) * 4 : 0);
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
   static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
-  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S>),
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S, SB>),
                                          lds_ok, 160 * 1024);
   if (e != hipSuccess) return e;
   const int64_t nrg = (n + 7) / 8;
   const int64_t grid = (nrg + (4 / S) - 1) / (4 / S);
-  hipLaunchKernelGGL((k_gemv_ternary_ksplit<C, TP_D, S>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
-                     wp, xq, out, (int)n, (int)k, (int)c);
+  hipLaunchKernelGGL((k_gemv_ternary_ksplit<C, TP_D, S, SB>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
+                     wp, xq, out, (int)n, (int)k, (int)c, sbt);
   return hipGetLastError();
 }
 
 // Persistent launch when x fits in LDS; returns hipErrorInvalidValue (no
 // launch) otherwise.
-template <int C>
+template <int C, bool SB>
 hipError_t launch_ternary_persist(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k,
-                                  int64_t c, float* out, hipStream_t s) {
-  const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8;
+                                  int64_t c, float* out, const SbTables& sbt, hipStream_t s) {
+  const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8 +
+                      (SB ? sb_lds_words(sbt.n_esc) * 4 : 0);
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
   static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
-  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR>),
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR, SB>),
                                          lds_ok, 160 * 1024);
   if (e != hipSuccess) return e;
   const int64_t nrg = (n + 64 / TP_LPR - 1) / (64 / TP_LPR);
   // workgroups resident at once: LDS and the waves per SIMD the register
   // budget allows
-  const int per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(TP_WAVES, (160 * 1024) / lds));
+  const int per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(SB ? TP_WAVES_SB : TP_WAVES, (160 * 1024) / lds));
   const int64_t grid = std::min<int64_t>((nrg + 3) / 4, (int64_t)device_cu_count() * per_cu);
-  hipLaunchKernelGGL((k_gemv_ternary_persist<C, TP_D, TP_LPR>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
-                     wp, xq, out, (int)n, (int)k, (int)c);
+  hipLaunchKernelGGL((k_gemv_ternary_persist<C, TP_D, TP_LPR, SB>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
+                     wp, xq, out, (int)n, (int)k, (int)c, sbt);
   return hipGetLastError();
 }
 
@@ -822,19 +980,18 @@ hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n,
                                  int64_t c, float* out, hipStream_t s) {
   const uint32_t* wp0 = reinterpret_cast<const uint32_t*>(w);
   {
-    // (a single column runs slightly faster on the tiled kernel below, whose
-    // per-tile staging is small at c = 1)
     // one column: the K-split kernel (wider splits spilled registers)
+    const SbTables none{};
     hipError_t e = hipErrorInvalidValue;
     if (c == 1) {
-      e = launch_ternary_ksplit<1>(wp0, xq, n, k, c, out, s);
+      e = launch_ternary_ksplit<1, false>(wp0, xq, n, k, c, out, none, s);
       if (e != hipErrorInvalidValue) return e;
     }
     switch (c) {
       case 1: break;
-      case 2: e = launch_ternary_persist<2>(wp0, xq, n, k, c, out, s); break;
-      case 3: case 4: e = launch_ternary_persist<4>(wp0, xq, n, k, c, out, s); break;
-      default: if (c <= 8) e = launch_ternary_persist<8>(wp0, xq, n, k, c, out, s); break;
+      case 2: e = launch_ternary_persist<2, false>(wp0, xq, n, k, c, out, none, s); break;
+      case 3: case 4: e = launch_ternary_persist<4, false>(wp0, xq, n, k, c, out, none, s); break;
+      default: if (c <= 8) e = launch_ternary_persist<8, false>(wp0, xq, n, k, c, out, none, s); break;
     }
     if (e != hipErrorInvalidValue) return e;
   }
@@ -868,6 +1025,36 @@ hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, i
     const hipError_t e = launch_ternary_narrow(w, xq + c0 * (k / 32) * Q8_BYTES, n, k,
                                                std::min<int64_t>(16, c - c0), out + c0 * n, s);
     if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// PTQ1_1 superblocks: passes of at most 8 columns on the kernels that keep
+// x in LDS (the widest pass that fits); hipErrorInvalidValue when even one
+// column does not fit (the entry point bounds k so that it does).
+hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, const int32_t* esc_idx,
+                                  const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq,
+                                  int64_t n, int64_t k, int64_t c, float* out, hipStream_t s) {
+  const uint32_t* wp = reinterpret_cast<const uint32_t*>(w);
+  const SbTables t{codebook, esc_idx, esc_patt, (int)n_esc};
+  for (int64_t c0 = 0; c0 < c; ) {
+    const int64_t left = c - c0;
+    const uint8_t* xp = xq + c0 * (k / 32) * Q8_BYTES;
+    float* op = out + c0 * n;
+    hipError_t e = hipErrorInvalidValue;
+    int64_t done = 0;
+    if (left == 1) {
+      e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, s);
+      done = 1;
+    } else {
+      // widest pass first; a pass that does not fit its x in LDS launches nothing
+      if (left >= 5) { e = launch_ternary_persist<8, true>(wp, xp, n, k, std::min<int64_t>(8, left), op, t, s); done = std::min<int64_t>(8, left); }
+      if (e == hipErrorInvalidValue && left >= 3) { e = launch_ternary_persist<4, true>(wp, xp, n, k, std::min<int64_t>(4, left), op, t, s); done = std::min<int64_t>(4, left); }
+      if (e == hipErrorInvalidValue) { e = launch_ternary_persist<2, true>(wp, xp, n, k, 2, op, t, s); done = 2; }
+      if (e == hipErrorInvalidValue) { e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, s); done = 1; }
+    }
+    if (e != hipSuccess) return e;
+    c0 += done;
   }
   return hipSuccess;
 }

@@ -94,5 +94,8 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x
                                 hipStream_t s);
 hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s);
+hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, const int32_t* esc_idx,
+                                  const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq,
+                                  int64_t n, int64_t k, int64_t c, float* out, hipStream_t s);
 
 }  // namespace wq

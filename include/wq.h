@@ -215,6 +215,65 @@ int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* 
 int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k,
                     int64_t c, float* out, void* stream);
 
+/*
+ * PTQ1_1 superblocks (Ternary post [2 weight compression], struct ptq1_1;
+ * [3.1 data format], sb = kbx >> 3, sub = kbx & 7): eight consecutive
+ * PTQ1_0 blocks of a row in 216 bytes, 1/28 fewer than 8 x 28.  The post
+ * fixes the sizes and the scheme, not the bit positions; this library's
+ * layout:
+ *   bytes   0..191  the qs[24] of sub-blocks 0..7, unchanged
+ *   bytes 192..204  qh[13]: tail trit t = 8 sub + e (element 120 + e of
+ *                   sub-block sub, stored as u = trit + 1) is base-3 digit
+ *                   t % 5 of qh[t / 5] (digit 0 least significant); digit 4
+ *                   of qh[12] is the free trit
+ *   bytes 205..214  eight 10-bit mantissas of d, an 80-bit little-endian
+ *                   field, mantissa sub at bit 10 sub
+ *   byte  215       exponent byte
+ *  Pattern index P = exponent byte + 256 * free digit (768 values).  P < 767
+ *  selects row P of a 767 x 8 codebook of fp16 exponent fields; P = 767
+ *  means the superblock's exponents are in the escape table (its index
+ *  row * k/1024 + sb, in ascending order, and 8 exponent fields).  The sign
+ *  of d is not stored (always +): d = (exponent << 10) | mantissa.
+ */
+
+/*
+ * wq_ptq1_1_encode -- PTQ1_0 blocks to PTQ1_1 superblocks (HOST pointers;
+ * compression is an offline weight-preparation step and runs on the CPU).
+ *   blocks       host [n][k/128][28] PTQ1_0 blocks; every d must be >= +0.
+ *   superblocks  host [n][k/1024][216] out.
+ *   codebook     host [767][8] out: the tensor's most frequent exponent
+ *                patterns by decreasing count (ties by increasing pattern,
+ *                exponents compared in sub-block order); unused rows zero.
+ *   esc_idx      host int32 [esc_cap] out, ascending superblock indices.
+ *   esc_patt     host [esc_cap][8] out, their exponent fields.
+ *   n_esc        out: the number of escaped superblocks (also when it
+ *                exceeds esc_cap, which returns WQ_ESHAPE).
+ * Requires k % 1024 == 0 and n * k / 1024 < 2^31; a negative d is
+ * WQ_EINVAL.
+ */
+int wq_ptq1_1_encode(const uint8_t* blocks, int64_t n, int64_t k, uint8_t* superblocks,
+                     uint8_t* codebook, int32_t* esc_idx, uint8_t* esc_patt, int64_t esc_cap,
+                     int64_t* n_esc);
+
+/*
+ * wq_gemv_ternary_ptq1_1 -- wq_gemv_ternary on PTQ1_1 superblocks: each
+ * sub-block decodes to the PTQ1_0 block it was made from (qs, its 8 tail
+ * trits, d from the codebook or escape exponent and its mantissa) inside
+ * the kernel, then the same exact integer sub-block sums and scaling
+ * (Ternary post [3.1]: "the same as the PTQ1_0 format").
+ *   superblocks  [n][k/1024][216] (device).
+ *   codebook     [767][8] (device), esc_idx int32 [n_esc], esc_patt
+ *                [n_esc][8] (device), as wq_ptq1_1_encode writes them.
+ *   x_q8         [c][k/32] block_q8_1; out [c][n] float32.
+ * Requires k % 1024 == 0 and k <= 65536 (x of a column and the tables are
+ * staged in LDS), n_esc <= 2048 (else WQ_EUNSUPPORTED), all pointers 4-byte
+ * aligned.  Any c >= 1 (passes of at most 8 columns).
+ */
+int wq_gemv_ternary_ptq1_1(const uint8_t* superblocks, const uint8_t* codebook,
+                           const int32_t* esc_idx, const uint8_t* esc_patt, int64_t n_esc,
+                           const uint8_t* x_q8, int64_t n, int64_t k, int64_t c, float* out,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,3 +132,20 @@ def test_calibration_kernels_validate_without_gpu(lib):
         assert fn(4, 0, FAKE, 1024, None) == g.WQ_ESHAPE
         assert fn(4, 10, FAKE, 1023, None) == g.WQ_ESHAPE
         assert fn((1 << 20) + 1, 10, FAKE, 1 << 40, None) == g.WQ_ESHAPE
+
+
+def test_ptq1_1_validation_without_gpu(lib):
+    import gemm_wq_quantize_amd as g
+    n_esc = ctypes.c_int64(0)
+    # the host encoder: shape and argument errors
+    assert lib.wq_ptq1_1_encode(FAKE, 4, 512, FAKE, FAKE, None, None, 0, None) == g.WQ_EINVAL
+    assert lib.wq_ptq1_1_encode(FAKE, -1, 1024, FAKE, FAKE, None, None, 0, ctypes.byref(n_esc)) == g.WQ_EINVAL
+    # the GEMV: k a multiple of 1024, at most 65536, at most 2048 escapes
+    args = lambda k, ne, c=1: (FAKE, FAKE, FAKE, FAKE, ne, FAKE, 8, k, c, FAKE, None)
+    assert lib.wq_gemv_ternary_ptq1_1(*args(512, 0)) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary_ptq1_1(*args(65536 + 1024, 0)) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary_ptq1_1(*args(1024, 2049)) == g.WQ_EUNSUPPORTED
+    assert lib.wq_gemv_ternary_ptq1_1(*args(1024, -1)) == g.WQ_EINVAL
+    assert lib.wq_gemv_ternary_ptq1_1(FAKE, FAKE, None, None, 3, FAKE, 8, 1024, 1, FAKE, None) == g.WQ_EINVAL
+    assert lib.wq_gemv_ternary_ptq1_1(ODD, FAKE, FAKE, FAKE, 0, FAKE, 8, 1024, 1, FAKE, None) == g.WQ_EALIGN
+    assert lib.wq_gemv_ternary_ptq1_1(*args(1024, 0, c=0)) == 0
