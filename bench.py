@@ -31,7 +31,6 @@ METRIC = "W4 GEMV weight GB/s (% of HBM peak); W4A16 GEMM TFLOP/s (% of MFMA pea
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
-FP32_VALU_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
 SETTLE_S = 0.4              # seconds of step replays before the warm-up steps
 
@@ -46,17 +45,21 @@ def sha_of(path):
 
 
 def read_traffic(kernel_src):
-    """HBM bytes per launch from the committed PMC summary, if it was taken on
-    the current kernel source (else None)."""
+    """Memory bytes per launch from the committed PMC summary, if it was taken
+    on the current kernel source (else None): FETCH_SIZE + WRITE_SIZE, and the
+    L2's DRAM-side request counters, each scaled by a plain copy."""
     path = os.path.join(ROOT, "profiles", "gemv_w4_decode_traffic.md")
     if not os.path.exists(path):
-        return None
+        return None, None
     text = open(path).read()
     m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_val or m_sha.group(1) != sha_of(kernel_src):
-        return None
-    return float(m_val.group(1))
+    if not m_sha or m_sha.group(1) != sha_of(kernel_src):
+        return None, None
+    vals = []
+    for key in ("hbm_bytes_per_launch", "dram_bytes_per_launch"):
+        m = re.search(key + r":\s*([0-9.eE+]+)", text)
+        vals.append(float(m.group(1)) if m else None)
+    return tuple(vals)
 
 
 def copies_for(nbytes, minimum=2):
@@ -218,7 +221,7 @@ def main():
             "alg_GBs": round(alg / (d * 1e-3) / 1e9, 1),
             "frac_hbm": round(alg / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "Mrows_per_s": round(s["n"] * c / (d * 1e-3) / 1e6, 1)}
-    traffic = read_traffic(os.path.join(ROOT, "gemm_wq_quantize_amd", "csrc", "gemv_w4.hip"))
+    traffic, traffic_dram = read_traffic(os.path.join(ROOT, "gemm_wq_quantize_amd", "csrc", "gemv_w4.hip"))
     log("per launch:", json.dumps(per_call))
     # roofline of the kernel: algorithmic bytes of one launch over its average
     # duration, both averaged over the six configurations of a step
@@ -272,12 +275,13 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gemv_w4",
+            "kernel": "k_gemv_w4_persist (c=1), k_gemv_w4_quad (c=2,4)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_dram_requests": traffic_dram,
             "alg_bytes_per_launch": round(alg_step / n_launch),
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
             "graph_replay_ms_per_step": round(graph_ms_per_step, 5),
@@ -382,11 +386,15 @@ def small_batch_rows(g, torch, wq_inputs, dev, log):
         for c in (8, 16, 32):
             ms = timed(torch, lambda i: g.wq_gemv_w4(cps[i % nc2][0], 1, cps[i % nc2][1], None, 8.0,
                                                       k, 128, x[:c], out[:c]), 50)
+            # the products run on the matrix cores; the weight stream (plus x
+            # and out) against HBM is the bound
             flops = 2.0 * n * k * c
+            alg = wb + 2 * k * c + 2 * n * c
             srow[f"K{k}_N{n}_c{c}"] = {
                 "us": round(ms * 1e3, 2), "weight_GBs": round(wb / (ms * 1e-3) / 1e9, 1),
+                "alg_GBs": round(alg / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
-                "frac_valu_fp32": round(flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),
                 "Mrows_per_s": round(n * c / (ms * 1e-3) / 1e6, 1)}
         del ws, cps
         torch.cuda.empty_cache()

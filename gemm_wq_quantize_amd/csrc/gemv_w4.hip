@@ -716,17 +716,21 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
   }
 }
 
-// Decode kernel with activations broadcast inside lane quads (bf16 x, c <= 4,
-// all of x in LDS).
+// Decode kernel on lane quads (bf16 x, c <= 4, all of x in LDS), the
+// products on the matrix cores.
 //
 // Lane l of a wave is (q, r) = (l / 4, l % 4): it owns output row r of the
 // wave's current row-quad and chunk q (32 k) of the current item of 16
-// chunks (512 k), one 16-byte load of its row per item.  The four lanes of
-// a quad sit on four rows at the same k, so they need the same activations:
-// lane r of the quad reads dwords 4r .. 4r + 3 of the chunk's x (16 bytes)
-// from LDS, and each v_dot2c takes x dword e from lane e / 4 of the quad
-// through a DPP quad_perm broadcast on its first operand.  Each x byte read
-// from LDS thus feeds four rows, with no per-row copies in registers.
+// chunks (512 k), one 16-byte load of its row per item, so each load
+// instruction reads 256 contiguous bytes of each of four rows.  Quad q is
+// block q of v_mfma_f32_4x4x4_16b_bf16 (16 independent 4 x 4 x 4 products
+// per instruction): the B operand of lane (q, r) is four consecutive k of
+// its row (bf16 128 + code, unpacked as in the other kernels), the A
+// operand is the same four k of activation column r (columns past c repeat
+// the last one; their results are never stored), and element i of the
+// result is column i of row r.  Eight instructions cover the chunk,
+// accumulating onto its zero-point fold term -(128 + z) * sum x; the VALU
+// is left with the unpacking and one scale FMA per column.
 //
 // One workgroup of 1024 lanes per CU owns a balanced contiguous block of
 // rows (+-1); its items (row-quad, 512-k slice) in row-quad-major order are
@@ -741,82 +745,6 @@ constexpr int QK_CH = 16;             // chunks per item: one per quad
 constexpr int QK_NT = 1024;           // lanes per workgroup (one per CU)
 constexpr int QK_NW = QK_NT / 64;     // waves per workgroup
 constexpr int QK_XP = 9;              // 16-byte x pieces a lane stages (C * nchp * 4 <= QK_XP * QK_NT)
-
-// chain{0,1} += 16 products of one 32-k chunk (two columns): pair e of the
-// lane's weights times x dword e, taken by DPP from component e % 4 of quad
-// lane e / 4.  The compiler cannot see inside the asm, so the block keeps its
-// own wait states: two before the first DPP read (after a VALU write of its
-// source) and three after the last dot product (before another VALU
-// instruction may read its result).
-__device__ __forceinline__ void qdot2(float& a0, float& a1, const uint4& x0, const uint4& x1,
-                                      const uint32_t (&w)[16]) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %2, %10 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %6, %10 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %3, %11 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %7, %11 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %4, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %8, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %5, %13 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %9, %13 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %2, %14 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %6, %14 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %3, %15 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %7, %15 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %4, %16 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %8, %16 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %5, %17 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %9, %17 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %2, %18 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %6, %18 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %3, %19 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %7, %19 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %4, %20 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %8, %20 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %5, %21 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %9, %21 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %2, %22 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %6, %22 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %3, %23 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %7, %23 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %4, %24 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %8, %24 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %5, %25 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %1, %9, %25 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 2"
-      : "+v"(a0), "+v"(a1)
-      : "v"(x0.x), "v"(x0.y), "v"(x0.z), "v"(x0.w), "v"(x1.x), "v"(x1.y), "v"(x1.z), "v"(x1.w),
-        "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]),
-        "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]));
-}
-
-// chain += 16 products of one 32-k chunk (one column)
-__device__ __forceinline__ void qdot1(float& a0, const uint4& x0, const uint32_t (&w)[16]) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %1, %5 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %2, %6 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %3, %7 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %4, %8 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %1, %9 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %2, %10 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %3, %11 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %4, %12 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %1, %13 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %2, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %3, %15 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %4, %16 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %1, %17 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %2, %18 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %3, %19 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %0, %4, %20 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 2"
-      : "+v"(a0)
-      : "v"(x0.x), "v"(x0.y), "v"(x0.z), "v"(x0.w),
-        "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]),
-        "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]));
-}
 
 // Sum over the 16 quads of a wave (lanes with the same l % 4), fixed order:
 // the four quads of each DPP row by rotation, then the four rows.
@@ -835,9 +763,12 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
   const int nkit = (nchunks + QK_CH - 1) / QK_CH;                  // items per row-quad
   const int nchp = nkit * QK_CH;                                     // chunks per column in LDS
   const int ngroups = p.gshift < 0 ? 1 : (nchunks >> p.gshift);
-  uint4* xs = smem;                                                  // [C][nchp][4] x pieces
-  float* zs = reinterpret_cast<float*>(xs + C * nchp * 4);          // [C][nchp] chunk terms
-  float* slots = zs + C * nchp;                                      // [NW][spw][4][C]
+  // x pieces [nchp][C][4] with one spare piece per chunk (bank spread),
+  // chunk terms [nchp][4]
+  constexpr int XPC = 4 * C + 1;                                     // pieces per chunk
+  uint4* xs = smem;
+  float* zs = reinterpret_cast<float*>(xs + nchp * XPC);
+  float* slots = zs + 4 * nchp;                                      // [NW][spw][4][C]
   int* wtab = reinterpret_cast<int*>(slots + QK_NW * spw * 4 * C);  // [NW][3]: i0, i1, rq_first
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -901,8 +832,8 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
 
   // x staging loads go out before the weight prologue (loads complete in
   // issue order, so waiting for x does not wait for the weights).  A lane
-  // stages 16-byte pieces u of the [C][nchp][4] array, u = tid + i * NT
-  // rotated by a per-workgroup offset: every CU reads the same x, and in the
+  // stages 16-byte pieces u = (column, chunk, piece) in [C][nchp][4] order,
+  // u = tid + i * NT rotated by a per-workgroup offset: every CU reads the same x, and in the
   // same order they would all ask the same L2 channel at once.  The four
   // pieces of a chunk stay on four consecutive lanes (the offset is a
   // multiple of 4).
@@ -942,8 +873,9 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
     sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0xB1, 0xF, 0xF, false));  // quad xor 1
     sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0x4E, 0xF, 0xF, false));  // quad xor 2
     if (tid + i * QK_NT < npieces) {
-      xs[u] = v;
-      if ((u & 3) == 0) zs[u >> 2] = sx * zfold;
+      const int col = u / (nchp * 4), ch = (u >> 2) - col * nchp;
+      xs[ch * XPC + col * 4 + (u & 3)] = v;
+      if ((u & 3) == 0) zs[ch * 4 + col] = sx * zfold;
     }
   }
   __syncthreads();
@@ -1000,18 +932,21 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
         if (HZ) zb = 128.f + __uint_as_float(zv[d]);
       }
       issue(d);  // the ring slot is free once unpacked
-      float ch[C];
-      uint4 xv[C];
+      // A operand: column min(r, C - 1) of this lane's chunk (rows of the
+      // block past c are never stored); C operand: the chunk's fold terms
       const int xo = ckit * QK_CH + q;  // chunk of this lane, < nchp
+      const uint4* xp = xs + xo * XPC + min(r, C - 1) * 4;
+      const uint4 xq[4] = {xp[0], xp[1], xp[2], xp[3]};
+      floatx4 ch = *reinterpret_cast<const floatx4*>(zs + xo * 4);
+      if (HZ) ch = -zb * ch;
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        xv[j] = xs[(j * nchp + xo) * 4 + r];
-        const float z = zs[j * nchp + xo];
-        ch[j] = HZ ? -zb * z : z;
+      for (int st = 0; st < 8; ++st) {  // k 4 st .. 4 st + 3 of the chunk
+        const uint4 xw = xq[st >> 1];
+        const uint2 xa = (st & 1) ? make_uint2(xw.z, xw.w) : make_uint2(xw.x, xw.y);
+        const uint2 wb = make_uint2(wp[2 * st], wp[2 * st + 1]);
+        ch = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4, xa), __builtin_bit_cast(bf16x4, wb),
+                                                  ch, 0, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j + 1 < C; j += 2) qdot2(ch[j], ch[j + 1], xv[j], xv[j + 1], wp);
-      if constexpr (C % 2 == 1) qdot1(ch[C - 1], xv[C - 1], wp);
 #pragma unroll
       for (int j = 0; j < C; ++j) acc[j] = fmaf(sc, ch[j], acc[j]);
       if (valid && ++ckit == nkit) {
@@ -1040,6 +975,229 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
       if (e > a && a < ihi && e > ilo) v += slots[((h * spw + (rq - wtab[h * 3 + 2])) * 4 + rr) * C + col];
     }
     const int64_t row = (int64_t)r0 + rq * 4 + rr;
+    if (p.out_bf16)
+      reinterpret_cast<uint16_t*>(p.out)[col * p.n + row] = (uint16_t)f32_to_bf16_rne(v);
+    else
+      reinterpret_cast<float*>(p.out)[col * p.n + row] = v;
+  }
+}
+
+// ---------------------------------------------------------------- MFMA GEMV
+// bf16 activations, 2..32 columns: the products run on the matrix cores
+// (v_mfma_f32_16x16x32_bf16) instead of v_dot2, which leaves the VALU only
+// the unpacking and the scaling.  x is the 16 x 32 A operand (one operand
+// row per activation column; columns at or past c are zero), the weights of
+// 16 output rows, unpacked to bf16 (128 + q) as in the other kernels, the
+// 32 x 16 B operand.
+//
+// An item is one tile of 16 rows x 128 k (inside one scale group: groups of
+// 128 k or more, or one per row).  Lane l (row n = l % 16, part g = l / 16)
+// loads the 16 bytes of row n at k0 + 32 g .. k0 + 32 g + 31 and the same
+// 32 k of x for column l % 16; MFMA m (m = 0..3) takes word m of each, so
+// the k slots lane l brings to MFMA m are k0 + 32 g + 8 m + 0..7 on both
+// operands and the instruction pairs equal k whatever its slot order.
+// Result element i of lane l is column 4 g + i of row n (CB blocks of 16
+// columns), so the row's scale is one value per lane.  The zero-point fold
+// -(128 + z) sum x of a k group comes from a second chain with B = 1.
+//
+// One workgroup (1024 lanes; 512 with two column blocks, whose x operands
+// take twice the registers) covers up to NRT row tiles for all of k, items
+// in (k group, row tile) order split evenly over its waves: a wave walks a
+// contiguous run of k groups and, for each, all the tiles, so the x operand
+// (loaded from L2 one k group ahead, no staging in LDS) serves every tile.
+// Each wave keeps one accumulator per tile; the partials are parked in LDS
+// and added in wave order.
+template <int CB, int NRT, int NT, int LAYOUT, int D, bool HZ, bool SBF>
+__global__ __launch_bounds__(NT) void k_gemv_w4_mfma(KArgs p, int rows_per_wg) {
+  constexpr int NW = NT / 64;
+  extern __shared__ uint4 smem[];
+  float* slots = reinterpret_cast<float*>(smem);  // [NW][NRT][16 CB columns][16 rows]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 15, g = lane >> 4;
+  const int k32 = (int)p.k, c = (int)p.c;
+  const int nkg = (k32 + 127) / 128;
+  const int ngroups = p.gshift < 0 ? 1 : ((k32 / 32) >> p.gshift);
+  // this workgroup's rows: rows_per_wg each, the last ones fewer (n < 2^31
+  // and rows_per_wg <= 16 NRT are checked by the launcher)
+  const int r0 = (int)blockIdx.x * rows_per_wg;
+  const int count = min(rows_per_wg, (int)p.n - r0);
+  const int nrt = (count + 15) / 16;
+  const int items = nrt * nkg;
+  const int i0 = wave * items / NW, i1 = (wave + 1) * items / NW;
+  const int kg_last = (i1 - 1) / max(nrt, 1);  // last k group of this wave
+
+  const int rowbytes = k32 / 2;
+  constexpr int ESZ = SBF ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.packed + (int64_t)r0 * rowbytes), 0, count * rowbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)p.scales + (int64_t)r0 * ngroups * ESZ), 0, count * ngroups * ESZ, 0x00020000);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)(HZ ? p.zeros : p.scales) + (int64_t)r0 * ngroups * ESZ), 0,
+      HZ ? count * ngroups * ESZ : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, c * k32 * 2, 0x00020000);
+
+  // x operand of k group kg for this lane (columns cb 16 + nl); only the
+  // lanes of real columns load, the others hold zeros
+  auto load_x = [&](uint4 (&xv)[CB][4], int kg) {
+    const int kk = kg * 128 + 32 * g;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) xv[cb][m] = make_uint4(0, 0, 0, 0);
+      const int col = cb * 16 + nl;
+      if (col < c && kk < k32) {
+        const int xo = (col * k32 + kk) * 2;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          xv[cb][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * m, 0, 0));
+      }
+    }
+  };
+
+  // weight ring: issue position (k group, row tile), items left to issue
+  int ikg = i0 / max(nrt, 1), irt = i0 - ikg * nrt, left = i1 - i0;
+  uint4 wv[D];
+  uint32_t sv[D], zv[D];
+  auto issue = [&](const int slot) {
+    // rows past the workgroup's read zeros (descriptor); k past the end is
+    // masked per lane, but the scale is the row's for every lane of a live
+    // item (each result element sums all 128 k of its row)
+    const int kk = ikg * 128 + 32 * g, row = irt * 16 + nl;
+    const bool live = left > 0, ok = live && kk < k32;
+    const int gi = p.gshift < 0 ? 0 : ((ikg * 4) >> p.gshift);
+    const uint32_t wo = ok ? (uint32_t)(row * rowbytes + kk / 2) : OOB;
+    const uint32_t so = live ? (uint32_t)((row * ngroups + gi) * ESZ) : OOB;
+    wv[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wo, 0, 0));
+    if (SBF) {
+      sv[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)so, 0, 0);
+      if (HZ) zv[slot] = __builtin_amdgcn_raw_buffer_load_b16(zrs, (int)so, 0, 0);
+    } else {
+      sv[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)so, 0, 0);
+      if (HZ) zv[slot] = __builtin_amdgcn_raw_buffer_load_b32(zrs, (int)so, 0, 0);
+    }
+    --left;
+    if (++irt == nrt) {
+      irt = 0;
+      ++ikg;
+    }
+  };
+
+  int ckg = i0 / max(nrt, 1), crt = i0 - ckg * nrt;  // consume position
+  uint4 xc[CB][4], xn[CB][4];
+  load_x(xc, ckg);
+  if (ckg + 1 <= kg_last) load_x(xn, ckg + 1);
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d);
+
+  const uint32_t magic_v = vconst(0x43004300u);
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const float zconst = 128.f + p.zero_const;
+  floatx4 acc[NRT][CB], sx[CB];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[t][cb] = zero4;
+  // sum of x over the k group, per column, in the result layout
+  auto xsum = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      floatx4 v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xc[cb][0]), ones, zero4, 0, 0, 0);
+#pragma unroll
+      for (int m = 1; m < 4; ++m)
+        v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xc[cb][m]), ones, v, 0, 0, 0);
+      sx[cb] = v;
+    }
+  };
+  xsum();
+
+  const int nsteps = i1 - i0;
+  for (int base = 0; base < nsteps; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const bool valid = base + d < nsteps;
+      bf16x8 wb[4];
+      {
+        const uint32_t w4[4] = {wv[d].x, wv[d].y, wv[d].z, wv[d].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          uint4 u;
+          if (LAYOUT == 1) {
+            u.x = pair_bf16_fast(w4[m], 0, magic_v);
+            u.y = pair_bf16_fast(w4[m], 1, magic_v);
+            u.z = pair_bf16_fast(w4[m], 2, magic_v);
+            u.w = pair_bf16_fast(w4[m], 3, magic_v);
+          } else {
+            u.x = pair_bf16<LAYOUT>(w4[m], 0);
+            u.y = pair_bf16<LAYOUT>(w4[m], 1);
+            u.z = pair_bf16<LAYOUT>(w4[m], 2);
+            u.w = pair_bf16<LAYOUT>(w4[m], 3);
+          }
+          wb[m] = __builtin_bit_cast(bf16x8, u);
+        }
+      }
+      float sc, zb = zconst;
+      if constexpr (SBF) {
+        sc = bf16_to_f32(sv[d]);
+        if (HZ) zb = 128.f + bf16_to_f32(zv[d]);
+      } else {
+        sc = __uint_as_float(sv[d]);
+        if (HZ) zb = 128.f + __uint_as_float(zv[d]);
+      }
+      issue(d);  // the ring slot is free once copied out
+      if (valid) {  // uniform
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          floatx4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xc[cb][0]), wb[0], zero4, 0, 0, 0);
+#pragma unroll
+          for (int m = 1; m < 4; ++m)
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xc[cb][m]), wb[m], t, 0, 0, 0);
+          floatx4 u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) u[i] = sc * fmaf(-zb, sx[cb][i], t[i]);
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+            if (rt == crt) acc[rt][cb] += u;  // uniform
+        }
+        if (++crt == nrt) {  // next k group: its x was loaded one group ahead
+          crt = 0;
+          ++ckg;
+          if (ckg <= kg_last) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+              for (int m = 0; m < 4; ++m) xc[cb][m] = xn[cb][m];
+            if (ckg + 1 <= kg_last) load_x(xn, ckg + 1);
+            xsum();
+          }
+        }
+      }
+    }
+  }
+
+  // park this wave's partial of every tile, then add them in wave order
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    if (rt >= nrt) break;  // uniform
+    float* dst = slots + (wave * NRT + rt) * 256 * CB;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(cb * 16 + 4 * g + i) * 16 + nl] = acc[rt][cb][i];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nrt * 16 * c; idx += NT) {
+    const int rt = idx / (16 * c);
+    const int rc = idx - rt * 16 * c;
+    const int col = rc >> 4, rr = rc & 15;
+    if (rt * 16 + rr >= count) continue;
+    float v = 0.f;
+    for (int h = 0; h < NW; ++h) v += slots[((h * NRT + rt) * 16 * CB + col) * 16 + rr];
+    const int64_t row = (int64_t)r0 + rt * 16 + rr;
     if (p.out_bf16)
       reinterpret_cast<uint16_t*>(p.out)[col * p.n + row] = (uint16_t)f32_to_bf16_rne(v);
     else
@@ -1448,10 +1606,7 @@ int quad_slots(int64_t n, int grid, int nkit) {
 // Returns hipErrorInvalidValue (without launching) when x does not fit in LDS.
 template <int C>
 hipError_t launch_quad(const KArgs& ka, int layout, hipStream_t s) {
-  // items in flight per lane: two at c = 2 (one or three were 2-4% slower),
-  // one at c = 3 and 4 (4-5% faster than two there: the loop is bound by
-  // the VALU, and a shorter ring leaves the other waves' loads the HBM)
-  constexpr int D = C <= 2 ? 2 : 1;
+  constexpr int D = 2;  // items in flight per lane (one was 3-6% slower)
   if (ka.n >= (int64_t(1) << 31) || ka.k >= (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int64_t nchunks = ka.k / 32;
   const int nkit = (int)((nchunks + QK_CH - 1) / QK_CH);
@@ -1465,7 +1620,8 @@ hipError_t launch_quad(const KArgs& ka, int layout, hipStream_t s) {
     return hipErrorInvalidValue;
   if (C * nchp * 4 > (int64_t)QK_XP * QK_NT) return hipErrorInvalidValue;  // staging registers
   const int spw = quad_slots(ka.n, grid, nkit);
-  const int64_t lds = C * nchp * (64 + 4) + (int64_t)QK_NW * spw * 4 * C * 4 + QK_NW * 3 * 4;
+  // x pieces (4 C + 1 per chunk), fold terms (4 per chunk), parked partials
+  const int64_t lds = nchp * (4 * C + 1) * 16 + nchp * 16 + (int64_t)QK_NW * spw * 4 * C * 4 + QK_NW * 3 * 4;
   if (lds > PERSIST_LDS_MAX) return hipErrorInvalidValue;
   const bool hz = ka.zeros != nullptr;
   const int sb = ka.scale_bf16 ? 1 : 0;
@@ -1484,15 +1640,64 @@ hipError_t launch_quad(const KArgs& ka, int layout, hipStream_t s) {
   return hipLaunchKernel(fn, dim3(grid), dim3(QK_NT), args, (size_t)lds, s);
 }
 
+// bf16 x, c <= 16 CB.  Returns hipErrorInvalidValue (without launching) for
+// groups of 32 or 64 k (an item would span several) and for shapes past the
+// kernel's 32-bit offsets.
+template <int CB>
+hipError_t launch_mfma(const KArgs& ka, int layout, hipStream_t s) {
+  constexpr int NRT = CB == 1 ? 6 : 3;  // row tiles per workgroup (accumulators per lane)
+  constexpr int NT = CB == 1 ? 1024 : 512;
+  constexpr int D = 2;                  // items in flight per lane
+  if (ka.gshift == 0 || ka.gshift == 1) return hipErrorInvalidValue;
+  if (ka.n >= (int64_t(1) << 31) || ka.k >= (int64_t(1) << 24)) return hipErrorInvalidValue;
+  const int64_t ngroups = ka.gshift < 0 ? 1 : ((ka.k / 32) >> ka.gshift);
+  // an even share of the rows per CU, at most NRT tiles of 16 per workgroup
+  const int cus = cu_count();
+  int64_t rows = std::max<int64_t>(1, (ka.n + cus - 1) / cus);
+  rows = std::min<int64_t>(rows, 16 * NRT);
+  const int64_t grid = (ka.n + rows - 1) / rows;
+  // 32-bit offsets within a workgroup's rows (weights and scales; x offsets
+  // stay below 64 k < 2^31)
+  if ((rows + 16) * (ka.k / 2) >= (int64_t(1) << 31) || (rows + 16) * ngroups * 4 >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  const int64_t lds = (int64_t)(NT / 64) * NRT * 256 * CB * 4;
+  const bool hz = ka.zeros != nullptr;
+  const int sb = ka.scale_bf16 ? 1 : 0;
+#define WQ_MFN(L, Z, S) reinterpret_cast<const void*>(&k_gemv_w4_mfma<CB, NRT, NT, L, D, Z, S>)
+  const void* fns[2][2][2] = {{{WQ_MFN(0, false, false), WQ_MFN(0, false, true)},
+                               {WQ_MFN(0, true, false), WQ_MFN(0, true, true)}},
+                              {{WQ_MFN(1, false, false), WQ_MFN(1, false, true)},
+                               {WQ_MFN(1, true, false), WQ_MFN(1, true, true)}}};
+#undef WQ_MFN
+  const void* fn = fns[layout][hz][sb];
+  if (lds > 64 * 1024) {
+    static std::atomic<uint64_t> lds_ok[2][2][2];  // devices where fn may use all of the LDS
+    const hipError_t e = allow_dynamic_lds(fn, lds_ok[layout][hz][sb], PERSIST_LDS_MAX);
+    if (e != hipSuccess) return e == hipErrorInvalidValue ? hipErrorNotSupported : e;
+  }
+  int rows_arg = (int)rows;
+  void* args[] = {const_cast<KArgs*>(&ka), &rows_arg};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(NT), args, (size_t)lds, s);
+}
+
 // bf16 x, c <= 4: the persistent kernels when all of x fits in LDS (one
 // column: two rows per lane, x from LDS per lane; two to four columns: x
-// shared by lane quads), else the streaming kernel.
+// shared by lane quads), else for two to four columns the matrix-core
+// kernel, else (groups of 32 or 64 k) the streaming kernel.
 template <int C>
 hipError_t launch_stream_c(const KArgs& ka, int layout, hipStream_t s) {
   static_assert(C <= 4, "decode batches");
   hipError_t e;
-  if constexpr (C == 1) e = launch_persist<C>(ka, layout, s);
-  else e = launch_quad<C>(ka, layout, s);
+  if constexpr (C == 1) {
+    e = launch_persist<C>(ka, layout, s);
+  } else {
+    // the quad kernel streams the decode shapes faster than the matrix-core
+    // kernel (x staged once per CU, 256 contiguous bytes per row per load);
+    // past its LDS the matrix-core kernel takes over
+    e = launch_quad<C>(ka, layout, s);
+    if (e != hipErrorInvalidValue) return e;
+    e = launch_mfma<1>(ka, layout, s);
+  }
   if (e != hipErrorInvalidValue) return e;
   // rows per half-wave: 2 when that still leaves >= 4 workgroups per CU
   if (ka.n >= 16 * 1024) return launch_stream<2, C, 4>(ka, layout, s);
@@ -1567,7 +1772,11 @@ hipError_t launch_bf16(const KArgs& ka, int layout, hipStream_t s) {
     case 4: return launch_stream_c<4>(ka, layout, s);
     default: break;
   }
-  // wide batches: passes of at most 16 columns over x[c0:c0+16] -> out[c0:c0+16]
+  // wider batches on the matrix cores: one or two blocks of 16 columns
+  const hipError_t em = ka.c <= 16 ? launch_mfma<1>(ka, layout, s) : launch_mfma<2>(ka, layout, s);
+  if (em != hipErrorInvalidValue) return em;
+  // else (groups of 32 or 64 k) passes of at most 16 columns over
+  // x[c0:c0+16] -> out[c0:c0+16]
   for (int64_t c0 = 0; c0 < ka.c; c0 += 16) {
     KArgs kp = ka;
     kp.c = std::min<int64_t>(16, ka.c - c0);

@@ -224,15 +224,24 @@ def test_gemv_ragged_and_dtypes(case):
 
 
 # One case per launch path of wq_gemv_w4 that the workloads above do not
-# reach: bf16 x too large for the persistent kernel's LDS (the streaming
-# kernel, c = 3 and 4 at K = 28672), the persistent kernel on plain-layout
-# weights with stored bf16 zeros, fp32 x with N >= 16384 (two rows per
-# half-wave), and fp32 x wider than 16 columns (passes of 16).
+# reach.  bf16 x: the matrix-core kernel at c = 4 past the quad kernel's LDS
+# (K = 28672), on plain-layout weights (1 and 2 blocks of 16 columns, stored
+# zeros, fp32 scales) and on one group per row whose K is not a multiple of
+# 128 (a partial last item); the quad kernel on plain-layout weights with
+# stored zeros (groups of 128 and 64 k); with groups of 64 k, which the
+# matrix-core kernel leaves to the others, the streaming kernel when x is
+# too large for the quad kernel's LDS (c = 3 and 4 at K = 28672).  fp32 x:
+# N >= 16384 (two rows per half-wave) and c > 16 (passes of 16).
 PATHS = [
     # n, k, group, c, x dtype, scale dtype, zeros, out dtype, layout
-    (2048, 28672, 128, 3, "bf16", "bf16", False, torch.bfloat16, 1),
     (2048, 28672, 128, 4, "bf16", "bf16", False, torch.bfloat16, 1),
     (500, 2048, 128, 2, "bf16", "bf16", True, torch.bfloat16, 0),
+    (777, 2048, 128, 16, "bf16", "f32", True, torch.float32, 0),
+    (1000, 1024, 256, 20, "bf16", "bf16", True, torch.bfloat16, 0),
+    (333, 160, 160, 5, "bf16", "f32", False, torch.float32, 1),
+    (500, 2048, 64, 2, "bf16", "bf16", True, torch.bfloat16, 0),
+    (2048, 28672, 64, 3, "bf16", "bf16", False, torch.bfloat16, 1),
+    (2048, 28672, 64, 4, "bf16", "f32", False, torch.float32, 1),
     (16400, 1024, 128, 3, "f32", "f32", False, torch.float32, 1),
     (16400, 1024, 64, 8, "f32", "bf16", True, torch.float32, 0),
     (300, 1024, 64, 24, "f32", "f32", True, torch.float32, 1),
