@@ -322,12 +322,13 @@ __device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsu
 // The 128 digits u = t + 1 of one block (its 7 words in v) in k order:
 // dg[i] holds elements 4i..4i+3, one per byte.  lt is this lane's copy of
 // the digit table.
+template <int COPIES = LUT_COPIES>
 __device__ __forceinline__ void tern_decode(const uint32_t (&v)[7], const uint32_t* lt,
                                             uint32_t (&dg)[32]) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {  // qs bytes 0..15: element 16 j + b
-    const uint32_t l0 = lt[(v[g] & 0xFF) * LUT_COPIES], l1 = lt[((v[g] >> 8) & 0xFF) * LUT_COPIES];
-    const uint32_t l2 = lt[((v[g] >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(v[g] >> 24) * LUT_COPIES];
+    const uint32_t l0 = lt[(v[g] & 0xFF) * COPIES], l1 = lt[((v[g] >> 8) & 0xFF) * COPIES];
+    const uint32_t l2 = lt[((v[g] >> 16) & 0xFF) * COPIES], l3 = lt[(v[g] >> 24) * COPIES];
     uint32_t d0, d1, d2, d3, d4;
     transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
     dg[g] = d0; dg[4 + g] = d1; dg[8 + g] = d2; dg[12 + g] = d3; dg[16 + g] = d4;
@@ -335,8 +336,8 @@ __device__ __forceinline__ void tern_decode(const uint32_t (&v)[7], const uint32
 #pragma unroll
   for (int g = 0; g < 2; ++g) {  // qs bytes 16..23: element 80 + 8 j + b
     const uint32_t x = v[4 + g];
-    const uint32_t l0 = lt[(x & 0xFF) * LUT_COPIES], l1 = lt[((x >> 8) & 0xFF) * LUT_COPIES];
-    const uint32_t l2 = lt[((x >> 16) & 0xFF) * LUT_COPIES], l3 = lt[(x >> 24) * LUT_COPIES];
+    const uint32_t l0 = lt[(x & 0xFF) * COPIES], l1 = lt[((x >> 8) & 0xFF) * COPIES];
+    const uint32_t l2 = lt[((x >> 16) & 0xFF) * COPIES], l3 = lt[(x >> 24) * COPIES];
     uint32_t d0, d1, d2, d3, d4;
     transpose4(l0, l1, l2, l3, d0, d1, d2, d3, d4);
     dg[20 + g] = d0; dg[22 + g] = d1; dg[24 + g] = d2; dg[26 + g] = d3; dg[28 + g] = d4;
@@ -485,6 +486,289 @@ __device__ __forceinline__ void tern_decode_sb(const uint32_t (&v)[12], const ui
 }
 
 // dynamic LDS: table [256][16], x [C][bpr][36 words], sum q [C][k/32], d [C][k/32]
+// ---- Persistent GEMV on the int8 matrix cores (c <= 8, x and the digit
+// table in LDS once per CU).
+//
+// One 1024-lane workgroup per CU owns a balanced block of rows.  Lane l is
+// (q, r) = (l / 4, l % 4); quad q is block q of v_mfma_i32_4x4x4_16b_i8 (16
+// independent 4 x 4 x 4 int8 products per instruction) and covers rows
+// 4 (q / 8) .. 4 (q / 8) + 3 of the current 8-row group at PTQ1_0 block
+// 8 t + q % 8 of the current item t (8 rows x 1024 k).  Lane (q, r) decodes
+// its row's block as in the other kernels (table reads, byte transposes) to
+// 32 dwords of digits u = t + 1; MFMA s of a sub-block takes digit dword s
+// as its B operand and, as the A operand, the same four k of activation
+// column 4 cs + r (columns past c repeat the last; their results are never
+// stored).  The accumulator starts at -sum q of the sub-block, so after the
+// eight instructions of a 32-k sub-block element i holds the exact int32
+// sum over t q of column 4 cs + i, which the VALU scales by d_x and, per
+// block, by d_w.
+//
+// LDS: the digit table with one copy per lane (word 64 e + l: its reads
+// never meet in a bank, and the address e * 256 + 4 l is one v_perm of the
+// weight word and 4 l), then one record per 128-k block: each column's 128
+// int8 q (144 bytes apart), and per 32-k sub-block -sum q and d_x of each
+// column.  The record length is padded so that the sixteen lanes of four
+// quads (four blocks x four columns) start in sixteen different bank
+// groups.  Items (8-row group, 1024-k slice) in row-group-major order are
+// cut into 16 equal ranges, one per wave; a wave parks a row group's
+// partials in LDS when it leaves it and the outputs add the parks in wave
+// order (deterministic).
+constexpr int TM_NT = 1024;
+constexpr int TM_NW = TM_NT / 64;
+constexpr int TM_LUT_BYTES = 243 * 64 * 4;
+constexpr int TM_XCOL = 144;  // bytes between the columns of a block record
+constexpr int TM_XPRE = 2;    // x blocks per lane loaded ahead of the weights
+
+// Sums per sub-block in a record (-sum q and d_x for this many columns).
+__host__ __device__ constexpr int tm_sumw(int C) { return C; }
+// Record bytes per 128-k block for C columns: the smallest length >= the
+// data whose 16-byte units put lanes (block b, column r), b, r < 4, in
+// sixteen different groups of four banks.
+__host__ __device__ constexpr int tm_record(int C) {
+  const int base = C * TM_XCOL + 4 * tm_sumw(C) * 8;
+  for (int pad = 0; pad < 256; pad += 16) {
+    const int u = (base + pad) / 16;
+    bool seen[16] = {};
+    bool ok = true;
+    for (int b = 0; b < 4 && ok; ++b)
+      for (int r = 0; r < 4 && ok; ++r) {
+        if (r >= C) continue;  // lanes past c read column c - 1 (the same address)
+        const int g = (b * u + r * (TM_XCOL / 16)) & 15;
+        if (seen[g]) ok = false;
+        seen[g] = true;
+      }
+    if (ok) return base + pad;
+  }
+  return base;
+}
+
+template <int C, int D>
+__global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __restrict__ w,
+                                                           const uint8_t* __restrict__ xq,
+                                                           float* __restrict__ out, int n, int k,
+                                                           int c, int spw) {
+  constexpr int CS = (C + 3) / 4;        // MFMA column sets
+  constexpr int RB = tm_record(C);       // record bytes per block
+  constexpr int SW = tm_sumw(C);
+  constexpr int XSUM = C * TM_XCOL;      // offset of the sums in a record
+  extern __shared__ uint4 tm_smem[];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(tm_smem);
+  const int bpr = k / 128, nsb = k / 32;
+  uint8_t* rec = lds + TM_LUT_BYTES;                                     // [bpr][RB]
+  float* slots = reinterpret_cast<float*>(rec + bpr * RB);              // [NW][spw][8][C]
+  int* wtab = reinterpret_cast<int*>(slots + TM_NW * spw * 8 * C);      // [NW][3]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 2, r = lane & 3;
+  const int kb = q & 7, rin = (q >> 3) * 4 + r;  // block in the item, row in the 8-row group
+  const int nwg = (int)gridDim.x, b = (int)blockIdx.x;
+  const int r0 = b * (n / nwg) + min(b, n % nwg);
+  const int count = n / nwg + (b < n % nwg ? 1 : 0);
+  const int nro = (count + 7) / 8;
+  const int nit = (bpr + 7) / 8;  // items per row group
+  const int items = nro * nit;
+  const int i0 = wave * items / TM_NW, i1 = (wave + 1) * items / TM_NW;
+  const int ro_first = i0 / nit;
+  if (lane == 0) {
+    wtab[wave * 3 + 0] = i0;
+    wtab[wave * 3 + 1] = i1;
+    wtab[wave * 3 + 2] = ro_first;
+  }
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)w + (int64_t)r0 * bpr * PT_BYTES), 0, count * bpr * PT_BYTES, 0x00020000);
+
+  // weight ring: issue position (row, block) of this lane, items left
+  int irow = ro_first * 8 + rin, iblk = (i0 - ro_first * nit) * 8 + kb, left = i1 - i0;
+  uint32_t wd[D][7];
+  auto issue = [&](int slot) {
+    const bool ok = left > 0 && irow < count && iblk < bpr;
+    const uint32_t o = ok ? (uint32_t)((irow * bpr + iblk) * PT_BYTES) : T_OOB;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) wd[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * j), 0, 0);
+    --left;
+    iblk += 8;
+    if (iblk - kb >= nit * 8) {
+      iblk = kb;
+      irow += 8;
+    }
+  };
+  // x blocks (q8_1, 36 bytes) of the staging: the first TM_XPRE per lane
+  // are loaded before the weight prologue, since a wave's loads complete in
+  // issue order and the staging would otherwise wait for its weights.  The
+  // order is rotated per workgroup: every CU reads the same x.
+  const int nxb = c * nsb;
+  const int xrot = (int)(((uint32_t)b * 2654435761u) % (uint32_t)nxb);
+  auto xblock = [&](int i) {
+    const int v = i + xrot;
+    return v >= nxb ? v - nxb : v;
+  };
+  // (buffer loads, no branch: a conditional load would put the first use of
+  // its value, and so the wait for it, right behind it)
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)xq, 0, nxb * Q8_BYTES, 0x00020000);
+  uint32_t xpre[TM_XPRE][9];
+#pragma unroll
+  for (int i = 0; i < TM_XPRE; ++i) {
+    const int idx = tid + i * TM_NT;
+    const uint32_t o = idx < nxb ? (uint32_t)(xblock(idx) * Q8_BYTES) : T_OOB;
+    const uint4 lo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)o, 0, 0));
+    const uint4 hi = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(o + 16), 0, 0));
+    xpre[i][0] = lo.x; xpre[i][1] = lo.y; xpre[i][2] = lo.z; xpre[i][3] = lo.w;
+    xpre[i][4] = hi.x; xpre[i][5] = hi.y; xpre[i][6] = hi.z; xpre[i][7] = hi.w;
+    xpre[i][8] = __builtin_amdgcn_raw_buffer_load_b32(xrs, (int)(o + 32), 0, 0);
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d);
+
+  // one-time staging: the digit table (one copy per lane), then per block
+  // x q, -sum q and d_x of each column
+  for (int idx = tid; idx < 243 * 16; idx += TM_NT) {
+    const uint32_t e = idx >> 4;
+    const uint32_t ent = (e % 3) | ((e / 3) % 3) << 8 | ((e / 9) % 3) << 16 | ((e / 27) % 3) << 24 |
+                         ((e / 81) % 3) << 4;
+    *reinterpret_cast<uint4*>(lds + e * 256 + (idx & 15) * 16) = make_uint4(ent, ent, ent, ent);
+  }
+  auto put_x = [&](int xi, const uint32_t (&bk)[9]) {
+    const int col = xi / nsb, sb = xi - col * nsb;
+    int sum = 0;
+#pragma unroll
+    for (int i = 1; i < 9; ++i) sum = __builtin_amdgcn_sdot4((int)bk[i], 0x01010101, sum, false);
+    uint8_t* rb = rec + (sb >> 2) * RB;
+    uint4* dst = reinterpret_cast<uint4*>(rb + col * TM_XCOL + (sb & 3) * 32);
+    dst[0] = make_uint4(bk[1], bk[2], bk[3], bk[4]);
+    dst[1] = make_uint4(bk[5], bk[6], bk[7], bk[8]);
+    int* sums = reinterpret_cast<int*>(rb + XSUM + (sb & 3) * SW * 8);
+    sums[col] = -sum;
+    reinterpret_cast<float*>(sums + SW)[col] = f16_to_f32(bk[0] & 0xFFFFu);
+  };
+#pragma unroll
+  for (int i = 0; i < TM_XPRE; ++i) {
+    const int idx = tid + i * TM_NT;
+    if (idx < nxb) put_x(xblock(idx), xpre[i]);
+  }
+  for (int idx = tid + TM_XPRE * TM_NT; idx < nxb; idx += TM_NT) {  // the rest (wide x)
+    const int xi = xblock(idx);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(xq + (int64_t)xi * Q8_BYTES);
+    uint32_t bk[9];
+#pragma unroll
+    for (int j = 0; j < 9; ++j) bk[j] = src[j];
+    put_x(xi, bk);
+  }
+  __syncthreads();
+
+  float acc[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) acc[j] = 0.f;
+  // sum the 8 blocks of each row (lanes of one half-wave with equal l % 4,
+  // fixed order) and park them in this wave's slot ro - ro_first
+  auto park = [&](int ro) {
+    float* dst = slots + ((wave * spw + (ro - ro_first)) * 8 + rin) * C;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float v = acc[j];
+      v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror 4
+      v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror 8
+      v += __shfl_xor(v, 16);
+      if (kb == 0) dst[j] = v;
+      acc[j] = 0.f;
+    }
+  };
+
+  const uint32_t lane4 = (uint32_t)lane * 4;
+  int cro = ro_first, cit = i0 - ro_first * nit;  // consume position
+  const int nsteps = i1 - i0;
+  for (int base = 0; base < nsteps; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const bool valid = base + d < nsteps;
+      uint32_t v[7];
+#pragma unroll
+      for (int j = 0; j < 7; ++j) v[j] = wd[d][j];
+      issue(d);  // the ring slot is free once copied out
+      if (!valid) continue;  // uniform; no load below
+      // digits: table word of byte i of a weight word at byte offset
+      // (byte << 8) | 4 lane, one v_perm
+      uint32_t dg[32];
+      {
+        auto look = [&](uint32_t word, int i) {
+          const uint32_t a = __builtin_amdgcn_perm(word, lane4, 0x0C0C0000u | ((4u + i) << 8));
+          return *reinterpret_cast<const uint32_t*>(lds + a);
+        };
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {  // qs bytes 0..15: element 16 j + byte
+          uint32_t d0, d1, d2, d3, d4;
+          transpose4(look(v[g], 0), look(v[g], 1), look(v[g], 2), look(v[g], 3), d0, d1, d2, d3, d4);
+          dg[g] = d0; dg[4 + g] = d1; dg[8 + g] = d2; dg[12 + g] = d3; dg[16 + g] = d4;
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {  // qs bytes 16..23: element 80 + 8 j + byte
+          uint32_t d0, d1, d2, d3, d4;
+          transpose4(look(v[4 + g], 0), look(v[4 + g], 1), look(v[4 + g], 2), look(v[4 + g], 3), d0, d1, d2, d3, d4);
+          dg[20 + g] = d0; dg[22 + g] = d1; dg[24 + g] = d2; dg[26 + g] = d3; dg[28 + g] = d4;
+        }
+        const uint32_t h = v[6] & 0xFFFFu;  // qh: elements 120..127
+        dg[30] = (h | (h << 14)) & 0x03030303u;
+        dg[31] = ((h >> 4) | (h << 10)) & 0x03030303u;
+      }
+      const float dw = f16_to_f32(v[6] >> 16);  // 0 past the end of the row or past its rows
+      const int blk = min(cit * 8 + kb, bpr - 1);  // reads stay in the staged range
+      const uint8_t* rb = rec + blk * RB;
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) {
+        constexpr int NJ = C < 4 ? C : 4;  // columns of this set
+        const uint8_t* xp = rb + min(cs * 4 + r, c - 1) * TM_XCOL;
+        float part[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) part[j] = 0.f;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int* sums = reinterpret_cast<const int*>(rb + XSUM + s4 * SW * 8) + cs * 4;
+          const float* dx = reinterpret_cast<const float*>(sums + SW);
+          intx4 acc_i;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc_i[j] = sums[j < NJ ? j : 0];
+          const uint4 xa = *reinterpret_cast<const uint4*>(xp + s4 * 32);
+          const uint4 xb = *reinterpret_cast<const uint4*>(xp + s4 * 32 + 16);
+          const int xw[8] = {(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, (int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w};
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+            acc_i = __builtin_amdgcn_mfma_i32_4x4x4i8(xw[s], (int)dg[8 * s4 + s], acc_i, 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) part[j] = fmaf(dx[j], (float)acc_i[j], part[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[cs * 4 + j] = fmaf(dw, part[j], acc[cs * 4 + j]);
+      }
+      if (++cit == nit) {  // uniform: the wave leaves its row group
+        park(cro);
+        cit = 0;
+        ++cro;
+      }
+    }
+  }
+  if (nsteps > 0 && cit != 0) park(cro);
+  __syncthreads();
+
+  // outputs: the parks of each row in wave order
+  for (int idx = tid; idx < nro * 8 * c; idx += TM_NT) {
+    const int ro = idx / (8 * c);
+    const int rc = idx - ro * 8 * c;
+    const int rr = rc / c, col = rc - rr * c;
+    if (ro * 8 + rr >= count) continue;
+    const int ilo = ro * nit, ihi = ilo + nit;
+    // wave h owns items [floor(h items / NW), floor((h + 1) items / NW)); the
+    // one owning item i is floor(((i + 1) NW - 1) / items)
+    const int hlo = ((ilo + 1) * TM_NW - 1) / items, hhi = (ihi * TM_NW - 1) / items;
+    float v = 0.f;
+    for (int h = hlo; h <= hhi; ++h) {
+      const int a = wtab[h * 3 + 0], e = wtab[h * 3 + 1];
+      if (e > a && a < ihi && e > ilo) v += slots[((h * spw + (ro - wtab[h * 3 + 2])) * 8 + rr) * C + col];
+    }
+    out[(int64_t)col * n + r0 + ro * 8 + rr] = v;
+  }
+}
+
 // LPR lanes per row (8 or 16): a wave holds 64 / LPR rows, a lane one block
 // of its row per item (an item = LPR consecutive blocks of each row).
 // SB: the weights are PTQ1_1 superblocks (LPR = 8: an item is one superblock
@@ -975,18 +1259,70 @@ hipError_t launch_ternary_persist(const uint32_t* wp, const uint8_t* xq, int64_t
   return hipGetLastError();
 }
 
+// Largest number of 8-row groups one wave of k_gemv_ternary_mq touches, over
+// the two row counts (q and q + 1) the workgroups get.
+int tm_slots(int64_t n, int grid, int nit) {
+  const int64_t qn = n / grid;
+  int best = 1;
+  for (int64_t cnt = qn; cnt <= qn + 1; ++cnt) {
+    const int64_t items = ((cnt + 7) / 8) * nit;
+    for (int h = 0; h < TM_NW; ++h) {
+      const int64_t a = h * items / TM_NW, b = (h + 1) * items / TM_NW;
+      if (b > a) best = std::max(best, (int)((b - 1) / nit - a / nit + 1));
+    }
+  }
+  return best;
+}
+
+// The matrix-core GEMV for c <= C when x and the table fit in LDS; returns
+// hipErrorInvalidValue (no launch) otherwise.
+template <int C>
+hipError_t launch_ternary_mq(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
+                             float* out, hipStream_t s) {
+  constexpr int D = 2;
+  if (n >= (int64_t(1) << 30) || k >= (int64_t(1) << 24)) return hipErrorInvalidValue;
+  const int64_t bpr = k / 128;
+  int grid = device_cu_count();
+  if ((int64_t)grid * 8 > n) grid = (int)std::max<int64_t>(1, n / 8);
+  const int64_t maxrows = (n + grid - 1) / grid + 8;
+  if (maxrows * bpr * PT_BYTES >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const int nit = (int)((bpr + 7) / 8);
+  const int spw = tm_slots(n, grid, nit);
+  // (at least 64 KiB: a table address of any byte value, 243..255 included,
+  // stays inside the allocation)
+  const int64_t lds = std::max<int64_t>(
+      65536, TM_LUT_BYTES + bpr * tm_record(C) + (int64_t)TM_NW * spw * 8 * C * 4 + TM_NW * 3 * 4);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  const void* fn = reinterpret_cast<const void*>(&k_gemv_ternary_mq<C, D>);
+  static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
+  const hipError_t e = allow_dynamic_lds(fn, lds_ok, 160 * 1024);
+  if (e != hipSuccess) return e == hipErrorInvalidValue ? hipErrorNotSupported : e;
+  int n_arg = (int)n, k_arg = (int)k, c_arg = (int)c, spw_arg = spw;
+  void* args[] = {const_cast<uint32_t**>(&wp), const_cast<uint8_t**>(&xq), &out, &n_arg, &k_arg, &c_arg, &spw_arg};
+  return hipLaunchKernel(fn, dim3(grid), dim3(TM_NT), args, (size_t)lds, s);
+}
+
 // Up to 16 columns on the vector units.
 hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                  int64_t c, float* out, hipStream_t s) {
   const uint32_t* wp0 = reinterpret_cast<const uint32_t*>(w);
   {
-    // one column: the K-split kernel (wider splits spilled registers)
+    // one column: the K-split kernel (wider splits spilled registers; the
+    // matrix-core kernel was 3-6% slower at one column, and needs more LDS);
+    // 2-8 columns: the matrix-core kernel
     const SbTables none{};
     hipError_t e = hipErrorInvalidValue;
     if (c == 1) {
       e = launch_ternary_ksplit<1, false>(wp0, xq, n, k, c, out, none, s);
       if (e != hipErrorInvalidValue) return e;
     }
+    switch (c) {
+      case 1: break;
+      case 2: e = launch_ternary_mq<2>(wp0, xq, n, k, c, out, s); break;
+      case 3: case 4: e = launch_ternary_mq<4>(wp0, xq, n, k, c, out, s); break;
+      default: if (c <= 8) e = launch_ternary_mq<8>(wp0, xq, n, k, c, out, s); break;
+    }
+    if (e != hipErrorInvalidValue) return e;
     switch (c) {
       case 1: break;
       case 2: e = launch_ternary_persist<2, false>(wp0, xq, n, k, c, out, none, s); break;
