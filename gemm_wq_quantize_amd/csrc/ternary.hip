@@ -413,14 +413,15 @@ struct SbTables {
 __host__ __device__ constexpr int sb_lds_words(int n_esc) { return 1534 + n_esc + 2 * n_esc; }
 
 // Codebook and escape table into LDS (256 threads; one-time per workgroup).
+template <int NTH = 256>
 __device__ __forceinline__ void tern_stage_sb(uint32_t* dst, const SbTables& t) {
   const int tid = threadIdx.x;
   const uint32_t* cb = reinterpret_cast<const uint32_t*>(t.codebook);
-  for (int i = tid; i < 1534; i += 256) dst[i] = cb[i];
+  for (int i = tid; i < 1534; i += NTH) dst[i] = cb[i];
   const int ne = t.n_esc;
-  for (int i = tid; i < ne; i += 256) dst[1534 + i] = (uint32_t)t.esc_idx[i];
+  for (int i = tid; i < ne; i += NTH) dst[1534 + i] = (uint32_t)t.esc_idx[i];
   const uint32_t* ep = reinterpret_cast<const uint32_t*>(t.esc_patt);
-  for (int i = tid; i < 2 * ne; i += 256) dst[1534 + ne + i] = ep[i];
+  for (int i = tid; i < 2 * ne; i += NTH) dst[1534 + ne + i] = ep[i];
 }
 
 // The 128 digits and the scale of sub-block sub (= this lane's block within
@@ -428,12 +429,13 @@ __device__ __forceinline__ void tern_stage_sb(uint32_t* dst, const SbTables& t) 
 // 23, v[6..11] the superblock's bytes 192..215.  gidx: the superblock's
 // index (the escape key); tbl: the staged tables (codebook bytes, then the
 // escape indices and patterns).
+template <int COPIES = LUT_COPIES>
 __device__ __forceinline__ void tern_decode_sb(const uint32_t (&v)[12], const uint32_t* lt,
                                                const uint32_t* tbl, int n_esc, int gidx, int sub,
                                                uint32_t (&dg)[32], float& dw) {
   // qs: exactly the PTQ1_0 sections
   uint32_t v7[7] = {v[0], v[1], v[2], v[3], v[4], v[5], 0u};
-  tern_decode(v7, lt, dg);
+  tern_decode<COPIES>(v7, lt, dg);
   // tail: the 8 digits from digit d0 of qh byte b0 on (b0 = 8 sub / 5,
   // d0 = 8 sub % 5), out of the three bytes b0 .. b0 + 2
   // (word selection by lane masks: a select chain on the array makes the
@@ -443,9 +445,9 @@ __device__ __forceinline__ void tern_decode_sb(const uint32_t (&v)[12], const ui
   const uint32_t lo = (v[6] & w0) | (v[7] & w1) | (v[8] & w2);
   const uint32_t hi = (v[7] & w0) | (v[8] & w1) | (v[9] & w2);
   const uint32_t three = __builtin_amdgcn_alignbit(hi, lo, 8 * (b0 & 3));
-  const uint32_t l0 = lt[(three & 0xFF) * LUT_COPIES];
-  const uint32_t l1 = lt[((three >> 8) & 0xFF) * LUT_COPIES];
-  const uint32_t l2 = lt[((three >> 16) & 0xFF) * LUT_COPIES];
+  const uint32_t l0 = lt[(three & 0xFF) * COPIES];
+  const uint32_t l1 = lt[((three >> 8) & 0xFF) * COPIES];
+  const uint32_t l2 = lt[((three >> 16) & 0xFF) * COPIES];
   // the digit sequence of the three bytes, one digit per byte: table entry =
   // digits 0..3 in bytes 0..3 (two bits each) and digit 4 in bits 4..5
   const uint32_t s0 = l0 & 0x03030303u;
@@ -457,7 +459,7 @@ __device__ __forceinline__ void tern_decode_sb(const uint32_t (&v)[12], const ui
   dg[30] = __builtin_amdgcn_alignbyte(d4 ? s2 : s1, d4 ? s1 : s0, d0 & 3);  // elements 120..123
   dg[31] = d4 ? s2 : __builtin_amdgcn_alignbyte(s2, s1, d0 & 3);            // elements 124..127
   // scale: pattern index from the exponent byte and the free trit
-  const uint32_t free = (lt[(v[9] & 0xFF) * LUT_COPIES] >> 4) & 3u;
+  const uint32_t free = (lt[(v[9] & 0xFF) * COPIES] >> 4) & 3u;
   const int pat = (int)((v[11] >> 24) | (free << 8));
   uint32_t e;
   if (pat < SB_CODEBOOK_ROWS) {
@@ -542,20 +544,26 @@ __host__ __device__ constexpr int tm_record(int C) {
   return base;
 }
 
-template <int C, int D>
+// SB: the weights are PTQ1_1 superblocks (an item's eight blocks are one
+// superblock; lane q % 8 decodes sub-block q % 8 from its 24 qs bytes and the
+// superblock's last 24 bytes), with the codebook and escape tables staged in
+// LDS after the x records.
+template <int C, int D, bool SB>
 __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __restrict__ w,
                                                            const uint8_t* __restrict__ xq,
                                                            float* __restrict__ out, int n, int k,
-                                                           int c, int spw) {
+                                                           int c, int spw, SbTables sbt) {
   constexpr int CS = (C + 3) / 4;        // MFMA column sets
   constexpr int RB = tm_record(C);       // record bytes per block
   constexpr int SW = tm_sumw(C);
   constexpr int XSUM = C * TM_XCOL;      // offset of the sums in a record
+  constexpr int W = SB ? 12 : 7;         // words a lane loads per item
   extern __shared__ uint4 tm_smem[];
   uint8_t* lds = reinterpret_cast<uint8_t*>(tm_smem);
   const int bpr = k / 128, nsb = k / 32;
   uint8_t* rec = lds + TM_LUT_BYTES;                                     // [bpr][RB]
-  float* slots = reinterpret_cast<float*>(rec + bpr * RB);              // [NW][spw][8][C]
+  uint32_t* tbl = reinterpret_cast<uint32_t*>(rec + bpr * RB);          // superblock tables
+  float* slots = reinterpret_cast<float*>(tbl + (SB ? sb_lds_words(sbt.n_esc) : 0));  // [NW][spw][8][C]
   int* wtab = reinterpret_cast<int*>(slots + TM_NW * spw * 8 * C);      // [NW][3]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -575,17 +583,27 @@ __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __res
     wtab[wave * 3 + 1] = i1;
     wtab[wave * 3 + 2] = ro_first;
   }
+  constexpr int BB = SB ? SB_BYTES / 8 : PT_BYTES;  // weight bytes per 128-k block
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)w + (int64_t)r0 * bpr * PT_BYTES), 0, count * bpr * PT_BYTES, 0x00020000);
+      (void*)((const uint8_t*)w + (int64_t)r0 * bpr * BB), 0, count * bpr * BB, 0x00020000);
 
   // weight ring: issue position (row, block) of this lane, items left
   int irow = ro_first * 8 + rin, iblk = (i0 - ro_first * nit) * 8 + kb, left = i1 - i0;
-  uint32_t wd[D][7];
+  uint32_t wd[D][W];
   auto issue = [&](int slot) {
     const bool ok = left > 0 && irow < count && iblk < bpr;
-    const uint32_t o = ok ? (uint32_t)((irow * bpr + iblk) * PT_BYTES) : T_OOB;
+    if constexpr (SB) {
+      // this sub-block's qs words, then the superblock's last 24 bytes
+      const uint32_t o = ok ? (uint32_t)((irow * nit + (iblk >> 3)) * SB_BYTES) : T_OOB;
 #pragma unroll
-    for (int j = 0; j < 7; ++j) wd[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * j), 0, 0);
+      for (int j = 0; j < 6; ++j) wd[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 24 * kb + 4 * j), 0, 0);
+#pragma unroll
+      for (int j = 0; j < 6; ++j) wd[slot][6 + j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 192 + 4 * j), 0, 0);
+    } else {
+      const uint32_t o = ok ? (uint32_t)((irow * bpr + iblk) * PT_BYTES) : T_OOB;
+#pragma unroll
+      for (int j = 0; j < 7; ++j) wd[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(o + 4 * j), 0, 0);
+    }
     --left;
     iblk += 8;
     if (iblk - kb >= nit * 8) {
@@ -655,6 +673,7 @@ __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __res
     for (int j = 0; j < 9; ++j) bk[j] = src[j];
     put_x(xi, bk);
   }
+  if constexpr (SB) tern_stage_sb<TM_NT>(tbl, sbt);
   __syncthreads();
 
   float acc[C];
@@ -676,21 +695,26 @@ __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __res
   };
 
   const uint32_t lane4 = (uint32_t)lane * 4;
+  const uint32_t* lut_lane = reinterpret_cast<const uint32_t*>(lds) + lane;  // this lane's table copy
   int cro = ro_first, cit = i0 - ro_first * nit;  // consume position
   const int nsteps = i1 - i0;
   for (int base = 0; base < nsteps; base += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const bool valid = base + d < nsteps;
-      uint32_t v[7];
+      uint32_t v[W];
 #pragma unroll
-      for (int j = 0; j < 7; ++j) v[j] = wd[d][j];
+      for (int j = 0; j < W; ++j) v[j] = wd[d][j];
       issue(d);  // the ring slot is free once copied out
       if (!valid) continue;  // uniform; no load below
-      // digits: table word of byte i of a weight word at byte offset
-      // (byte << 8) | 4 lane, one v_perm
       uint32_t dg[32];
-      {
+      float dw;
+      if constexpr (SB) {
+        // (rows past the workgroup's decode garbage that is never stored)
+        tern_decode_sb<64>(v, lut_lane, tbl, sbt.n_esc, (r0 + cro * 8 + rin) * nit + cit, kb, dg, dw);
+      } else {
+        // digits: table word of byte i of a weight word at byte offset
+        // (byte << 8) | 4 lane, one v_perm
         auto look = [&](uint32_t word, int i) {
           const uint32_t a = __builtin_amdgcn_perm(word, lane4, 0x0C0C0000u | ((4u + i) << 8));
           return *reinterpret_cast<const uint32_t*>(lds + a);
@@ -710,8 +734,8 @@ __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __res
         const uint32_t h = v[6] & 0xFFFFu;  // qh: elements 120..127
         dg[30] = (h | (h << 14)) & 0x03030303u;
         dg[31] = ((h >> 4) | (h << 10)) & 0x03030303u;
+        dw = f16_to_f32(v[6] >> 16);  // 0 past the end of the row or past its rows
       }
-      const float dw = f16_to_f32(v[6] >> 16);  // 0 past the end of the row or past its rows
       const int blk = min(cit * 8 + kb, bpr - 1);  // reads stay in the staged range
       const uint8_t* rb = rec + blk * RB;
 #pragma unroll
@@ -1276,9 +1300,9 @@ int tm_slots(int64_t n, int grid, int nit) {
 
 // The matrix-core GEMV for c <= C when x and the table fit in LDS; returns
 // hipErrorInvalidValue (no launch) otherwise.
-template <int C>
+template <int C, bool SB>
 hipError_t launch_ternary_mq(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
-                             float* out, hipStream_t s) {
+                             float* out, const SbTables& sbt, hipStream_t s) {
   constexpr int D = 2;
   if (n >= (int64_t(1) << 30) || k >= (int64_t(1) << 24)) return hipErrorInvalidValue;
   const int64_t bpr = k / 128;
@@ -1286,19 +1310,22 @@ hipError_t launch_ternary_mq(const uint32_t* wp, const uint8_t* xq, int64_t n, i
   if ((int64_t)grid * 8 > n) grid = (int)std::max<int64_t>(1, n / 8);
   const int64_t maxrows = (n + grid - 1) / grid + 8;
   if (maxrows * bpr * PT_BYTES >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (SB && bpr % 8 != 0) return hipErrorInvalidValue;  // whole superblocks
   const int nit = (int)((bpr + 7) / 8);
   const int spw = tm_slots(n, grid, nit);
   // (at least 64 KiB: a table address of any byte value, 243..255 included,
   // stays inside the allocation)
   const int64_t lds = std::max<int64_t>(
-      65536, TM_LUT_BYTES + bpr * tm_record(C) + (int64_t)TM_NW * spw * 8 * C * 4 + TM_NW * 3 * 4);
+      65536, TM_LUT_BYTES + bpr * tm_record(C) + (SB ? sb_lds_words(sbt.n_esc) * 4 : 0) +
+                 (int64_t)TM_NW * spw * 8 * C * 4 + TM_NW * 3 * 4);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const void* fn = reinterpret_cast<const void*>(&k_gemv_ternary_mq<C, D>);
+  const void* fn = reinterpret_cast<const void*>(&k_gemv_ternary_mq<C, D, SB>);
   static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
   const hipError_t e = allow_dynamic_lds(fn, lds_ok, 160 * 1024);
   if (e != hipSuccess) return e == hipErrorInvalidValue ? hipErrorNotSupported : e;
   int n_arg = (int)n, k_arg = (int)k, c_arg = (int)c, spw_arg = spw;
-  void* args[] = {const_cast<uint32_t**>(&wp), const_cast<uint8_t**>(&xq), &out, &n_arg, &k_arg, &c_arg, &spw_arg};
+  SbTables t = sbt;
+  void* args[] = {const_cast<uint32_t**>(&wp), const_cast<uint8_t**>(&xq), &out, &n_arg, &k_arg, &c_arg, &spw_arg, &t};
   return hipLaunchKernel(fn, dim3(grid), dim3(TM_NT), args, (size_t)lds, s);
 }
 
@@ -1318,9 +1345,9 @@ hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n,
     }
     switch (c) {
       case 1: break;
-      case 2: e = launch_ternary_mq<2>(wp0, xq, n, k, c, out, s); break;
-      case 3: case 4: e = launch_ternary_mq<4>(wp0, xq, n, k, c, out, s); break;
-      default: if (c <= 8) e = launch_ternary_mq<8>(wp0, xq, n, k, c, out, s); break;
+      case 2: e = launch_ternary_mq<2, false>(wp0, xq, n, k, c, out, none, s); break;
+      case 3: case 4: e = launch_ternary_mq<4, false>(wp0, xq, n, k, c, out, none, s); break;
+      default: if (c <= 8) e = launch_ternary_mq<8, false>(wp0, xq, n, k, c, out, none, s); break;
     }
     if (e != hipErrorInvalidValue) return e;
     switch (c) {
@@ -1366,8 +1393,9 @@ hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, i
 }
 
 // PTQ1_1 superblocks: passes of at most 8 columns on the kernels that keep
-// x in LDS (the widest pass that fits); hipErrorInvalidValue when even one
-// column does not fit (the entry point bounds k so that it does).
+// x in LDS (the widest pass that fits; the matrix-core kernel first, then
+// the vector kernels); hipErrorInvalidValue when even one column does not
+// fit (the entry point bounds k so that it does).
 hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, const int32_t* esc_idx,
                                   const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq,
                                   int64_t n, int64_t k, int64_t c, float* out, hipStream_t s) {
@@ -1380,12 +1408,20 @@ hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, con
     hipError_t e = hipErrorInvalidValue;
     int64_t done = 0;
     if (left == 1) {
-      e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, s);
+      // the matrix-core kernel (its two-column form, column 0 repeated: 7%
+      // faster than the K-split kernel here), else the K-split kernel
+      e = launch_ternary_mq<2, true>(wp, xp, n, k, 1, op, t, s);
+      if (e == hipErrorInvalidValue) e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, s);
       done = 1;
     } else {
-      // widest pass first; a pass that does not fit its x in LDS launches nothing
-      if (left >= 5) { e = launch_ternary_persist<8, true>(wp, xp, n, k, std::min<int64_t>(8, left), op, t, s); done = std::min<int64_t>(8, left); }
-      if (e == hipErrorInvalidValue && left >= 3) { e = launch_ternary_persist<4, true>(wp, xp, n, k, std::min<int64_t>(4, left), op, t, s); done = std::min<int64_t>(4, left); }
+      // widest pass first, the matrix-core kernel before the vector one; a
+      // pass that does not fit its x in LDS launches nothing
+      const int64_t w8 = std::min<int64_t>(8, left), w4 = std::min<int64_t>(4, left);
+      if (left >= 5) { e = launch_ternary_mq<8, true>(wp, xp, n, k, w8, op, t, s); done = w8; }
+      if (e == hipErrorInvalidValue && left >= 5) { e = launch_ternary_persist<8, true>(wp, xp, n, k, w8, op, t, s); done = w8; }
+      if (e == hipErrorInvalidValue && left >= 3) { e = launch_ternary_mq<4, true>(wp, xp, n, k, w4, op, t, s); done = w4; }
+      if (e == hipErrorInvalidValue && left >= 3) { e = launch_ternary_persist<4, true>(wp, xp, n, k, w4, op, t, s); done = w4; }
+      if (e == hipErrorInvalidValue) { e = launch_ternary_mq<2, true>(wp, xp, n, k, 2, op, t, s); done = 2; }
       if (e == hipErrorInvalidValue) { e = launch_ternary_persist<2, true>(wp, xp, n, k, 2, op, t, s); done = 2; }
       if (e == hipErrorInvalidValue) { e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, s); done = 1; }
     }

@@ -61,10 +61,12 @@ def test_ptq1_1_gemv_timed_shape():
         check_f32(gemv(dev, xq, k, n), ot.gemv_ternary_ptq1_1(*ref, xref))
 
 
-@pytest.mark.parametrize("k,n", [(8192, 300), (1024, 77), (16384, 40)])
+@pytest.mark.parametrize("k,n", [(8192, 300), (1024, 77), (16384, 40), (65536, 24)])
 def test_ptq1_1_gemv_escapes_and_passes(k, n):
     # independent exponents: most superblocks escape; widths that take every
-    # pass shape (1, 2, 3 columns; 5..8; more than 8 in passes)
+    # pass shape (1, 2, 3 columns; 5..8; more than 8 in passes); k = 65536
+    # is past the matrix-core kernel's LDS, so its passes run on the vector
+    # kernels (one column: the K-split kernel)
     p = wq_inputs.ternary_gemv(k, n, cmax=16, seed=k + n)
     rng = np.random.default_rng(n)
     d = ((rng.integers(5, 13, p.d_bits.shape) << 10) | rng.integers(0, 1024, p.d_bits.shape)).astype(np.uint16)
