@@ -11,7 +11,8 @@
 //
 // Tiling.  A 256-lane workgroup computes a 256 x 256 tile of C with four
 // waves in a 2 x 2 grid; each wave owns 128 x 128 = 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16.  K advances 64 per step through a three-stage LDS
+// v_mfma_f32_32x32x16_bf16 (with group scales a 1 x 4 grid, 256 x 64 =
+// 8 x 2 blocks each, so that every B word is dequantised by one wave).  K advances 64 per step through a three-stage LDS
 // ring filled by buffer loads that write LDS directly (no register staging):
 // while step t is multiplied, steps t+1 and t+2 are in flight, so one step of
 // MFMA work (about 0.85 us) never has to cover a whole memory latency.  B
@@ -43,7 +44,10 @@
 // q * s - z * s = (q - z) * s with one FMA -- exact, the product needs at
 // most 17 significant bits -- and rounds the pair to bf16 (RNE) for the
 // MFMA.  No row sums are needed; the only rounding beyond the float32
-// accumulation is that of (q - z) * s to bf16.
+// accumulation is that of (q - z) * s to bf16.  This dequantisation is about
+// 23 VALU instructions per B word, so the waves split the tile by columns:
+// each B word is then converted once per workgroup (with 2 x 2 waves, twice)
+// at the cost of twice the A fragment reads from LDS.
 #include "wq_internal.h"
 
 namespace wq {
@@ -180,12 +184,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-#ifndef WQ_G_SCHED
-#define WQ_G_SCHED 1  // 1: interleave MFMA / VALU / LDS reads with scheduling-group barriers
-#endif
-#ifndef WQ_G_VPM
-#define WQ_G_VPM 4    // VALU instructions placed after each MFMA with group scales
-#endif
+// VALU instructions placed after each MFMA by the scheduling groups with
+// group scales (three: 5% faster than four or two, 8192^3 group 128)
+constexpr int G_VPM = 3;
 
 // Epilogue staging: half the tile (128 rows x 256 bf16) at a time, rows
 // padded by 16 bytes so that the two rows one 2-byte LDS write touches (4
@@ -216,7 +217,13 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
+  // wave grid: 2 x 2 (128 x 128 each) with one scale per column; 1 x 4 (256
+  // rows x 64 columns each) with group scales, so that each B word is
+  // dequantised by one wave only
+  constexpr int MI = GS ? 8 : 4;  // 32-row blocks per wave
+  constexpr int NJ = GS ? 2 : 4;  // 32-column blocks per wave
+  const int wm = GS ? 0 : wave >> 1;
+  const int col0 = GS ? wave * 64 : WN * 128;  // the wave's first column in the tile
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int rows_a = (int)min((int64_t)BM, p.m - m0);
   const int rows_b = (int)min((int64_t)BN, p.n - n0);
@@ -307,11 +314,11 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  floatx16 acc[4][4];
+  floatx16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   // Row sums of A: this wave sums row blocks 2 WN and 2 WN + 1 only (the
@@ -327,55 +334,55 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 
   // LDS byte offsets (within a stage) of this lane's operands
-  int a_rd[4];
+  int a_rd[MI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_rd[i] = (wm * 128 + i * 32 + lr) * 128;
+  for (int i = 0; i < MI; ++i) a_rd[i] = (wm * 128 + i * 32 + lr) * 128;
   const int a_sw = swz(lr);  // == swz(row) for all four rows
-  int b_rd[4];
+  int b_rd[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = WN * 128 + j * 32 + lr;
+  for (int j = 0; j < NJ; ++j) {
+    const int n = col0 + j * 32 + lr;
     b_rd[j] = A_STAGE + (n * 2 + (lh ^ ((lr >> 3) & 1))) * 16;
   }
 
-  auto read_b = [&](int kt, uint4 (&bw)[4]) {
+  auto read_b = [&](int kt, uint4 (&bw)[NJ]) {
     const uint8_t* st = smem + (kt % NSTAGE) * STAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bw[j] = *reinterpret_cast<const uint4*>(st + b_rd[j]);
+    for (int j = 0; j < NJ; ++j) bw[j] = *reinterpret_cast<const uint4*>(st + b_rd[j]);
   };
   // group scales (and zeros) of this lane's four columns for step kt (raw words)
-  auto read_s = [&](int kt, uint32_t (&sw)[4], uint32_t (&zw)[4]) {
+  auto read_s = [&](int kt, uint32_t (&sw)[NJ], uint32_t (&zw)[NJ]) {
     const uint8_t* st = smem + (kt % NSTAGE) * STAGE + A_STAGE + B_STAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sw[j] = *reinterpret_cast<const uint32_t*>(st + (WN * 128 + j * 32 + lr) * 4);
-      zw[j] = GZ ? *reinterpret_cast<const uint32_t*>(st + S_STAGE + (WN * 128 + j * 32 + lr) * 4) : 0u;
+    for (int j = 0; j < NJ; ++j) {
+      sw[j] = *reinterpret_cast<const uint32_t*>(st + (col0 + j * 32 + lr) * 4);
+      zw[j] = GZ ? *reinterpret_cast<const uint32_t*>(st + S_STAGE + (col0 + j * 32 + lr) * 4) : 0u;
     }
   };
   // word -> float scale and offset term: the scale of column n for group g
   // is the high half when n * groups + g is odd (n and lr share parity)
   const float zb = 128.f + p.zero_const;
-  float gsc[4] = {0.f, 0.f, 0.f, 0.f}, gof[4] = {0.f, 0.f, 0.f, 0.f};
-  auto set_s = [&](int kt, const uint32_t (&sw)[4], const uint32_t (&zw)[4]) {
+  float gsc[NJ], gof[NJ];
+  auto set_s = [&](int kt, const uint32_t (&sw)[NJ], const uint32_t (&zw)[NJ]) {
     const bool hi = (((lr & p.ngroups) ^ (kt >> p.gshift)) & 1) != 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       gsc[j] = __uint_as_float(hi ? (sw[j] & 0xFFFF0000u) : (sw[j] << 16));
       const float z = GZ ? __uint_as_float(hi ? (zw[j] & 0xFFFF0000u) : (zw[j] << 16)) : p.zero_const;
       gof[j] = -z * gsc[j];
     }
   };
-  auto read_a = [&](int kt, int ks, bf16x8 (&af)[4]) {
+  auto read_a = [&](int kt, int ks, bf16x8 (&af)[MI]) {
     const uint8_t* st = smem + (kt % NSTAGE) * STAGE;
     const int chunk = lh * 4 + ks;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
       af[i] = *reinterpret_cast<const bf16x8*>(st + a_rd[i] + ((chunk ^ a_sw) << 4));
   };
-  auto compute = [&](const bf16x8 (&af)[4], const uint4 (&bw)[4], int ks) {
-    bf16x8 bfr[4];
+  auto compute = [&](const bf16x8 (&af)[MI], const uint4 (&bw)[NJ], int ks) {
+    bf16x8 bfr[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
       bfr[j] = unpack8(w, magic_v);
     }
@@ -390,42 +397,38 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
       rsq[ii][3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, rsq[ii][3], false);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-#if WQ_G_SCHED
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
       if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-#endif
   };
   // Group scales: slice ks of the step's B words dequantised ahead of use
   // (dq), so the 16 MFMAs of one slice (mm) overlap the VALU work of the next.
-  auto dq = [&](const uint4 (&bw)[4], int ks, bf16x8 (&bfr)[4]) {
+  auto dq = [&](const uint4 (&bw)[NJ], int ks, bf16x8 (&bfr)[NJ]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
       bfr[j] = unpack8_scaled(w, gsc[j], gof[j]);
     }
   };
-  auto mm = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+  auto mm = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-#if WQ_G_SCHED
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < MI * NJ; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, WQ_G_VPM, 0);  // VALU
-      if (t < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, G_VPM, 0);  // VALU
+      if (t < MI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-#endif
   };
 
   // ---- main loop.  Barrier b(t) publishes stage t (its loads landed) and
@@ -443,12 +446,12 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   wait_vmcnt<LOADS_PER_STAGE>();
   __syncthreads();
   issue_fenced(2, 0, 4);
-  uint4 bw[4];
-  bf16x8 a0[4], a1[4];
+  uint4 bw[NJ];
+  bf16x8 a0[MI], a1[MI];
   read_b(0, bw);
   if constexpr (GS) {
-    uint32_t sw[4], zw[4];
-    bf16x8 b0[4], b1[4];
+    uint32_t sw[NJ], zw[NJ];
+    bf16x8 b0[NJ], b1[NJ];
     read_s(0, sw, zw);
     set_s(0, sw, zw);
     read_a(0, 0, a0);
@@ -491,12 +494,12 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
       wait_vmcnt<LOADS_PER_STAGE>();
       __syncthreads();
       issue_fenced(kt + 3, 0, 4);
-      uint4 bn[4];
+      uint4 bn[NJ];
       read_b(kt + 1, bn);
       read_a(kt + 1, 0, a0);
       compute(a1, bw, 3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bw[j] = bn[j];
+      for (int j = 0; j < NJ; ++j) bw[j] = bn[j];
     }
   }
   wait_vmcnt<0>();  // no load may still be writing LDS below
@@ -515,10 +518,10 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // the accumulator with group scales), bf16 RNE; stage half the tile in
   // LDS, then write it with coalesced 16-byte stores.
   // Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  float sc[4], zc[4];
+  float sc[NJ], zc[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t col = n0 + WN * 128 + j * 32 + lr;
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t col = n0 + col0 + j * 32 + lr;
     sc[j] = GS ? 1.f : (col < p.n ? bf16_to_f32(p.scales[col]) : 0.f);
     zc[j] = (!GS && p.zeros && col < p.n) ? 128.f + bf16_to_f32(p.zeros[col]) : zb;
   }
@@ -526,22 +529,22 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * half + ii;
+    for (int ii = 0; ii < MI / 2; ++ii) {
+      const int i = MI / 2 * half + ii;
       float rsum[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const floatx4 v = GS ? floatx4{0.f, 0.f, 0.f, 0.f}
-                             : *reinterpret_cast<const floatx4*>(&rsx[wm][i][8 * g + 4 * lh]);
+                             : *reinterpret_cast<const floatx4*>(&rsx[wm][i & 3][8 * g + 4 * lh]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) rsum[4 * g + e] = v[e];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = WN * 128 + j * 32 + lr;
+      for (int j = 0; j < NJ; ++j) {
+        const int col = col0 + j * 32 + lr;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          // staged row: 64 wm + 32 ii + local row
+          // staged row: 64 wm + 32 ii + local row (wm = 0 with group scales)
           const int srow = wm * 64 + ii * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
           const float v = GS ? acc[i][j][e] : (acc[i][j][e] - zc[j] * rsum[e]) * sc[j];
           *reinterpret_cast<uint16_t*>(smem + srow * C_PITCH + col * 2) =
@@ -555,7 +558,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
     for (int u = 0; u < 16; ++u) {
       const int q = tid + 256 * u;
       const int srow = q >> 5, cch = q & 31;
-      const int64_t row = m0 + (srow >> 6) * 128 + half * 64 + (srow & 63);
+      const int64_t row = GS ? m0 + half * 128 + srow : m0 + (srow >> 6) * 128 + half * 64 + (srow & 63);
       const int64_t col = n0 + cch * 8;
       if (row >= p.m || col >= p.n) continue;
       const uint4 v = *reinterpret_cast<const uint4*>(smem + srow * C_PITCH + cch * 16);
@@ -576,7 +579,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * stage_bytes<GS, GZ>()];
   __shared__ __attribute__((aligned(16))) float rsx[2][4][32];  // row sums [wm][row block][row]
   // wave-uniform branch (the wave index is moved to a scalar register)
-  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1, GS, GZ>(p, smem, rsx);
+  if constexpr (GS) gemm_tile<0, GS, GZ>(p, smem, rsx);
+  else if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1, GS, GZ>(p, smem, rsx);
   else gemm_tile<0, GS, GZ>(p, smem, rsx);
 }
 
