@@ -66,7 +66,6 @@ template <bool GS, bool GZ> constexpr int stage_bytes() {
 }
 template <bool GS, bool GZ> constexpr int loads_per_stage() { return 10 + (GS ? 1 : 0) + (GZ ? 1 : 0); }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 struct GArgs {
   const uint16_t* a;
@@ -102,40 +101,6 @@ __device__ __forceinline__ bf16x8 unpack8(uint32_t w, uint32_t magic_v) {
   r[2] = and_or(w >> 8, 0x000F000Fu, magic_v);
   r[3] = and_or(w >> 12, 0x000F000Fu, magic_v);
   return __builtin_bit_cast(bf16x8, r);
-}
-
-// Buffer descriptor in SGPRs: raw (stride 0), num_records bytes; offsets at
-// or past num_records read as zero.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_records) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane
-// (lds_base wave-uniform).  Issued from asm so that the compiler does not
-// wait for these loads before every LDS read; completion is awaited with
-// explicit vmcnt waits below.  The compiler's hazard checks do not look
-// inside asm, so the asm keeps its own: one wait state between the M0 write
-// and the LDS-DMA load that reads M0.  (No other code in these kernels uses
-// M0, so clobbering it is safe.)
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// 4 bytes per lane from rsrc + voff into LDS at lds_base + 4 * lane
-__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(lds_base)
-               : "memory", "m0");
 }
 
 // byte b of v as float32: v_cvt_f32_ubyte{0..3} (written out: the compiler
@@ -175,14 +140,6 @@ __device__ __forceinline__ bf16x8 unpack8_scaled(uint32_t w, float s, float c) {
 
 // A-tile swizzle: physical 16-byte column of k-chunk c in row r is c ^ swz(r)
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
-// lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // VALU instructions placed after each MFMA by the scheduling groups with
 // group scales (three: 5% faster than four or two, 8192^3 group 128)
@@ -231,16 +188,16 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   const uint32_t kbytes_b = (uint32_t)(p.k / 2);   // bytes per packed B row
 
   // descriptors over this tile's rows; rows past M / N read as zero
-  const i32x4 ars = make_rsrc(p.a + m0 * p.k, (uint32_t)rows_a * kbytes_a);
-  const i32x4 brs = make_rsrc(p.b + n0 * (p.k / 2), (uint32_t)rows_b * kbytes_b);
+  const intx4 ars = make_rsrc(p.a + m0 * p.k, (uint32_t)rows_a * kbytes_a);
+  const intx4 brs = make_rsrc(p.b + n0 * (p.k / 2), (uint32_t)rows_b * kbytes_b);
   // group scales of this tile's columns, [rows_b][ngroups] bf16.  The range
   // is rounded up to whole 4-byte words: the base is 4-byte aligned, so the
   // word holding the last scale is one the caller's array already touches
   // (and cannot cross a page); the half past the array is never used.
-  const i32x4 srs = make_rsrc(GS ? (const void*)(p.scales + n0 * p.ngroups) : (const void*)p.scales,
+  const intx4 srs = make_rsrc(GS ? (const void*)(p.scales + n0 * p.ngroups) : (const void*)p.scales,
                               GS ? (((uint32_t)rows_b * (uint32_t)p.ngroups * 2u + 3u) & ~3u) : 0u);
   // stored zeros of the groups: the same layout, read the same way
-  const i32x4 zrs = make_rsrc(GZ ? (const void*)(p.zeros + n0 * p.ngroups) : (const void*)p.scales,
+  const intx4 zrs = make_rsrc(GZ ? (const void*)(p.zeros + n0 * p.ngroups) : (const void*)p.scales,
                               GZ ? (((uint32_t)rows_b * (uint32_t)p.ngroups * 2u + 3u) & ~3u) : 0u);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 

@@ -14,6 +14,8 @@
 // the per-block sums of q taken from the int8 data, never from the fp16 s.
 #include "wq_internal.h"
 
+#include <mutex>
+
 #include <algorithm>
 
 namespace wq {
@@ -1020,108 +1022,182 @@ __global__ __launch_bounds__(256, SB ? TP_WAVES_SB : TP_WAVES) void k_gemv_terna
   }
 }
 
-// ---- ternary x q8_1 GEMM on the int8 matrix cores (64 or more columns)
+// ---- ternary x q8_1 GEMM on the fp4 x fp8 matrix cores (64 or more columns)
 //
 // y[c][r] = sum_b d_w[r][b] sum_j d_x[c][4b + j] S[c][r][b][j] with the
-// exact sub-block sums S = sum_i t q over 32 k.  One v_mfma_i32_32x32x32_i8
-// covers exactly one 32-k q8_1 block, so it yields S for a 32 x 32 tile in
-// int32; the weights are the A operand (rows r) and x the B operand (columns
-// c), so the x scale of a result is the same for a whole lane (its column)
-// and is applied right after each product (a convert and an FMA per result:
-// the per-32 activation scales keep this path VALU-heavy), the weight scale
-// once per 128-k block.
+// exact sub-block sums S = sum_i t q over 32 k.  The products run on
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales: a trit is exact in
+// fp4 (e2m1: +-1 and 0) and an activation q = 16 qh + ql (qh = q >> 4 in
+// -8..7, ql = q & 15) is the exact fp8 (e4m3) pair (ql, 16 qh), so one
+// product over 64 k slots -- each k twice, once against ql and once against
+// 16 qh -- sums one 32-k sub-block: S comes out of the float32 accumulator
+// exactly (integers below 2^13), as float, so the VALU only multiplies by
+// d_x (one FMA per result and sub-block; int8 products need a convert as
+// well) and by d_w once per 128-k block.
 //
-// A 512-lane workgroup computes a 256 (r) x 128 (c) tile, a wave 64 x 64 (2 x
-// 2 products per 32 k; two waves per SIMD keep a wave within the 256 VGPRs
-// the VALU can address).  Per 128-k step lanes 0..255 each decode the block
-// of one weight row into int8 trits (the GEMV's table decode, then u - 1)
-// and lanes 256..383 each copy the four q8_1 blocks of one x row, into LDS
-// rows padded to 144 bytes (the 16 rows a ds_read_b128 cycle serves fall in
-// distinct bank quads); waves w and w + 4 share a SIMD, so every SIMD holds
-// one decoding wave.  Two LDS stages: step t + 1 is decoded and stored while step t
-// multiplies, with one barrier per step, and the global words of step t + 2
-// are loaded into registers meanwhile.
-constexpr int TG_BN = 256;     // weight rows per tile
-constexpr int TG_BM = 128;     // x rows per tile
-constexpr int TG_PITCH = 144;  // LDS bytes per operand row: 128 k + 16
-constexpr int TG_WST = TG_BN * TG_PITCH;  // bytes per weight stage
-constexpr int TG_XST = TG_BM * TG_PITCH;  // bytes per x stage
+// Two kernels first unpack the operands into a workspace: the PTQ1_0 blocks
+// into one byte per k (the fp4 pair (t, t)) and a float d_w per block, x
+// into two bytes per k and a float d_x per block.  The GEMM kernel then
+// streams both with buffer loads that write LDS directly (no registers,
+// no decode in the product loop): a 512-lane workgroup computes a 256 (r) x
+// 128 (c) tile, a wave 64 x 64 (2 x 2 products per sub-block, two waves per
+// SIMD), K advancing 128 per step through a two-stage LDS ring (68 KiB per
+// stage) with one barrier per step; each step's ten loads per lane are
+// spread over the first five of its eight product groups.  Per group the
+// products of the next one are issued before the current sums are scaled
+// (software pipeline), their operand reads first and part of the VALU work
+// in between, so the matrix cores run while the VALU scales.
+//
+// Operand layout of the product (checked on the device against a host
+// reference): lane l holds row / column l % 32; A's 32 fp4 k slots of lane
+// half h are slots 32 h + i, B's 32 fp8 bytes of half h pair with A's slots
+// 16 h + i (i < 16) and 32 + 16 h + (i - 16).  So a lane half takes 16
+// consecutive weight bytes (k 16 h .. 16 h + 15 of the sub-block) and the x
+// bytes of k 8 h .. 8 h + 7 and 16 + 8 h .. 16 + 8 h + 7 (16-byte chunks h and
+// 2 + h of the sub-block's 64 x bytes).
 
-__global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restrict__ w,
-                                                         const uint8_t* __restrict__ xq,
+// PTQ1_0 blocks -> fp4 trit pairs [n][k] (one byte per k) and float block
+// scales [n][k/128]: one lane per block
+__global__ __launch_bounds__(256) void k_unpack_ptq1_0_fp4(const uint32_t* __restrict__ w, int64_t nb,
+                                                           uint4* __restrict__ t4, float* __restrict__ dw) {
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * LUT_COPIES];
+  tern_lut_init(lut);
+  __syncthreads();
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nb) return;
+  uint32_t v[7];
+#pragma unroll
+  for (int q = 0; q < 7; ++q) v[q] = w[b * 7 + q];
+  uint32_t dg[32];
+  tern_decode(v, lut + (threadIdx.x & (LUT_COPIES - 1)), dg);
+  // digit u -> the fp4 (e2m1) pair (t, t) of t = u - 1: 0xAA, 0x00, 0x22
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = __builtin_amdgcn_perm(0u, 0x002200AAu, dg[4 * i + e]);
+    t4[b * 8 + i] = make_uint4(t[0], t[1], t[2], t[3]);
+  }
+  dw[b] = f16_to_f32(v[6] >> 16);
+}
+
+// block_q8_1 -> fp8 pairs [c][2k] and float d_x [c][k/32]: one lane per block
+__global__ __launch_bounds__(256) void k_unpack_q8_1_fp8(const uint32_t* __restrict__ xq, int64_t nb,
+                                                         uint4* __restrict__ q8, float* __restrict__ dx) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nb) return;
+  uint32_t v[9];
+#pragma unroll
+  for (int q = 0; q < 9; ++q) v[q] = xq[b * 9 + q];
+  // k takes the fp8 (e4m3) pair (ql, 16 qh), both exact (the hardware's own
+  // conversion, so the encoding is the one the products read)
+  uint32_t o[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q0 = (int)(int8_t)(v[1 + i] >> (16 * h)), q1 = (int)(int8_t)(v[1 + i] >> (16 * h + 8));
+      int w2 = __builtin_amdgcn_cvt_pk_fp8_f32((float)(q0 & 15), (float)((q0 >> 4) * 16), 0, false);
+      w2 = __builtin_amdgcn_cvt_pk_fp8_f32((float)(q1 & 15), (float)((q1 >> 4) * 16), w2, true);
+      o[2 * i + h] = (uint32_t)w2;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q8[b * 4 + i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  dx[b] = f16_to_f32(v[0] & 0xFFFFu);
+}
+
+constexpr int TG_BN = 256, TG_BM = 128;  // weight rows, x rows per tile; 128 k per step
+constexpr int TG_A = TG_BN * 128;        // 32 KiB of fp4 trit pairs
+constexpr int TG_B = TG_BM * 128 * 2;    // 32 KiB of fp8 (ql, 16 qh) pairs
+constexpr int TG_DX = TG_BM * 16;        // 4 d_x per x row
+constexpr int TG_DW = 512 * 4;           // 256 d_w (and 256 unused words)
+constexpr int TG_STAGE = TG_A + TG_B + TG_DX + TG_DW;
+constexpr int TG_NST = 2;
+// VALU instructions of a group's scaling placed before its first and second
+// product (the rest after; 8 and 24 were best of 0-32)
+constexpr int TG_V1 = 8, TG_V2 = 24;
+// 16-byte chunk c of weight row r sits at chunk c ^ tg_swz(r) (and of x row r
+// at c ^ (r % 16)): the 16 rows one ds_read_b128 cycle serves fall in 16
+// distinct bank groups
+__device__ __forceinline__ int tg_swz(int r) { return (r >> 1) & 7; }
+
+// Workspace layout (byte offsets, 256-aligned) for the unpacked operands.
+struct TernWs {
+  size_t dw, x, dx, bytes;
+};
+inline TernWs tern_ws(int64_t n, int64_t k, int64_t c) {
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  TernWs w;
+  w.dw = al((size_t)(n * k));
+  w.x = w.dw + al((size_t)(n * (k / 128) * 4));
+  w.dx = w.x + al((size_t)(c * k * 2));
+  w.bytes = w.dx + al((size_t)(c * (k / 32) * 4));
+  return w;
+}
+
+__global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint8_t* __restrict__ wt,
+                                                         const float* __restrict__ dwf,
+                                                         const uint8_t* __restrict__ xt,
+                                                         const float* __restrict__ dxf,
                                                          float* __restrict__ out, int n, int k,
                                                          int m, int tiles_m) {
-  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * LUT_COPIES];
-  __shared__ __attribute__((aligned(16))) uint8_t wt[2 * TG_WST];
-  __shared__ __attribute__((aligned(16))) uint8_t xt[2 * TG_XST];
-  __shared__ __attribute__((aligned(16))) float dws[2 * TG_BN];
-  __shared__ __attribute__((aligned(16))) float dxs[2 * TG_BM * 4];
-
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[TG_NST * TG_STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1, wm = wave & 1;  // the wave's 64 weight rows, 64 x rows
   const int bpr = k / 128, nsb = k / 32;
   const int tm = (int)blockIdx.x % tiles_m, tn = (int)blockIdx.x / tiles_m;
   const int n0 = tn * TG_BN, m0 = tm * TG_BM;
-
-  // lanes 0..255: weight row n0 + t (one 28-byte block per step); lanes
-  // 256..383: x row m0 + t - 256 (four 36-byte blocks per step: 144
-  // contiguous bytes, 16-byte aligned since a row is k / 32 * 36 bytes, a
-  // multiple of 144)
-  const bool wl = tid < TG_BN;
-  const bool xl = tid >= TG_BN && tid < TG_BN + TG_BM;
-  const int wrow = n0 + tid, xrow = m0 + tid - TG_BN;
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)w, 0, (int)((int64_t)n * bpr * PT_BYTES), 0x00020000);
-  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)xq, 0, (int)((int64_t)m * nsb * Q8_BYTES), 0x00020000);
-  uint32_t pw[7], px[36];
-  auto fetch = [&](int kb) {  // global words of step kb
-    if (wl) {
-      const uint32_t ow = wrow < n ? (uint32_t)((wrow * bpr + kb) * PT_BYTES) : T_OOB;
+  const int rows_a = min(TG_BN, n - n0), rows_b = min(TG_BM, m - m0);
+  // descriptors over this tile's rows; rows past n / m read as zero
+  const intx4 ars = make_rsrc(wt + (int64_t)n0 * k, (uint32_t)rows_a * (uint32_t)k);
+  const intx4 brs = make_rsrc(xt + (int64_t)m0 * 2 * k, (uint32_t)rows_b * (uint32_t)k * 2u);
+  const intx4 xds = make_rsrc(dxf + (int64_t)m0 * nsb, (uint32_t)rows_b * (uint32_t)nsb * 4u);
+  const intx4 wds = make_rsrc(dwf + (int64_t)n0 * bpr, (uint32_t)rows_a * (uint32_t)bpr * 4u);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  // Loads of a step: 0..3 weights (16-byte slot s = 64 (8 i + wave) + lane:
+  // row s / 8, stored chunk s % 8), 4..7 x (row s / 16, stored chunk s % 16),
+  // 8 the d_x (word t: row t / 4, sub-block t % 4), 9 the d_w (row t < 256)
+  uint32_t a_voff[4], b_voff[4];
 #pragma unroll
-      for (int q = 0; q < 7; ++q) pw[q] = __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)(ow + 4 * q), 0, 0);
-    }
-    if (xl) {
-      const uint32_t ox = xrow < m ? (uint32_t)((xrow * nsb + 4 * kb) * Q8_BYTES) : T_OOB;
+  for (int i = 0; i < 4; ++i) {
+    const int s = (i * 8 + wave) * 64 + lane, r = s >> 3;
+    a_voff[i] = (uint32_t)r * (uint32_t)k + 16u * (uint32_t)((s & 7) ^ tg_swz(r));
+  }
 #pragma unroll
-      for (int q = 0; q < 9; ++q) {
-        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(ox + 16 * q), 0, 0));
-        px[4 * q] = v.x; px[4 * q + 1] = v.y; px[4 * q + 2] = v.z; px[4 * q + 3] = v.w;
-      }
-    }
-  };
-  auto put = [&](int st) {  // registers -> LDS stage st
-    if (wl) {
-      uint32_t dg[32];
-      tern_decode(pw, lut + (lane & (LUT_COPIES - 1)), dg);
-      uint4* dst = reinterpret_cast<uint4*>(wt + st * TG_WST + tid * TG_PITCH);
+  for (int i = 0; i < 4; ++i) {
+    const int s = (i * 8 + wave) * 64 + lane, r = s >> 4;
+    b_voff[i] = (uint32_t)r * (uint32_t)k * 2u + 16u * (uint32_t)((s & 15) ^ (r & 15));
+  }
+  const uint32_t dx_voff = (uint32_t)((tid >> 2) * nsb + (tid & 3)) * 4u;
+  const uint32_t dw_voff = tid < TG_BN ? (uint32_t)(tid * bpr) * 4u : T_OOB;
+  // Loads [first, last) of step kt into stage kt % 2.  Steps past the end
+  // load at T_OOB (zeros into a stage no one reads), so every lane issues
+  // ten loads per step and the vmcnt waits below hold.
+  auto issue_part = [&](int kt, int first, int last) {
+    const uint32_t st = lds0 + (uint32_t)(kt % TG_NST) * TG_STAGE;
+    const bool live = kt < bpr;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // digits u in {0,1,2} per byte -> trits u - 1 (no carries: u + 0x7F <= 0x81)
-        uint32_t t[4];
+    for (int i = 0; i < 4; ++i)
+      if (i >= first && i < last)
+        dma16(ars, live ? a_voff[i] + (uint32_t)kt * 128u : T_OOB,
+              __builtin_amdgcn_readfirstlane(st + (uint32_t)(i * 8 + wave) * 1024u));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = (dg[4 * i + e] + 0x7F7F7F7Fu) ^ 0x80808080u;
-        dst[i] = make_uint4(t[0], t[1], t[2], t[3]);
-      }
-      dws[st * TG_BN + tid] = f16_to_f32(pw[6] >> 16);  // 0 for rows past n (zero block)
-    }
-    if (xl) {
-      const int xr = tid - TG_BN;
-      uint4* xd = reinterpret_cast<uint4*>(xt + st * TG_XST + xr * TG_PITCH);
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        xd[2 * sb] = make_uint4(px[9 * sb + 1], px[9 * sb + 2], px[9 * sb + 3], px[9 * sb + 4]);
-        xd[2 * sb + 1] = make_uint4(px[9 * sb + 5], px[9 * sb + 6], px[9 * sb + 7], px[9 * sb + 8]);
-        dxs[st * TG_BM * 4 + xr * 4 + sb] = f16_to_f32(px[9 * sb] & 0xFFFFu);
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      if (4 + i >= first && 4 + i < last)
+        dma16(brs, live ? b_voff[i] + (uint32_t)kt * 256u : T_OOB,
+              __builtin_amdgcn_readfirstlane(st + TG_A + (uint32_t)(i * 8 + wave) * 1024u));
+    if (8 >= first && 8 < last)
+      dma4(xds, live ? dx_voff + (uint32_t)kt * 16u : T_OOB,
+           __builtin_amdgcn_readfirstlane(st + TG_A + TG_B + (uint32_t)wave * 256u));
+    if (9 >= first && 9 < last)
+      dma4(wds, live && dw_voff != T_OOB ? dw_voff + (uint32_t)kt * 4u : T_OOB,
+           __builtin_amdgcn_readfirstlane(st + TG_A + TG_B + TG_DX + (uint32_t)wave * 256u));
   };
 
-  typedef float f32x16 __attribute__((ext_vector_type(16)));
-  typedef int i32x16 __attribute__((ext_vector_type(16)));
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  f32x16 acc[2][2];
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  floatx16 acc[2][2];
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -1130,65 +1206,95 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restr
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
   const int l32 = lane & 31, lh = lane >> 5;
 
-  // Per row block bi: its 8 products (sub-block j, column block bj) with
-  // the x scale applied to each product's int32 sums, then the weight scales
-  // of its rows.  The j loop is unrolled by two only, so at most four
-  // products' sums are live (fully unrolled, the compiler issued all 16
-  // products of a step at once and spilled their results; by two it saves
-  // address arithmetic, 1.19 -> 1.14 ms at 4096 x 17280 x 5120).
-  auto compute = [&](int st) {
-    const uint8_t* ws = wt + st * TG_WST;
-    const uint8_t* xs = xt + st * TG_XST;
-    const uint8_t* wrow0 = ws + (wn * 64 + l32) * TG_PITCH + 16 * lh;
-    const uint8_t* xcol0 = xs + (wm * 64 + l32) * TG_PITCH + 16 * lh;
-    const float* dxc = dxs + st * TG_BM * 4 + (wm * 64 + l32) * 4;
+  // Step kt from stage kt % 2, while step kn's loads go out.  Product group
+  // nn = 4 bi + j: row block bi, sub-block j, both column blocks.
+  auto compute = [&](int kt, int kn) {
+    const uint8_t* st = smem + (kt % TG_NST) * TG_STAGE;
+    const int ra = wn * 64 + l32, rb = wm * 64 + l32;  // + 32 bi / + 32 bj (same swizzles)
+    const int sa = tg_swz(ra), sbx = rb & 15;
+    const float4 dxa = *reinterpret_cast<const float4*>(st + TG_A + TG_B + rb * 16);
+    const float4 dxb = *reinterpret_cast<const float4*>(st + TG_A + TG_B + (rb + 32) * 16);
+    const float dx[2][4] = {{dxa.x, dxa.y, dxa.z, dxa.w}, {dxb.x, dxb.y, dxb.z, dxb.w}};
+    floatx16 sp[2][2];  // sums of group nn (slot nn % 2), column blocks 0 and 1
+    floatx16 t[2];      // the row block's d_x-scaled sums over its sub-blocks so far
+    intx4 opa;
+    i32x8 opb[2];
+    auto load = [&](int nn) {
+      const int bi = nn >> 2, j = nn & 3, c = 2 * j + lh;
+      opa = *reinterpret_cast<const intx4*>(st + (ra + 32 * bi) * 128 + ((c ^ sa) << 4));
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      f32x16 t0, t1;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) t0[e] = t1[e] = 0.f;
-#pragma unroll 2
-      for (int j = 0; j < 4; ++j) {  // 32-k sub-block: one q8_1 block of every column
-        const i32x4 af = *reinterpret_cast<const i32x4*>(wrow0 + bi * 32 * TG_PITCH + 32 * j);
-        const i32x4 b0 = *reinterpret_cast<const i32x4*>(xcol0 + 32 * j);
-        const i32x4 b1 = *reinterpret_cast<const i32x4*>(xcol0 + 32 * TG_PITCH + 32 * j);
-        const float dx0 = dxc[j], dx1 = dxc[32 * 4 + j];
-        const i32x16 z = {};
-        const i32x16 s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b0, z, 0, 0, 0);
-        const i32x16 s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b1, z, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) t0[e] = fmaf(dx0, (float)s0[e], t0[e]);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) t1[e] = fmaf(dx1, (float)s1[e], t1[e]);
+      for (int bj = 0; bj < 2; ++bj) {
+        const uint8_t* row = st + TG_A + (rb + 32 * bj) * 256;
+        const intx4 lo = *reinterpret_cast<const intx4*>(row + (((4 * j + lh) ^ sbx) << 4));
+        const intx4 hi = *reinterpret_cast<const intx4*>(row + (((4 * j + 2 + lh) ^ sbx) << 4));
+        opb[bj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      // weight scales of this lane's 16 result rows (8 (e / 4) + 4 lh + e % 4)
+    };
+    auto prod = [&](int nn) {
+      const floatx16 z = {};
+      const i32x8 a8 = __builtin_shufflevector(opa, opa, 0, 1, 2, 3, 0, 1, 2, 3);  // fp4: 4 words read
+      // A fp4 (e2m1, cbsz 4), B fp8 (e4m3, blgp 0), block scales 2^0 (E8M0 127)
+      sp[nn & 1][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, opb[0], z, 4, 0, 0, 0x7f, 0, 0x7f);
+      sp[nn & 1][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, opb[1], z, 4, 0, 0, 0x7f, 0, 0x7f);
+    };
+    auto scale = [&](int nn) {
+      const int j = nn & 3;
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          t[bj][e] = j == 0 ? dx[bj][j] * sp[nn & 1][bj][e] : fmaf(dx[bj][j], sp[nn & 1][bj][e], t[bj][e]);
+    };
+    auto finish = [&](int bi) {  // weight scales of this lane's 16 result rows (8 (e / 4) + 4 lh + e % 4)
       float dw[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 v = *reinterpret_cast<const float4*>(dws + st * TG_BN + wn * 64 + bi * 32 + 8 * g + 4 * lh);
+        const float4 v = *reinterpret_cast<const float4*>(st + TG_A + TG_B + TG_DX + (wn * 64 + bi * 32 + 8 * g + 4 * lh) * 4);
         dw[4 * g] = v.x; dw[4 * g + 1] = v.y; dw[4 * g + 2] = v.z; dw[4 * g + 3] = v.w;
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        acc[bi][0][e] = fmaf(dw[e], t0[e], acc[bi][0][e]);
-        acc[bi][1][e] = fmaf(dw[e], t1[e], acc[bi][1][e]);
+        acc[bi][0][e] = fmaf(dw[e], t[0][e], acc[bi][0][e]);
+        acc[bi][1][e] = fmaf(dw[e], t[1][e], acc[bi][1][e]);
+      }
+    };
+    load(0);
+    prod(0);
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) {
+      // The memory clobber keeps group nn + 1's operand reads (and so its
+      // products) in this region; the asm that takes t keeps the scaling of
+      // nn here too (the compiler otherwise sank it below every product).
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (nn < 7) { load(nn + 1); prod(nn + 1); }
+      scale(nn);
+      asm volatile("" ::"v"(t[0]), "v"(t[1]));
+      if ((nn & 3) == 3) finish(nn >> 2);
+      if (nn < 7) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);      // the operand reads
+        __builtin_amdgcn_sched_group_barrier(0x002, TG_V1, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one product
+        __builtin_amdgcn_sched_group_barrier(0x002, TG_V2, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // the other
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
+      if (nn < 5) {  // two of the next step's ten loads per group
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(kn, 2 * nn, 2 * nn + 2);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  fetch(0);
-  if (tid < 256) tern_lut_init(lut);
+  asm volatile("s_nop 4");  // VALU-written SGPRs (descriptors) read by the first loads
+  issue_part(0, 0, 10);
+  wait_vmcnt<0>();
   __syncthreads();
-  put(0);
-  if (bpr > 1) fetch(1);
-  __syncthreads();
-  for (int kb = 0; kb < bpr; ++kb) {
-    compute(kb & 1);
-    if (kb + 1 < bpr) {
-      put((kb + 1) & 1);  // the other stage: every wave finished step kb - 1 at the last barrier
-      if (kb + 2 < bpr) fetch(kb + 2);
-    }
-    __syncthreads();
+  for (int kt = 0; kt < bpr; ++kt) {
+    compute(kt, kt + 1);  // step kt + 1 into the other stage: every wave finished step kt - 1
+    wait_vmcnt<0>();      // this lane's loads of step kt + 1 landed
+    __syncthreads();      // all lanes': publishes stage kt + 1, frees stage kt
   }
 
   // y[c][r]: lane column c, rows r = 8 (e / 4) + 4 lh + e % 4 (four consecutive)
@@ -1203,7 +1309,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ternary(const uint32_t* __restr
       for (int g = 0; g < 4; ++g) {
         const int r = n0 + wn * 64 + bi * 32 + 8 * g + 4 * lh;
         float* dst = out + (int64_t)col * n + r;
-        const f32x16& a = acc[bi][bj];
+        const floatx16& a = acc[bi][bj];
         if (vec_ok && r + 3 < n) {
           *reinterpret_cast<float4*>(dst) = make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         } else {
@@ -1375,13 +1481,70 @@ hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n,
 }
 
 
+size_t gemm_ternary_workspace(int64_t n, int64_t k, int64_t c) { return tern_ws(n, k, c).bytes; }
+
+hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
+                               float* out, void* ws, hipStream_t s) {
+  const TernWs L = tern_ws(n, k, c);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const int64_t nbw = n * (k / 128), nbx = c * (k / 32);
+  hipLaunchKernelGGL(k_unpack_ptq1_0_fp4, dim3((unsigned)((nbw + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(w), nbw, reinterpret_cast<uint4*>(base),
+                     reinterpret_cast<float*>(base + L.dw));
+  hipLaunchKernelGGL(k_unpack_q8_1_fp8, dim3((unsigned)((nbx + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(xq), nbx, reinterpret_cast<uint4*>(base + L.x),
+                     reinterpret_cast<float*>(base + L.dx));
+  const int tiles_m = (int)((c + TG_BM - 1) / TG_BM), tiles_n = (int)((n + TG_BN - 1) / TG_BN);
+  hipLaunchKernelGGL(k_gemm_ternary, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s, base,
+                     reinterpret_cast<const float*>(base + L.dw), base + L.x,
+                     reinterpret_cast<const float*>(base + L.dx), out, (int)n, (int)k, (int)c, tiles_m);
+  return hipGetLastError();
+}
+
+// The GEMM's workspace comes from a memory pool of this library's own, one
+// per device, allocated and freed in stream order around each call; its
+// release threshold is at the maximum, so what a call frees stays in the
+// pool for the next one.
+static hipError_t tern_pool(hipMemPool_t* pool) {
+  static std::mutex mu;
+  static hipMemPool_t pools[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!pools[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    e = hipMemPoolCreate(&p, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(p);
+      return e;
+    }
+    pools[dev] = p;
+  }
+  *pool = pools[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s) {
-  if (c >= 64) {  // a batch wide enough for the int8 matrix cores
-    const int tiles_m = (int)((c + TG_BM - 1) / TG_BM), tiles_n = (int)((n + TG_BN - 1) / TG_BN);
-    hipLaunchKernelGGL(k_gemm_ternary, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s,
-                       reinterpret_cast<const uint32_t*>(w), xq, out, (int)n, (int)k, (int)c, tiles_m);
-    return hipGetLastError();
+  if (c >= 64) {  // a batch wide enough for the matrix cores
+    hipMemPool_t pool = nullptr;
+    hipError_t e = tern_pool(&pool);
+    if (e != hipSuccess) return e;
+    void* ws = nullptr;
+    e = hipMallocFromPoolAsync(&ws, gemm_ternary_workspace(n, k, c), pool, s);
+    if (e != hipSuccess) return e;
+    e = launch_gemm_ternary(w, xq, n, k, c, out, ws, s);
+    const hipError_t f = hipFreeAsync(ws, s);
+    return e != hipSuccess ? e : f;
   }
   // 17..63 columns: passes of at most 16 over x[c0:c0+16] -> out[c0:c0+16]
   for (int64_t c0 = 0; c0 < c; c0 += 16) {

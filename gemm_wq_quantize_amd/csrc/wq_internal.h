@@ -34,6 +34,50 @@ __device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// ---- Global -> LDS loads that bypass registers (buffer_load ... lds).
+
+// Buffer descriptor in SGPRs: raw (stride 0), num_records bytes; offsets at
+// or past num_records read as zero.
+__device__ __forceinline__ intx4 make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  intx4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at lds_base + 16 * lane
+// (lds_base wave-uniform).  Issued from asm so that the compiler does not
+// wait for these loads before every LDS read; completion is awaited with
+// explicit vmcnt waits (wait_vmcnt).  The compiler's hazard checks do not look
+// inside asm, so the asm keeps its own: one wait state between the M0 write
+// and the LDS-DMA load that reads M0.  (No other code in the kernels that use
+// these loads uses M0, so clobbering it is safe.)
+__device__ __forceinline__ void dma16(intx4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// 4 bytes per lane from rsrc + voff into LDS at lds_base + 4 * lane
+__device__ __forceinline__ void dma4(intx4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Host-side per-device caches.  Each entry is an atomic, so concurrent first
 // calls from several host threads are well defined (at worst both query the
 // runtime and store the same value).
@@ -96,6 +140,11 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x
                                 hipStream_t s);
 hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s);
+// The c >= 64 product with a caller-provided workspace of
+// gemm_ternary_workspace(n, k, c) bytes (256-byte aligned).
+size_t gemm_ternary_workspace(int64_t n, int64_t k, int64_t c);
+hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
+                               float* out, void* ws, hipStream_t s);
 hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, const int32_t* esc_idx,
                                   const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq,
                                   int64_t n, int64_t k, int64_t c, float* out, hipStream_t s);

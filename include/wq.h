@@ -207,10 +207,14 @@ int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* 
  * Requires c >= 0 (0 is a no-op), k % 128 == 0, w_blocks and x_q8 4-byte
  * aligned, out 4-byte aligned (16-byte for c >= 64).  Up to 16 columns run
  * on the vector units; 17 <= c <= 63 runs as passes of at most 16 columns.
- * c >= 64 (a prefill batch) runs on the int8 matrix cores
- * (v_mfma_i32_32x32x32_i8: one product per 32-k activation block, so S is
- * still exact in int32); it also requires n * k / 128 * 28 and c * k / 32 * 36
- * below 2^31 (32-bit offsets).
+ * c >= 64 (a prefill batch) runs on the fp4 x fp8 matrix cores: trits are
+ * exact in fp4 and each q is the exact fp8 pair (q & 15, 16 (q >> 4)), so one
+ * v_mfma_scale_f32_32x32x64_f8f6f4 product per 32-k activation block gives S
+ * exactly.  That path first unpacks both operands into a workspace of about
+ * n k + 2 c k bytes, allocated and freed in stream order from a memory pool
+ * the library keeps per device (what a call frees stays in the pool); an
+ * allocation failure is WQ_EHIP.  It also requires n * k / 128 * 28 and
+ * c * k / 32 * 36 below 2^31.
  */
 int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k,
                     int64_t c, float* out, void* stream);
