@@ -33,6 +33,7 @@ _SIGS = {
     "wq_pack_ptq1_0": ([_p, _p, _i64, _i64, _p, _p], _i),
     "wq_quantize_q8_1": ([_p, _i64, _i64, _p, _p], _i),
     "wq_gemv_ternary": ([_p, _p, _i64, _i64, _i64, _p, _p], _i),
+    "wq_gemv_ternary_noalloc": ([_p, _p, _i64, _i64, _i64, _p, _p], _i),
     "wq_ptq1_1_encode": ([_p, _i64, _i64, _p, _p, _p, _p, _i64, _p], _i),
     "wq_gemv_ternary_ptq1_1": ([_p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _p], _i),
     # calibration kernels (include/wq_peaks.h)
@@ -223,18 +224,33 @@ def wq_quantize_q8_1(x, x_q8, stream=None):
                                                     _sptr(st)))
 
 
-def wq_gemv_ternary(w_blocks, x_q8, k, out, stream=None):
-    """out fp32 [c][n] from PTQ1_0 weights [n][k/128][28] and q8_1 x [c][k/32][36]."""
+def _ternary_args(w_blocks, x_q8, k, out):
     n = w_blocks.shape[0]
     c = x_q8.shape[0]
     _require(w_blocks.dtype == torch.uint8 and x_q8.dtype == torch.uint8, "blocks are uint8")
     _require(w_blocks.numel() == n * (k // 128) * 28 and x_q8.numel() == c * (k // 32) * 36,
              "w_blocks [n][k/128][28], x_q8 [c][k/32][36]")
     _require(out.dtype == torch.float32 and out.numel() == c * n, "out is fp32 [c][n]")
+    return n, c
+
+
+def wq_gemv_ternary(w_blocks, x_q8, k, out, stream=None):
+    """out fp32 [c][n] from PTQ1_0 weights [n][k/128][28] and q8_1 x [c][k/32][36]."""
+    n, c = _ternary_args(w_blocks, x_q8, k, out)
     st = _stream(stream)
     d = st.device
     _check("wq_gemv_ternary",
            lib.wq_gemv_ternary(_ptr(w_blocks, d), _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
+
+
+def wq_gemv_ternary_noalloc(w_blocks, x_q8, k, out, stream=None):
+    """wq_gemv_ternary with no device allocation (workspace in the library's
+    static scratch; a larger workspace raises)."""
+    n, c = _ternary_args(w_blocks, x_q8, k, out)
+    st = _stream(stream)
+    d = st.device
+    _check("wq_gemv_ternary_noalloc",
+           lib.wq_gemv_ternary_noalloc(_ptr(w_blocks, d), _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
 
 
 def wq_ptq1_1_encode(blocks):

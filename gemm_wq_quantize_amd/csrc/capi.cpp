@@ -55,6 +55,27 @@ int gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* 
   return hip_status(wq::launch_gemm_w4a16(a, b, scales, zeros, group, zero_const, m, n, k, c_out,
                                           as_stream(stream)));
 }
+// shared validation of the two ternary GEMV entry points; *launch is false
+// for an empty problem (WQ_OK, nothing to enqueue)
+int check_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k, int64_t c,
+                       const float* out, bool* launch) {
+  *launch = false;
+  if (n < 0 || k < 0 || c < 0) return WQ_EINVAL;
+  if (n == 0 || c == 0) return WQ_OK;
+  if (!w_blocks || !x_q8 || !out) return WQ_EINVAL;
+  // up to 16 columns per pass on the vector units; 64 or more on the fp4 x fp8 matrix cores
+  if (k == 0 || k % 128 != 0) return WQ_ESHAPE;
+  if (!aligned(w_blocks, 4) || !aligned(x_q8, 4) || !aligned(out, c >= 64 ? 16 : 4)) return WQ_EALIGN;
+  if (n / 32 + 1 > kMaxGrid) return WQ_ESHAPE;
+  if (c >= 64) {  // 32-bit buffer offsets and the tile grid
+    if (mul_sat(mul_sat(n, k / 128), 28) >= (int64_t(1) << 31) ||
+        mul_sat(mul_sat(c, k / 32), 36) >= (int64_t(1) << 31))
+      return WQ_ESHAPE;
+    if (mul_sat(c / 128 + 1, n / 128 + 1) > kMaxGrid) return WQ_ESHAPE;
+  }
+  *launch = true;
+  return WQ_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -168,22 +189,22 @@ int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* 
   return hip_status(wq::launch_quantize_q8_1(x, c, k, x_q8, as_stream(stream)));
 }
 
+
 int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k, int64_t c,
                     float* out, void* stream) {
-  if (n < 0 || k < 0 || c < 0) return WQ_EINVAL;
-  if (n == 0 || c == 0) return WQ_OK;
-  if (!w_blocks || !x_q8 || !out) return WQ_EINVAL;
-  // up to 16 columns per pass on the vector units; 64 or more on the int8 matrix cores
-  if (k == 0 || k % 128 != 0) return WQ_ESHAPE;
-  if (!aligned(w_blocks, 4) || !aligned(x_q8, 4) || !aligned(out, c >= 64 ? 16 : 4)) return WQ_EALIGN;
-  if (n / 32 + 1 > kMaxGrid) return WQ_ESHAPE;
-  if (c >= 64) {  // 32-bit buffer offsets and the tile grid
-    if (mul_sat(mul_sat(n, k / 128), 28) >= (int64_t(1) << 31) ||
-        mul_sat(mul_sat(c, k / 32), 36) >= (int64_t(1) << 31))
-      return WQ_ESHAPE;
-    if (mul_sat(c / 128 + 1, n / 128 + 1) > kMaxGrid) return WQ_ESHAPE;
-  }
+  bool launch = false;
+  const int v = check_gemv_ternary(w_blocks, x_q8, n, k, c, out, &launch);
+  if (v != WQ_OK || !launch) return v;
   return hip_status(wq::launch_gemv_ternary(w_blocks, x_q8, n, k, c, out, as_stream(stream)));
+}
+
+int wq_gemv_ternary_noalloc(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k,
+                            int64_t c, float* out, void* stream) {
+  bool launch = false;
+  const int v = check_gemv_ternary(w_blocks, x_q8, n, k, c, out, &launch);
+  if (v != WQ_OK || !launch) return v;
+  if (c >= 64 && wq::gemm_ternary_workspace(n, k, c) > wq::kTernScratchBytes) return WQ_ESHAPE;
+  return hip_status(wq::launch_gemv_ternary_noalloc(w_blocks, x_q8, n, k, c, out, as_stream(stream)));
 }
 
 int wq_gemv_ternary_ptq1_1(const uint8_t* superblocks, const uint8_t* codebook,

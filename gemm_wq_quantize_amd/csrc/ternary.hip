@@ -1533,6 +1533,40 @@ static hipError_t tern_pool(hipMemPool_t* pool) {
   return hipSuccess;
 }
 
+// Scratch of the entry point that allocates nothing: the GEMM's unpacked
+// operands, at most kTernScratchBytes.  Every device holds its own copy for
+// the life of the process.  In host code `scratch` names a host-side stand-in;
+// its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kTernScratchBytes];
+
+static hipError_t scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with this device current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_gemv_ternary_noalloc(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
+                                       int64_t c, float* out, hipStream_t s) {
+  if (c < 64) return launch_gemv_ternary(w, xq, n, k, c, out, s);  // no workspace below 64 columns
+  if (gemm_ternary_workspace(n, k, c) > kTernScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_gemm_ternary(w, xq, n, k, c, out, ws, s);
+}
+
 hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s) {
   if (c >= 64) {  // a batch wide enough for the matrix cores

@@ -145,6 +145,12 @@ hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, i
 size_t gemm_ternary_workspace(int64_t n, int64_t k, int64_t c);
 hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
                                float* out, void* ws, hipStream_t s);
+// launch_gemv_ternary with the c >= 64 workspace in the library's static
+// scratch (nothing allocated); hipErrorInvalidValue when the workspace
+// exceeds it.
+constexpr size_t kTernScratchBytes = size_t(64) << 20;
+hipError_t launch_gemv_ternary_noalloc(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
+                                       int64_t c, float* out, hipStream_t s);
 hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, const int32_t* esc_idx,
                                   const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq,
                                   int64_t n, int64_t k, int64_t c, float* out, hipStream_t s);

@@ -220,6 +220,24 @@ int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int
                     int64_t c, float* out, void* stream);
 
 /*
+ * wq_gemv_ternary_noalloc -- wq_gemv_ternary for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, results
+ * bit-identical to wq_gemv_ternary's.  It calls no allocator: the c >= 64
+ * product's workspace (the unpacked operands, about n k + 2 c k bytes)
+ * lives in a static device array of the library, WQ_TERNARY_SCRATCH_BYTES
+ * (64 MiB) on every device the library runs on, held until the process
+ * ends; a larger workspace is WQ_ESHAPE, before anything is launched.  Below
+ * 64 columns no workspace is used.  Every call on a device shares that
+ * device's array (it keeps the last call's contents, all of which the next
+ * call rewrites before reading), so calls that overlap on one device --
+ * on different streams, or from several host threads -- race.
+ */
+#define WQ_TERNARY_SCRATCH_BYTES (64ll << 20)
+int wq_gemv_ternary_noalloc(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k,
+                            int64_t c, float* out, void* stream);
+
+/*
  * PTQ1_1 superblocks (Ternary post [2 weight compression], struct ptq1_1;
  * [3.1 data format], sb = kbx >> 3, sub = kbx & 7): eight consecutive
  * PTQ1_0 blocks of a row in 216 bytes, 1/28 fewer than 8 x 28.  The post

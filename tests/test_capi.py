@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("wq_pack_int4", "wq_quantize_pack_int4", "wq_gemv_w4", "wq_gemm_w4a16",
-                 "wq_pack_ptq1_0", "wq_quantize_q8_1", "wq_gemv_ternary", "wq_status_string",
+                 "wq_pack_ptq1_0", "wq_quantize_q8_1", "wq_gemv_ternary", "wq_gemv_ternary_noalloc", "wq_status_string",
                  "wq_abi_version", "wq_peak_read", "wq_peak_read_sink_words", "wq_peak_mfma_bf16",
                  "wq_peak_valu_fma"):
         assert want in names
@@ -84,6 +84,12 @@ def test_validation_errors_without_gpu(lib):
     # of weights; 2^20 columns of 128 q8_1 blocks is 4.8 GB of activations
     assert lib.wq_gemv_ternary(FAKE, FAKE, 1 << 22, 4096, 64, FAKE, None) == g.WQ_ESHAPE
     assert lib.wq_gemv_ternary(FAKE, FAKE, 64, 4096, 1 << 20, FAKE, None) == g.WQ_ESHAPE
+    # the entry point that allocates nothing: the same checks, and a workspace
+    # (about n k + 2 c k bytes) beyond its 64 MiB scratch is refused up front
+    assert lib.wq_gemv_ternary_noalloc(FAKE, FAKE, 4, 100, 1, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary_noalloc(FAKE, FAKE, 64, 4096, 1 << 20, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary_noalloc(FAKE, FAKE, 17280, 5120, 4096, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary_noalloc(None, None, 10, 128, 0, None, None) == 0
     assert lib.wq_pack_ptq1_0(FAKE, FAKE, 2, 64, FAKE, None) == g.WQ_ESHAPE
     # sizes whose products overflow int64 are rejected, not wrapped round
     huge = 1 << 40
