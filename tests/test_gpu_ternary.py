@@ -124,7 +124,7 @@ def test_ternary_gemv_passes_of_16(k, n, c):
     assert np.array_equal(got, exact.astype(np.float64))
 
 
-# ---- 64 or more columns: the int8 matrix-core kernel
+# ---- 64 or more columns: the fp4 x fp8 matrix-core kernel on unpacked operands
 @pytest.mark.parametrize("k,n,c", [(1024, 256, 64), (640, 333, 200), (5120, 2048, 128),
                                    (384, 77, 130)])
 def test_ternary_gemm(k, n, c):
@@ -156,8 +156,9 @@ def test_ternary_gemm_timed_shape_sampled_columns():
 
 @pytest.mark.parametrize("k,n,c", [(1024, 300, 64), (5120, 200, 129)])
 def test_ternary_gemm_unit_scale_exact(k, n, c):
-    # unit scales and integer x: the int32 products and the float32 sums are
-    # exact, so the result is the integer product bit for bit
+    # unit scales and integer x (a +-127 in every block): the products' sums
+    # (exact integers in float32) and the scaled sums are exact, so the result
+    # is the integer product bit for bit
     say("ternary gemm unit scale", k, n, c)
     p = wq_inputs.ternary_gemv(k, n, cmax=c, unit_scale=True)
     wb = gpu_blocks(p.trits, p.d_bits)
