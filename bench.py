@@ -475,7 +475,6 @@ def ternary_rows(g, torch, wq_inputs, dev, log):
             "Mrows_per_s": round(17280 * cc / (ms * 1e-3) / 1e6, 1)}
     rows["gemv_ternary_ptq1_1"] = srow
     log("ternary ptq1_1:", json.dumps(srow))
-    del scs, sup_d
     # 4096 activation columns: the matrix-core path (fp4 trits x fp8 pairs,
     # priced as 2 ops per useful MAC against the 5 POP/s int8 / fp8 peak;
     # the call includes unpacking both operands)
@@ -490,7 +489,13 @@ def ternary_rows(g, torch, wq_inputs, dev, log):
                                  "frac_mfma_int8": round(tops / INT8_PEAK_TOPS, 4),
                                  "kernel": "k_unpack_ptq1_0_fp4 + k_unpack_q8_1_fp8 + k_gemm_ternary (v_mfma_scale_f32_32x32x64_f8f6f4)"}
     log("ternary gemm 4096 x 17280 x 5120:", json.dumps(rows["gemm_ternary_4096"]))
-    del xg, yg
+    # the same product on PTQ1_1 superblocks (unpacked by their own kernel)
+    ms = timed(torch, lambda i: g.wq_gemv_ternary_ptq1_1(scs[i % nc1], *tabs, xg, 5120, yg), 5)
+    tops = 2.0 * mg * 17280 * 5120 / (ms * 1e-3) / 1e12
+    rows["gemm_ternary_ptq1_1_4096"] = {"ms": round(ms, 4), "TOPs": round(tops, 1),
+                                        "frac_mfma_int8": round(tops / INT8_PEAK_TOPS, 4)}
+    log("ternary gemm on ptq1_1 superblocks:", json.dumps(rows["gemm_ternary_ptq1_1_4096"]))
+    del xg, yg, scs, sup_d
     return rows
 
 

@@ -220,8 +220,12 @@ int wq_gemv_ternary_ptq1_1(const uint8_t* superblocks, const uint8_t* codebook,
   if (n_esc > 2048) return WQ_EUNSUPPORTED;  // escape table staged in LDS
   if (n >= (int64_t(1) << 30) || mul_sat(mul_sat(n, k / 128), 28) >= (int64_t(1) << 31))
     return WQ_ESHAPE;
-  if (!aligned(superblocks, 4) || !aligned(codebook, 4) || !aligned(x_q8, 4) || !aligned(out, 4) ||
-      (n_esc > 0 && (!aligned(esc_idx, 4) || !aligned(esc_patt, 4))))
+  if (c >= 64) {  // the matrix-core product: activations' 32-bit offsets and the tile grid
+    if (mul_sat(mul_sat(c, k / 32), 36) >= (int64_t(1) << 31)) return WQ_ESHAPE;
+    if (mul_sat(c / 128 + 1, n / 128 + 1) > kMaxGrid) return WQ_ESHAPE;
+  }
+  if (!aligned(superblocks, 4) || !aligned(codebook, 4) || !aligned(x_q8, 4) ||
+      !aligned(out, c >= 64 ? 16 : 4) || (n_esc > 0 && (!aligned(esc_idx, 4) || !aligned(esc_patt, 4))))
     return WQ_EALIGN;
   return hip_status(wq::launch_gemv_ternary_sb(superblocks, codebook, esc_idx, esc_patt, n_esc, x_q8,
                                                n, k, c, out, as_stream(stream)));

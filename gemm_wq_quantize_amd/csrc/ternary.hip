@@ -1081,6 +1081,42 @@ __global__ __launch_bounds__(256) void k_unpack_ptq1_0_fp4(const uint32_t* __res
   dw[b] = f16_to_f32(v[6] >> 16);
 }
 
+// PTQ1_1 superblocks -> the same fp4 trit pairs and float block scales as
+// k_unpack_ptq1_0_fp4 (sub-block sub of superblock sb is block 8 sb + sub):
+// one lane per sub-block, decoded with the codebook and escape tables staged
+// in LDS as in the GEMV kernels
+__global__ __launch_bounds__(256) void k_unpack_ptq1_1_fp4(const uint32_t* __restrict__ w, int64_t nb,
+                                                           int bpr, SbTables sbt, uint4* __restrict__ t4,
+                                                           float* __restrict__ dw) {
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * LUT_COPIES];
+  __shared__ __attribute__((aligned(16))) uint32_t tbl[sb_lds_words(SB_ESC_MAX)];
+  tern_lut_init(lut);
+  tern_stage_sb(tbl, sbt);
+  __syncthreads();
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nb) return;
+  const int64_t row = b / bpr;
+  const int blk = (int)(b - row * bpr), sub = blk & 7, nit = bpr >> 3;
+  const int64_t gidx = row * nit + (blk >> 3);  // the superblock (escape key)
+  const uint32_t* sw = w + gidx * (SB_BYTES / 4);
+  uint32_t v[12];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) v[j] = sw[6 * sub + j];  // this sub-block's qs
+#pragma unroll
+  for (int j = 0; j < 6; ++j) v[6 + j] = sw[48 + j];   // the superblock's bytes 192..215
+  uint32_t dg[32];
+  float d;
+  tern_decode_sb(v, lut + (threadIdx.x & (LUT_COPIES - 1)), tbl, sbt.n_esc, (int)gidx, sub, dg, d);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = __builtin_amdgcn_perm(0u, 0x002200AAu, dg[4 * i + e]);
+    t4[b * 8 + i] = make_uint4(t[0], t[1], t[2], t[3]);
+  }
+  dw[b] = d;
+}
+
 // block_q8_1 -> fp8 pairs [c][2k] and float d_x [c][k/32]: one lane per block
 __global__ __launch_bounds__(256) void k_unpack_q8_1_fp8(const uint32_t* __restrict__ xq, int64_t nb,
                                                          uint4* __restrict__ q8, float* __restrict__ dx) {
@@ -1483,14 +1519,11 @@ hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n,
 
 size_t gemm_ternary_workspace(int64_t n, int64_t k, int64_t c) { return tern_ws(n, k, c).bytes; }
 
-hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
-                               float* out, void* ws, hipStream_t s) {
+// x unpacked and the product, once the weights are in the workspace
+static hipError_t gemm_ternary_unpacked(const uint8_t* xq, int64_t n, int64_t k, int64_t c, float* out,
+                                        uint8_t* base, hipStream_t s) {
   const TernWs L = tern_ws(n, k, c);
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  const int64_t nbw = n * (k / 128), nbx = c * (k / 32);
-  hipLaunchKernelGGL(k_unpack_ptq1_0_fp4, dim3((unsigned)((nbw + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<const uint32_t*>(w), nbw, reinterpret_cast<uint4*>(base),
-                     reinterpret_cast<float*>(base + L.dw));
+  const int64_t nbx = c * (k / 32);
   hipLaunchKernelGGL(k_unpack_q8_1_fp8, dim3((unsigned)((nbx + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(xq), nbx, reinterpret_cast<uint4*>(base + L.x),
                      reinterpret_cast<float*>(base + L.dx));
@@ -1499,6 +1532,17 @@ hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, i
                      reinterpret_cast<const float*>(base + L.dw), base + L.x,
                      reinterpret_cast<const float*>(base + L.dx), out, (int)n, (int)k, (int)c, tiles_m);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
+                               float* out, void* ws, hipStream_t s) {
+  const TernWs L = tern_ws(n, k, c);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const int64_t nbw = n * (k / 128);
+  hipLaunchKernelGGL(k_unpack_ptq1_0_fp4, dim3((unsigned)((nbw + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(w), nbw, reinterpret_cast<uint4*>(base),
+                     reinterpret_cast<float*>(base + L.dw));
+  return gemm_ternary_unpacked(xq, n, k, c, out, base, s);
 }
 
 // The GEMM's workspace comes from a memory pool of this library's own, one
@@ -1567,19 +1611,25 @@ hipError_t launch_gemv_ternary_noalloc(const uint8_t* w, const uint8_t* xq, int6
   return launch_gemm_ternary(w, xq, n, k, c, out, ws, s);
 }
 
+// run(ws) with a workspace of `bytes` from the pool, freed in stream order
+template <class F>
+static hipError_t with_pool_workspace(size_t bytes, hipStream_t s, F run) {
+  hipMemPool_t pool = nullptr;
+  hipError_t e = tern_pool(&pool);
+  if (e != hipSuccess) return e;
+  void* ws = nullptr;
+  e = hipMallocFromPoolAsync(&ws, bytes, pool, s);
+  if (e != hipSuccess) return e;
+  e = run(ws);
+  const hipError_t f = hipFreeAsync(ws, s);
+  return e != hipSuccess ? e : f;
+}
+
 hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s) {
-  if (c >= 64) {  // a batch wide enough for the matrix cores
-    hipMemPool_t pool = nullptr;
-    hipError_t e = tern_pool(&pool);
-    if (e != hipSuccess) return e;
-    void* ws = nullptr;
-    e = hipMallocFromPoolAsync(&ws, gemm_ternary_workspace(n, k, c), pool, s);
-    if (e != hipSuccess) return e;
-    e = launch_gemm_ternary(w, xq, n, k, c, out, ws, s);
-    const hipError_t f = hipFreeAsync(ws, s);
-    return e != hipSuccess ? e : f;
-  }
+  if (c >= 64)  // a batch wide enough for the matrix cores
+    return with_pool_workspace(gemm_ternary_workspace(n, k, c), s,
+                               [&](void* ws) { return launch_gemm_ternary(w, xq, n, k, c, out, ws, s); });
   // 17..63 columns: passes of at most 16 over x[c0:c0+16] -> out[c0:c0+16]
   for (int64_t c0 = 0; c0 < c; c0 += 16) {
     const hipError_t e = launch_ternary_narrow(w, xq + c0 * (k / 32) * Q8_BYTES, n, k,
@@ -1598,6 +1648,17 @@ hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, con
                                   int64_t n, int64_t k, int64_t c, float* out, hipStream_t s) {
   const uint32_t* wp = reinterpret_cast<const uint32_t*>(w);
   const SbTables t{codebook, esc_idx, esc_patt, (int)n_esc};
+  if (c >= 64) {  // a prefill batch: the superblocks unpacked, then the matrix-core product
+    return with_pool_workspace(gemm_ternary_workspace(n, k, c), s, [&](void* ws) {
+      const TernWs L = tern_ws(n, k, c);
+      uint8_t* base = static_cast<uint8_t*>(ws);
+      const int64_t nbw = n * (k / 128);
+      hipLaunchKernelGGL(k_unpack_ptq1_1_fp4, dim3((unsigned)((nbw + 255) / 256)), dim3(256), 0, s, wp,
+                         nbw, (int)(k / 128), t, reinterpret_cast<uint4*>(base),
+                         reinterpret_cast<float*>(base + L.dw));
+      return gemm_ternary_unpacked(xq, n, k, c, out, base, s);
+    });
+  }
   for (int64_t c0 = 0; c0 < c; ) {
     const int64_t left = c - c0;
     const uint8_t* xp = xq + c0 * (k / 32) * Q8_BYTES;

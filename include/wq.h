@@ -289,7 +289,10 @@ int wq_ptq1_1_encode(const uint8_t* blocks, int64_t n, int64_t k, uint8_t* super
  *   x_q8         [c][k/32] block_q8_1; out [c][n] float32.
  * Requires k % 1024 == 0 and k <= 65536 (x of a column and the tables are
  * staged in LDS), n_esc <= 2048 (else WQ_EUNSUPPORTED), all pointers 4-byte
- * aligned.  Any c >= 1 (passes of at most 8 columns).
+ * aligned (out 16-byte for c >= 64).  Up to 63 columns run as passes of at
+ * most 8; c >= 64 unpacks the superblocks into the fp4 trit pairs of the
+ * PTQ1_0 path and runs its matrix-core product (same workspace, pool and
+ * limits as wq_gemv_ternary with c >= 64).
  */
 int wq_gemv_ternary_ptq1_1(const uint8_t* superblocks, const uint8_t* codebook,
                            const int32_t* esc_idx, const uint8_t* esc_patt, int64_t n_esc,

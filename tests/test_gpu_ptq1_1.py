@@ -78,13 +78,39 @@ def test_ptq1_1_gemv_escapes_and_passes(k, n):
         check_f32(gemv(dev, xq, k, n), ot.gemv_ternary_ptq1_1(*ref, ot.quantize_q8_1(p.x[:c])))
 
 
-@pytest.mark.parametrize("c", [1, 4, 8])
+@pytest.mark.parametrize("k,n,c", [(5120, 500, 64), (2048, 333, 130), (8192, 77, 96)])
+def test_ptq1_1_prefill(k, n, c):
+    # 64 or more columns: the superblocks unpacked, then the matrix-core
+    # product; ragged tiles in both directions, most superblocks escaped
+    p = wq_inputs.ternary_gemv(k, n, cmax=c, seed=k + c)
+    rng = np.random.default_rng(c)
+    d = ((rng.integers(5, 13, p.d_bits.shape) << 10) | rng.integers(0, 1024, p.d_bits.shape)).astype(np.uint16)
+    dev, ref = encode_both(p.trits, d)
+    say("ptq1_1 prefill", k, n, c, "escapes", len(ref[2]))
+    xq = gpu_q8(p.x)
+    check_f32(gemv(dev, xq, k, n), ot.gemv_ternary_ptq1_1(*ref, ot.quantize_q8_1(p.x)))
+
+
+def test_ptq1_1_prefill_timed_shape_sampled_columns():
+    # the ternary GEMM's workload on superblocks with the post's exponent
+    # statistics; 8 seeded columns against the oracle, the rest finite
+    k, n, c = 5120, 17280, 4096
+    p = wq_inputs.ternary_correlated_scales(k, n, cmax=c, seed=3)
+    dev, ref = encode_both(p.trits, p.d_bits)
+    say("ptq1_1 prefill", k, n, c, "sampled columns")
+    got = gemv(dev, gpu_q8(p.x), k, n)
+    cols = np.sort(np.random.default_rng(3).choice(c, 8, replace=False))
+    check_f32(got[cols], ot.gemv_ternary_ptq1_1(*ref, ot.quantize_q8_1(p.x[cols])))
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("c", [1, 4, 8, 96])
 def test_ptq1_1_unit_scale_exact(c):
     # every d = 1.0 (one pattern) and integer activations with +-127 in each
     # block of 32: the exact integer product, bit for bit
     k, n = 5120, 4000
     say("ptq1_1 unit scale", k, n, c)
-    p = wq_inputs.ternary_gemv(k, n, cmax=8, unit_scale=True)
+    p = wq_inputs.ternary_gemv(k, n, cmax=max(c, 8), unit_scale=True)
     dev, _ = encode_both(p.trits, p.d_bits)
     got = gemv(dev, gpu_q8(p.x[:c]), k, n)
     exact = p.x[:c].astype(np.int64) @ p.trits.astype(np.int64).T
