@@ -32,6 +32,19 @@ two; they are pinned by round trips and by the post's byte-0 example only):
            fidelity; the exact path never uses it):
            y[c, r] = sum_b d_w[r, b // 4] * d_x[c, b] * S[r, c, b].
 
+PT plane layout of the activations (section 3.1): the q8_1 data of one
+column regrouped by 128-element block i (K/128 of them) into nine planes of
+K/128 16-byte slots.  Element e (0..127) of block i sits at byte
+16 (floor(e / 16) * K/128 + i) + e mod 16 -- plane floor(e / 16) -- and plane
+8 holds the four (d, s) pairs of each block.  The post draws plane 8 only as
+"all (d, s)" of the block; reading (parity unpinned beyond the sizes, the
+plane picture and the round trip):
+  R-pt     Slot i of plane 8 holds the (d, s) words of the block's four q8_1
+           sub-blocks in order, each as in block_q8_1 (fp16 d, then fp16 s):
+           sub-block j of block i at byte 16 (8 K/128 + i) + 4 j.  K must be a
+           multiple of 128.  A batch of c columns is c consecutive PT arrays
+           of 9 K / 8 bytes (the size of the column's q8_1 blocks).
+
 PTQ1_1 superblock (section 2, struct ptq1_1; section 3.1, sb = kbx >> 3,
 sub = kbx & 7): eight consecutive PTQ1_0 blocks of a row in 216 bytes --
 qs[192], qh[13], eight 10-bit mantissas, one exponent byte.  The post fixes
@@ -357,3 +370,57 @@ def decode_ptq1_1(sup: np.ndarray, codebook, esc_idx, esc_pat) -> np.ndarray:
 def gemv_ternary_ptq1_1(sup, codebook, esc_idx, esc_pat, x_blocks) -> np.ndarray:
     """y[c, r] for PTQ1_1 weights: the PTQ1_0 GEMV of the decoded blocks."""
     return gemv_ternary(decode_ptq1_1(sup, codebook, esc_idx, esc_pat), x_blocks)
+
+
+# ---------------------------------------------------------------- PT planes
+PT_PLANES = 9     # eight planes of q, one of (d, s)
+PT_SLOT = 16      # bytes per block per plane
+
+
+def pt_offset(e: int, i: int, k: int) -> int:
+    """Byte of element e (0..127) of 128-element block i in a column's PT
+    array (Ternary post, section 3.1: plane floor(e / 16), slot i)."""
+    return PT_SLOT * ((e // 16) * (k // QK) + i) + e % 16
+
+
+def pt_ds_offset(j: int, i: int, k: int) -> int:
+    """Byte of the (d, s) pair of sub-block j (0..3) of block i: plane 8
+    (reading R-pt)."""
+    return PT_SLOT * (8 * (k // QK) + i) + 4 * j
+
+
+def q8_1_to_pt(blocks: np.ndarray) -> np.ndarray:
+    """block_q8_1 bytes [c][K/32][36] -> PT arrays uint8 [c][9 K / 8]."""
+    b = np.asarray(blocks, dtype=np.uint8)
+    c, nsb, _ = b.shape
+    k = nsb * Q8_QK
+    assert k % QK == 0
+    nb = k // QK
+    q = b[:, :, 4:].reshape(c, k)          # q of element 128 i + e, as bytes
+    out = np.zeros((c, PT_PLANES * nb * PT_SLOT), dtype=np.uint8)
+    e = np.arange(QK)
+    for i in range(nb):
+        offs = np.array([pt_offset(int(v), i, k) for v in e])
+        out[:, offs] = q[:, QK * i + e]
+        for j in range(QK // Q8_QK):
+            o = pt_ds_offset(j, i, k)
+            out[:, o:o + 4] = b[:, 4 * i + j, 0:4]
+    return out
+
+
+def pt_to_q8_1(pt: np.ndarray) -> np.ndarray:
+    """Inverse of ``q8_1_to_pt``: PT arrays [c][9 K / 8] -> [c][K/32][36]."""
+    p = np.asarray(pt, dtype=np.uint8)
+    c, nbytes = p.shape
+    assert nbytes % (PT_PLANES * PT_SLOT) == 0
+    nb = nbytes // (PT_PLANES * PT_SLOT)
+    k = nb * QK
+    out = np.zeros((c, k // Q8_QK, Q8_BYTES), dtype=np.uint8)
+    e = np.arange(QK)
+    for i in range(nb):
+        offs = np.array([pt_offset(int(v), i, k) for v in e])
+        out[:, 4 * i:4 * i + 4, 4:] = p[:, offs].reshape(c, 4, Q8_QK)
+        for j in range(QK // Q8_QK):
+            o = pt_ds_offset(j, i, k)
+            out[:, 4 * i + j, 0:4] = p[:, o:o + 4]
+    return out

@@ -198,6 +198,17 @@ def _sb_escape_key_without_row(mp):
     mp.setattr(ternary, "superblock_index", lambda row, sb, nsb: sb)
 
 
+def _pt_block_major(mp):
+    # block i's eight 16-byte slots together (16 (8 i + plane) + e mod 16)
+    # instead of plane-major slots
+    mp.setattr(ternary, "pt_offset", lambda e, i, k: 16 * (8 * i + e // 16) + e % 16)
+
+
+def _pt_ds_reversed(mp):
+    # the four (d, s) pairs of a block in reverse sub-block order
+    mp.setattr(ternary, "pt_ds_offset", lambda j, i, k: 16 * (8 * (k // 128) + i) + 4 * (3 - j))
+
+
 CASES = {
     "int4: low nibble holds the odd k": (_swap_nibbles, _int4_pins),
     "int4: gfx950 order replaced by its inverse": (_inverse_interleave, _int4_pins),
@@ -218,6 +229,8 @@ CASES = {
     "ptq1_1: mantissa field big-endian": (_sb_mantissa_big_endian, _ternary_pins),
     "ptq1_1: codebook ties by decreasing pattern": (_sb_ties_descending, _ternary_pins),
     "ptq1_1: escape table keyed by the superblock within its row": (_sb_escape_key_without_row, _ternary_pins),
+    "pt: slots block-major instead of plane-major": (_pt_block_major, _ternary_pins),
+    "pt: (d, s) pairs of a block in reverse order": (_pt_ds_reversed, _ternary_pins),
 }
 
 

@@ -251,3 +251,72 @@ def test_ptq1_1_rejects_negative_scale():
     d[0, 3] = 0xBC00
     with pytest.raises(AssertionError):
         ternary.encode_ptq1_1(ternary.encode_ptq1_0(np.zeros((1, 1024), np.int8), d))
+
+
+# ---------------------------------------------------------------- PT planes
+def _q8_blocks(c, k, seed):
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 256, (c, k // 32, 36), dtype=np.uint8)
+
+
+def test_pt_sizes_match_post():
+    g = load_golden("ptq1_0_layout.txt")
+    k = int(g["pt_example_k"][0])
+    nb = k // 128
+    assert nb == int(g["pt_example_blocks_per_plane"][0])
+    assert 128 // 32 == int(g["pt_ds_pairs_per_block"][0])
+    pt = ternary.q8_1_to_pt(_q8_blocks(1, k, 1))
+    planes, slot = int(g["pt_planes"][0]), int(g["pt_slot_bytes"][0])
+    assert pt.shape == (1, planes * nb * slot)
+    # the same bytes as the column's q8_1 blocks: 9 K / 8 = 36 K / 32
+    assert pt.shape[1] == (k // 32) * ternary.Q8_BYTES == 9 * k // 8
+    # the four (d, s) pairs of a block fill its 16-byte slot of plane 8
+    assert int(g["pt_ds_pairs_per_block"][0]) * 4 == slot
+    assert int(g["pt_elements_per_plane_slot"][0]) * (planes - 1) == 128
+
+
+def test_pt_offset_is_a_bijection():
+    # planes 0..7: every (block, element) to its own byte of [0, 8 * 16 * K/128)
+    for k in (128, 1024, 5120):
+        nb = k // 128
+        offs = sorted(ternary.pt_offset(e, i, k) for i in range(nb) for e in range(128))
+        assert offs == list(range(8 * 16 * nb))
+        ds = sorted(ternary.pt_ds_offset(j, i, k) + b for i in range(nb) for j in range(4) for b in range(4))
+        assert ds == list(range(8 * 16 * nb, 9 * 16 * nb))
+
+
+def test_pt_matches_plane_picture():
+    # the post's picture read directly: plane p = [block 0][block 1]... with
+    # elements 16p .. 16p + 15 of each block, then plane 8 = the (d, s) words
+    c, k = 3, 1024
+    blk = _q8_blocks(c, k, 2)
+    pt = ternary.q8_1_to_pt(blk)
+    nb = k // 128
+    q = blk[:, :, 4:].reshape(c, nb, 8, 16)        # [col][block][plane][16]
+    planes = q.transpose(0, 2, 1, 3).reshape(c, 8 * nb * 16)
+    assert np.array_equal(pt[:, :8 * nb * 16], planes)
+    ds = blk[:, :, 0:4].reshape(c, nb, 16)         # four (d, s) words per block
+    assert np.array_equal(pt[:, 8 * nb * 16:], ds.reshape(c, nb * 16))
+
+
+def test_pt_handworked_offsets():
+    # K = 256 (two blocks per plane): element 17 of block 1 is plane 1, slot
+    # 1, byte 1 -> 16 * (1 * 2 + 1) + 1 = 49; element 127 of block 0 is
+    # plane 7, slot 0, byte 15 -> 16 * 14 + 15 = 239; the (d, s) pair of
+    # sub-block 3 of block 1 starts at 16 * (8 * 2 + 1) + 12 = 284
+    assert ternary.pt_offset(17, 1, 256) == 49
+    assert ternary.pt_offset(127, 0, 256) == 239
+    assert ternary.pt_ds_offset(3, 1, 256) == 284
+    blk = np.zeros((1, 8, 36), np.uint8)
+    blk[0, 4, 4 + 17] = 0xAB      # block 1 = sub-blocks 4..7; element 17 is in sub-block 4
+    blk[0, 3, 4 + 31] = 0xCD      # element 127 of block 0: sub-block 3, q[31]
+    blk[0, 7, 0:4] = [1, 2, 3, 4]
+    pt = ternary.q8_1_to_pt(blk)[0]
+    assert pt[49] == 0xAB and pt[239] == 0xCD and list(pt[284:288]) == [1, 2, 3, 4]
+    assert np.count_nonzero(pt) == 6
+
+
+def test_pt_round_trip():
+    for c, k in ((1, 128), (2, 5120), (3, 17280 // 128 * 128)):
+        blk = _q8_blocks(c, k, 3)
+        assert np.array_equal(ternary.pt_to_q8_1(ternary.q8_1_to_pt(blk)), blk)
