@@ -32,10 +32,13 @@ _SIGS = {
     "wq_gemm_w4a16_zp": ([_p, _p, _i, _p, _p, _i64, _i64, _i64, _i64, _p, _p], _i),
     "wq_pack_ptq1_0": ([_p, _p, _i64, _i64, _p, _p], _i),
     "wq_quantize_q8_1": ([_p, _i64, _i64, _p, _p], _i),
+    "wq_quantize_q8_1_pt": ([_p, _i64, _i64, _p, _p], _i),
     "wq_gemv_ternary": ([_p, _p, _i64, _i64, _i64, _p, _p], _i),
+    "wq_gemv_ternary_pt": ([_p, _p, _i64, _i64, _i64, _p, _p], _i),
     "wq_gemv_ternary_noalloc": ([_p, _p, _i64, _i64, _i64, _p, _p], _i),
     "wq_ptq1_1_encode": ([_p, _i64, _i64, _p, _p, _p, _p, _i64, _p], _i),
     "wq_gemv_ternary_ptq1_1": ([_p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _p], _i),
+    "wq_gemv_ternary_ptq1_1_pt": ([_p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _p], _i),
     # calibration kernels (include/wq_peaks.h)
     "wq_peak_read_sink_words": ([], _i64),
     "wq_peak_read": ([_p, _i64, _p, _i64, _p], _i),
@@ -214,14 +217,23 @@ def wq_pack_ptq1_0(trits, d, blocks, stream=None):
            lib.wq_pack_ptq1_0(_ptr(trits, dv), _ptr(d, dv), n, k, _ptr(blocks, dv), _sptr(st)))
 
 
-def wq_quantize_q8_1(x, x_q8, stream=None):
-    """fp32 x [c][k] -> block_q8_1 uint8 [c][k/32][36]."""
+def _quantize_q8_1(name, x, x_q8, stream):
     c, k = x.shape
     _require(x.dtype == torch.float32 and x_q8.dtype == torch.uint8, "x fp32, x_q8 uint8")
     _require(x_q8.numel() == c * (k // 32) * 36, "x_q8 holds c * k / 32 * 36 bytes")
     st = _stream(stream)
-    _check("wq_quantize_q8_1", lib.wq_quantize_q8_1(_ptr(x, st.device), c, k, _ptr(x_q8, st.device),
-                                                    _sptr(st)))
+    _check(name, getattr(lib, name)(_ptr(x, st.device), c, k, _ptr(x_q8, st.device), _sptr(st)))
+
+
+def wq_quantize_q8_1(x, x_q8, stream=None):
+    """fp32 x [c][k] -> block_q8_1 uint8 [c][k/32][36]."""
+    _quantize_q8_1("wq_quantize_q8_1", x, x_q8, stream)
+
+
+def wq_quantize_q8_1_pt(x, x_pt, stream=None):
+    """fp32 x [c][k] -> the same q8_1 blocks in the PT plane layout, uint8
+    [c][9k/8]."""
+    _quantize_q8_1("wq_quantize_q8_1_pt", x, x_pt, stream)
 
 
 def _ternary_args(w_blocks, x_q8, k, out):
@@ -241,6 +253,15 @@ def wq_gemv_ternary(w_blocks, x_q8, k, out, stream=None):
     d = st.device
     _check("wq_gemv_ternary",
            lib.wq_gemv_ternary(_ptr(w_blocks, d), _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
+
+
+def wq_gemv_ternary_pt(w_blocks, x_pt, k, out, stream=None):
+    """wq_gemv_ternary with x in the PT plane layout, uint8 [c][9k/8]."""
+    n, c = _ternary_args(w_blocks, x_pt, k, out)
+    st = _stream(stream)
+    d = st.device
+    _check("wq_gemv_ternary_pt",
+           lib.wq_gemv_ternary_pt(_ptr(w_blocks, d), _ptr(x_pt, d), n, k, c, _ptr(out, d), _sptr(st)))
 
 
 def wq_gemv_ternary_noalloc(w_blocks, x_q8, k, out, stream=None):
@@ -280,6 +301,17 @@ def wq_ptq1_1_encode(blocks):
 def wq_gemv_ternary_ptq1_1(superblocks, codebook, esc_idx, esc_patt, x_q8, k, out, stream=None):
     """out fp32 [c][n] from PTQ1_1 superblocks [n][k/1024][216] (device), the
     codebook [767][8] and escape table (device), and q8_1 x [c][k/32][36]."""
+    _gemv_ternary_ptq1_1("wq_gemv_ternary_ptq1_1", superblocks, codebook, esc_idx, esc_patt, x_q8, k, out,
+                         stream)
+
+
+def wq_gemv_ternary_ptq1_1_pt(superblocks, codebook, esc_idx, esc_patt, x_pt, k, out, stream=None):
+    """wq_gemv_ternary_ptq1_1 with x in the PT plane layout, uint8 [c][9k/8]."""
+    _gemv_ternary_ptq1_1("wq_gemv_ternary_ptq1_1_pt", superblocks, codebook, esc_idx, esc_patt, x_pt, k, out,
+                         stream)
+
+
+def _gemv_ternary_ptq1_1(name, superblocks, codebook, esc_idx, esc_patt, x_q8, k, out, stream):
     n = superblocks.shape[0]
     c = x_q8.shape[0]
     n_esc = esc_idx.numel()
@@ -293,11 +325,10 @@ def wq_gemv_ternary_ptq1_1(superblocks, codebook, esc_idx, esc_patt, x_q8, k, ou
     _require(out.dtype == torch.float32 and out.numel() == c * n, "out is fp32 [c][n]")
     st = _stream(stream)
     d = st.device
-    _check("wq_gemv_ternary_ptq1_1",
-           lib.wq_gemv_ternary_ptq1_1(_ptr(superblocks, d), _ptr(codebook, d),
-                                      _ptr(esc_idx, d) if n_esc else None,
-                                      _ptr(esc_patt, d) if n_esc else None, n_esc,
-                                      _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
+    _check(name, getattr(lib, name)(_ptr(superblocks, d), _ptr(codebook, d),
+                                    _ptr(esc_idx, d) if n_esc else None,
+                                    _ptr(esc_patt, d) if n_esc else None, n_esc,
+                                    _ptr(x_q8, d), n, k, c, _ptr(out, d), _sptr(st)))
 
 
 # ---- calibration kernels (include/wq_peaks.h): practical ceilings of the

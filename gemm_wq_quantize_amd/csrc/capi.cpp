@@ -76,6 +76,39 @@ int check_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, 
   *launch = true;
   return WQ_OK;
 }
+int quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, bool pt, void* stream) {
+  if (c < 0 || k < 0) return WQ_EINVAL;
+  if (c == 0 || k == 0) return WQ_OK;
+  if (!x || !x_q8) return WQ_EINVAL;
+  if (k % (pt ? 128 : 32) != 0) return WQ_ESHAPE;
+  if (pt && k > (int64_t(1) << 30)) return WQ_ESHAPE;  // a column's plane offsets in 32 bits
+  if (!aligned(x, 16) || !aligned(x_q8, 4)) return WQ_EALIGN;
+  if (mul_sat(c, k) / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
+  return hip_status(wq::launch_quantize_q8_1(x, c, k, x_q8, pt, as_stream(stream)));
+}
+
+int gemv_ternary_ptq1_1(const uint8_t* superblocks, const uint8_t* codebook, const int32_t* esc_idx,
+                        const uint8_t* esc_patt, int64_t n_esc, const uint8_t* x_q8, bool pt, int64_t n,
+                        int64_t k, int64_t c, float* out, void* stream) {
+  if (n < 0 || k < 0 || c < 0 || n_esc < 0) return WQ_EINVAL;
+  if (n == 0 || c == 0) return WQ_OK;
+  if (!superblocks || !codebook || !x_q8 || !out || (n_esc > 0 && (!esc_idx || !esc_patt)))
+    return WQ_EINVAL;
+  // superblocks of 8 blocks; x of one column must fit in LDS beside the tables
+  if (k == 0 || k % 1024 != 0 || k > 65536) return WQ_ESHAPE;
+  if (n_esc > 2048) return WQ_EUNSUPPORTED;  // escape table staged in LDS
+  if (n >= (int64_t(1) << 30) || mul_sat(mul_sat(n, k / 128), 28) >= (int64_t(1) << 31))
+    return WQ_ESHAPE;
+  if (c >= 64) {  // the matrix-core product: activations' 32-bit offsets and the tile grid
+    if (mul_sat(mul_sat(c, k / 32), 36) >= (int64_t(1) << 31)) return WQ_ESHAPE;
+    if (mul_sat(c / 128 + 1, n / 128 + 1) > kMaxGrid) return WQ_ESHAPE;
+  }
+  if (!aligned(superblocks, 4) || !aligned(codebook, 4) || !aligned(x_q8, 4) ||
+      !aligned(out, c >= 64 ? 16 : 4) || (n_esc > 0 && (!aligned(esc_idx, 4) || !aligned(esc_patt, 4))))
+    return WQ_EALIGN;
+  return hip_status(wq::launch_gemv_ternary_sb(superblocks, codebook, esc_idx, esc_patt, n_esc, x_q8, pt,
+                                               n, k, c, out, as_stream(stream)));
+}
 }  // namespace
 
 extern "C" {
@@ -179,14 +212,13 @@ int wq_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
   return hip_status(wq::launch_pack_ptq1_0(trits, d, n, k, blocks, as_stream(stream)));
 }
 
+
 int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* stream) {
-  if (c < 0 || k < 0) return WQ_EINVAL;
-  if (c == 0 || k == 0) return WQ_OK;
-  if (!x || !x_q8) return WQ_EINVAL;
-  if (k % 32 != 0) return WQ_ESHAPE;
-  if (!aligned(x, 16) || !aligned(x_q8, 4)) return WQ_EALIGN;
-  if (mul_sat(c, k) / 256 + 1 > kMaxGrid) return WQ_ESHAPE;
-  return hip_status(wq::launch_quantize_q8_1(x, c, k, x_q8, as_stream(stream)));
+  return quantize_q8_1(x, c, k, x_q8, false, stream);
+}
+
+int wq_quantize_q8_1_pt(const float* x, int64_t c, int64_t k, uint8_t* x_pt, void* stream) {
+  return quantize_q8_1(x, c, k, x_pt, true, stream);
 }
 
 
@@ -195,7 +227,16 @@ int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int
   bool launch = false;
   const int v = check_gemv_ternary(w_blocks, x_q8, n, k, c, out, &launch);
   if (v != WQ_OK || !launch) return v;
-  return hip_status(wq::launch_gemv_ternary(w_blocks, x_q8, n, k, c, out, as_stream(stream)));
+  return hip_status(wq::launch_gemv_ternary(w_blocks, x_q8, false, n, k, c, out, as_stream(stream)));
+}
+
+int wq_gemv_ternary_pt(const uint8_t* w_blocks, const uint8_t* x_pt, int64_t n, int64_t k, int64_t c,
+                       float* out, void* stream) {
+  bool launch = false;
+  const int v = check_gemv_ternary(w_blocks, x_pt, n, k, c, out, &launch);
+  if (v != WQ_OK || !launch) return v;
+  if (k > (int64_t(1) << 30)) return WQ_ESHAPE;  // a column's plane offsets in 32 bits
+  return hip_status(wq::launch_gemv_ternary(w_blocks, x_pt, true, n, k, c, out, as_stream(stream)));
 }
 
 int wq_gemv_ternary_noalloc(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k,
@@ -207,28 +248,21 @@ int wq_gemv_ternary_noalloc(const uint8_t* w_blocks, const uint8_t* x_q8, int64_
   return hip_status(wq::launch_gemv_ternary_noalloc(w_blocks, x_q8, n, k, c, out, as_stream(stream)));
 }
 
+
 int wq_gemv_ternary_ptq1_1(const uint8_t* superblocks, const uint8_t* codebook,
                            const int32_t* esc_idx, const uint8_t* esc_patt, int64_t n_esc,
                            const uint8_t* x_q8, int64_t n, int64_t k, int64_t c, float* out,
                            void* stream) {
-  if (n < 0 || k < 0 || c < 0 || n_esc < 0) return WQ_EINVAL;
-  if (n == 0 || c == 0) return WQ_OK;
-  if (!superblocks || !codebook || !x_q8 || !out || (n_esc > 0 && (!esc_idx || !esc_patt)))
-    return WQ_EINVAL;
-  // superblocks of 8 blocks; x of one column must fit in LDS beside the tables
-  if (k == 0 || k % 1024 != 0 || k > 65536) return WQ_ESHAPE;
-  if (n_esc > 2048) return WQ_EUNSUPPORTED;  // escape table staged in LDS
-  if (n >= (int64_t(1) << 30) || mul_sat(mul_sat(n, k / 128), 28) >= (int64_t(1) << 31))
-    return WQ_ESHAPE;
-  if (c >= 64) {  // the matrix-core product: activations' 32-bit offsets and the tile grid
-    if (mul_sat(mul_sat(c, k / 32), 36) >= (int64_t(1) << 31)) return WQ_ESHAPE;
-    if (mul_sat(c / 128 + 1, n / 128 + 1) > kMaxGrid) return WQ_ESHAPE;
-  }
-  if (!aligned(superblocks, 4) || !aligned(codebook, 4) || !aligned(x_q8, 4) ||
-      !aligned(out, c >= 64 ? 16 : 4) || (n_esc > 0 && (!aligned(esc_idx, 4) || !aligned(esc_patt, 4))))
-    return WQ_EALIGN;
-  return hip_status(wq::launch_gemv_ternary_sb(superblocks, codebook, esc_idx, esc_patt, n_esc, x_q8,
-                                               n, k, c, out, as_stream(stream)));
+  return gemv_ternary_ptq1_1(superblocks, codebook, esc_idx, esc_patt, n_esc, x_q8, false, n, k, c, out,
+                             stream);
+}
+
+int wq_gemv_ternary_ptq1_1_pt(const uint8_t* superblocks, const uint8_t* codebook,
+                              const int32_t* esc_idx, const uint8_t* esc_patt, int64_t n_esc,
+                              const uint8_t* x_pt, int64_t n, int64_t k, int64_t c, float* out,
+                              void* stream) {
+  return gemv_ternary_ptq1_1(superblocks, codebook, esc_idx, esc_patt, n_esc, x_pt, true, n, k, c, out,
+                             stream);
 }
 
 }  // extern "C"

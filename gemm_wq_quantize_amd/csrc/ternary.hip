@@ -24,6 +24,47 @@ namespace {
 constexpr int PT_BYTES = 28;
 constexpr int Q8_BYTES = 36;
 
+// Activations come in one of two layouts, chosen at compile time (PT) so
+// that each kernel's record-order build is unchanged by the other.  A column
+// of x is nsb = k / 32 block_q8_1 records (36 bytes each) in record order.
+// In the PT layout (Ternary post, section 3.1) the same bytes are regrouped:
+// block sb is sub-block j = sb & 3 of 128-element block i = sb >> 2, its q
+// fill slot i of planes 2 j and 2 j + 1 (k / 128 slots of 16 bytes per
+// plane) and its (d, s) word is word j of slot i of plane 8.  Both layouts
+// take 36 bytes per block, so columns start at the same offsets.
+//
+// Byte offsets of block sb from its column's start in the PT layout: its
+// (d, s) word, q[0..15] and q[16..31].
+struct XBlk {
+  uint32_t ds, q0, q1;
+};
+__device__ __forceinline__ XBlk pt_block(int nsb, int sb) {
+  const int nb = nsb >> 2, i = sb >> 2, j = sb & 3;
+  return {(uint32_t)(16 * (8 * nb + i) + 4 * j), (uint32_t)(16 * (2 * j * nb + i)),
+          (uint32_t)(16 * ((2 * j + 1) * nb + i))};
+}
+
+// The nine words of block sb of column col, (d, s) first.
+template <bool PT>
+__device__ __forceinline__ void xq_load(const uint8_t* __restrict__ xq, int64_t col, int nsb, int64_t sb,
+                                        uint32_t& hd, uint32_t (&q)[8]) {
+  if constexpr (PT) {
+    const uint8_t* cb = xq + col * nsb * Q8_BYTES;
+    const XBlk xb = pt_block(nsb, (int)sb);
+    hd = *reinterpret_cast<const uint32_t*>(cb + xb.ds);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[i] = *reinterpret_cast<const uint32_t*>(cb + xb.q0 + 4 * i);
+      q[4 + i] = *reinterpret_cast<const uint32_t*>(cb + xb.q1 + 4 * i);
+    }
+  } else {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(xq + (col * nsb + sb) * Q8_BYTES);
+    hd = src[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = src[1 + i];
+  }
+}
+
 // ---------------------------------------------------------------- packing
 __global__ __launch_bounds__(256) void k_pack_ptq1_0(const int8_t* __restrict__ trits,
                                                      const uint16_t* __restrict__ d,
@@ -60,9 +101,10 @@ __global__ __launch_bounds__(256) void k_pack_ptq1_0(const int8_t* __restrict__ 
 
 // ---------------------------------------------------------------- q8_1
 // One 32-lane team per block of 32 activations.
+template <bool PT>
 __global__ __launch_bounds__(256) void k_quantize_q8_1(const float* __restrict__ x,
                                                        uint8_t* __restrict__ out,
-                                                       int64_t nblocks) {
+                                                       int64_t nblocks, int nsb) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t b = gid >> 5;
   const int lane = threadIdx.x & 31;
@@ -83,11 +125,20 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float* __restrict__
 #pragma unroll
   for (int off = 16; off > 0; off >>= 1) qs += __shfl_xor(qs, off);
   if (!active) return;
-  uint8_t* blk = out + b * Q8_BYTES;
-  blk[4 + lane] = (uint8_t)(int8_t)q;
+  uint8_t* blk = out + b * Q8_BYTES;  // the record (record order)
+  uint32_t* dsw = reinterpret_cast<uint32_t*>(blk);
+  if constexpr (PT) {                 // the column's planes
+    const int64_t col = b / nsb;
+    uint8_t* cb = out + col * nsb * Q8_BYTES;
+    const XBlk xb = pt_block(nsb, (int)(b - col * nsb));
+    cb[(lane < 16 ? xb.q0 : xb.q1) + (lane & 15)] = (uint8_t)(int8_t)q;
+    dsw = reinterpret_cast<uint32_t*>(cb + xb.ds);
+  } else {
+    blk[4 + lane] = (uint8_t)(int8_t)q;
+  }
   if (lane == 0) {
     const uint32_t sbits = f32_to_f16_rne(dv * (float)qs);
-    *reinterpret_cast<uint32_t*>(blk) = dbits | sbits << 16;
+    *dsw = dbits | sbits << 16;
   }
 }
 
@@ -122,7 +173,7 @@ __device__ __forceinline__ void transpose4(uint32_t l0, uint32_t l1, uint32_t l2
   d3 = __builtin_amdgcn_perm(e, c, 0x07060302u);
 }
 
-template <int C>
+template <int C, bool PT>
 __global__ __launch_bounds__(256) void k_gemv_ternary(const uint32_t* __restrict__ w,
                                                       const uint8_t* __restrict__ xq,
                                                       float* __restrict__ out, int64_t n,
@@ -167,10 +218,14 @@ __global__ __launch_bounds__(256) void k_gemv_ternary(const uint32_t* __restrict
       uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       uint32_t hd = 0;
       if (col < c && gsb < k / 32) {
-        const uint32_t* s = reinterpret_cast<const uint32_t*>(xq + ((int64_t)col * (k / 32) + gsb) * Q8_BYTES);
-        hd = s[0];
+        if constexpr (PT) {
+          xq_load<true>(xq, col, (int)(k / 32), gsb, hd, q);
+        } else {
+          const uint32_t* s = reinterpret_cast<const uint32_t*>(xq + ((int64_t)col * (k / 32) + gsb) * Q8_BYTES);
+          hd = s[0];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = s[1 + i];
+          for (int i = 0; i < 8; ++i) q[i] = s[1 + i];
+        }
       }
       uint4* dst = &xs[(col * T_K + sb * 32) / 16];
       dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
@@ -292,7 +347,7 @@ __device__ __forceinline__ void tern_lut_init(uint32_t* lut) {
 // One-time staging of a workgroup's LDS: the digit table in LUT_COPIES
 // interleaved copies and the activations (x blocks padded to XB_WORDS words,
 // per-32 sum of q and d).  Columns c..C-1 stage zeros.
-template <int C>
+template <int C, bool PT>
 __device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsum, float* xd,
                                            const uint8_t* __restrict__ xq, int bpr, int nsb, int c) {
   tern_lut_init(lut);
@@ -301,10 +356,7 @@ __device__ __forceinline__ void tern_stage(uint32_t* lut, uint32_t* xs, int* xsu
     const int col = idx / nsb, sb = idx - col * nsb;
     uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0}, hd = 0;
     if (col < c) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(xq + ((int64_t)col * nsb + sb) * Q8_BYTES);
-      hd = src[0];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = src[1 + i];
+      xq_load<PT>(xq, col, nsb, sb, hd, q);
     }
     uint32_t* dst = xs + (col * bpr + (sb >> 2)) * XB_WORDS + (sb & 3) * 8;
     int sum = 0;
@@ -550,7 +602,7 @@ __host__ __device__ constexpr int tm_record(int C) {
 // superblock; lane q % 8 decodes sub-block q % 8 from its 24 qs bytes and the
 // superblock's last 24 bytes), with the codebook and escape tables staged in
 // LDS after the x records.
-template <int C, int D, bool SB>
+template <int C, int D, bool SB, bool PT>
 __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __restrict__ w,
                                                            const uint8_t* __restrict__ xq,
                                                            float* __restrict__ out, int n, int k,
@@ -616,7 +668,10 @@ __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __res
   // x blocks (q8_1, 36 bytes) of the staging: the first TM_XPRE per lane
   // are loaded before the weight prologue, since a wave's loads complete in
   // issue order and the staging would otherwise wait for its weights.  The
-  // order is rotated per workgroup: every CU reads the same x.
+  // order is rotated per workgroup: every CU reads the same x.  A block is
+  // three loads in either layout: 16 + 16 + 4 bytes from words 0, 4 and 8 of
+  // a record, or the two 16-byte plane slots of its q (words 1 and 5) and its
+  // (d, s) word.
   const int nxb = c * nsb;
   const int xrot = (int)(((uint32_t)b * 2654435761u) % (uint32_t)nxb);
   auto xblock = [&](int i) {
@@ -627,16 +682,28 @@ __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __res
   // its value, and so the wait for it, right behind it)
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)xq, 0, nxb * Q8_BYTES, 0x00020000);
-  uint32_t xpre[TM_XPRE][9];
+  uint32_t xpre[TM_XPRE][9];  // the three loads' words, in load order
 #pragma unroll
   for (int i = 0; i < TM_XPRE; ++i) {
     const int idx = tid + i * TM_NT;
-    const uint32_t o = idx < nxb ? (uint32_t)(xblock(idx) * Q8_BYTES) : T_OOB;
-    const uint4 lo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)o, 0, 0));
-    const uint4 hi = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(o + 16), 0, 0));
+    uint32_t o1, o2, o3;
+    if constexpr (PT) {
+      const int xi = xblock(idx < nxb ? idx : 0), col = xi / nsb;
+      const uint32_t cb = (uint32_t)(col * nsb * Q8_BYTES);
+      const XBlk xb = pt_block(nsb, xi - col * nsb);
+      o1 = idx < nxb ? cb + xb.q0 : T_OOB;
+      o2 = idx < nxb ? cb + xb.q1 : T_OOB;
+      o3 = idx < nxb ? cb + xb.ds : T_OOB;
+    } else {
+      o1 = idx < nxb ? (uint32_t)(xblock(idx) * Q8_BYTES) : T_OOB;
+      o2 = o1 + 16;
+      o3 = o1 + 32;
+    }
+    const uint4 lo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)o1, 0, 0));
+    const uint4 hi = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)o2, 0, 0));
     xpre[i][0] = lo.x; xpre[i][1] = lo.y; xpre[i][2] = lo.z; xpre[i][3] = lo.w;
     xpre[i][4] = hi.x; xpre[i][5] = hi.y; xpre[i][6] = hi.z; xpre[i][7] = hi.w;
-    xpre[i][8] = __builtin_amdgcn_raw_buffer_load_b32(xrs, (int)(o + 32), 0, 0);
+    xpre[i][8] = __builtin_amdgcn_raw_buffer_load_b32(xrs, (int)o3, 0, 0);
   }
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
@@ -665,14 +732,32 @@ __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __res
 #pragma unroll
   for (int i = 0; i < TM_XPRE; ++i) {
     const int idx = tid + i * TM_NT;
-    if (idx < nxb) put_x(xblock(idx), xpre[i]);
+    if (idx >= nxb) continue;
+    if constexpr (PT) {
+      // words in block order: (d, s), then q (the PT loads brought (d, s) last)
+      uint32_t bk[9];
+      bk[0] = xpre[i][8];
+#pragma unroll
+      for (int j = 1; j < 9; ++j) bk[j] = xpre[i][j - 1];
+      put_x(xblock(idx), bk);
+    } else {
+      put_x(xblock(idx), xpre[i]);
+    }
   }
   for (int idx = tid + TM_XPRE * TM_NT; idx < nxb; idx += TM_NT) {  // the rest (wide x)
     const int xi = xblock(idx);
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(xq + (int64_t)xi * Q8_BYTES);
     uint32_t bk[9];
+    if constexpr (PT) {
+      const int col = xi / nsb;
+      uint32_t q8[8];
+      xq_load<true>(xq, col, nsb, xi - col * nsb, bk[0], q8);
 #pragma unroll
-    for (int j = 0; j < 9; ++j) bk[j] = src[j];
+      for (int j = 0; j < 8; ++j) bk[1 + j] = q8[j];
+    } else {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(xq + (int64_t)xi * Q8_BYTES);
+#pragma unroll
+      for (int j = 0; j < 9; ++j) bk[j] = src[j];
+    }
     put_x(xi, bk);
   }
   if constexpr (SB) tern_stage_sb<TM_NT>(tbl, sbt);
@@ -800,7 +885,7 @@ __global__ __launch_bounds__(TM_NT) void k_gemv_ternary_mq(const uint32_t* __res
 // SB: the weights are PTQ1_1 superblocks (LPR = 8: an item is one superblock
 // of each row, lane sub its sub-block), with the codebook and the escape
 // table staged in LDS after the activations.
-template <int C, int D, int LPR, bool SB>
+template <int C, int D, int LPR, bool SB, bool PT>
 __global__ __launch_bounds__(256, SB ? TP_WAVES_SB : TP_WAVES) void k_gemv_ternary_persist(const uint32_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
                                                               float* __restrict__ out, int n, int k,
@@ -853,7 +938,7 @@ __global__ __launch_bounds__(256, SB ? TP_WAVES_SB : TP_WAVES) void k_gemv_terna
 
   // ---- one-time staging: digit table and the activations (and the
   // superblock tables)
-  tern_stage<C>(lut, xs, xsum, xd, xq, bpr, nsb, c);
+  tern_stage<C, PT>(lut, xs, xsum, xd, xq, bpr, nsb, c);
   if constexpr (SB) tern_stage_sb(tbl, sbt);
   __syncthreads();
 
@@ -918,7 +1003,7 @@ __global__ __launch_bounds__(256, SB ? TP_WAVES_SB : TP_WAVES) void k_gemv_terna
 // one workgroup (4 / S row groups per 256-lane workgroup, not persistent), so
 // S times more waves run, and the S partial sums of a row are added in LDS in
 // part order.
-template <int C, int D, int S, bool SB>
+template <int C, int D, int S, bool SB, bool PT>
 __global__ __launch_bounds__(256, SB ? TP_WAVES_SB : TP_WAVES) void k_gemv_ternary_ksplit(const uint32_t* __restrict__ w,
                                                              const uint8_t* __restrict__ xq,
                                                              float* __restrict__ out, int n, int k,
@@ -971,7 +1056,7 @@ __global__ __launch_bounds__(256, SB ? TP_WAVES_SB : TP_WAVES) void k_gemv_terna
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
 
-  tern_stage<C>(lut, xs, xsum, xd, xq, bpr, nsb, c);
+  tern_stage<C, PT>(lut, xs, xsum, xd, xq, bpr, nsb, c);
   if constexpr (SB) tern_stage_sb(tbl, sbt);
   __syncthreads();
 
@@ -1118,13 +1203,24 @@ __global__ __launch_bounds__(256) void k_unpack_ptq1_1_fp4(const uint32_t* __res
 }
 
 // block_q8_1 -> fp8 pairs [c][2k] and float d_x [c][k/32]: one lane per block
-__global__ __launch_bounds__(256) void k_unpack_q8_1_fp8(const uint32_t* __restrict__ xq, int64_t nb,
-                                                         uint4* __restrict__ q8, float* __restrict__ dx) {
+template <bool PT>
+__global__ __launch_bounds__(256) void k_unpack_q8_1_fp8(const uint8_t* __restrict__ xq, int64_t nb,
+                                                         uint4* __restrict__ q8, float* __restrict__ dx,
+                                                         int nsb) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nb) return;
   uint32_t v[9];
+  if constexpr (PT) {
+    const int col = (int)b / nsb;  // nb * 36 < 2^31
+    uint32_t xw[8];
+    xq_load<true>(xq, col, nsb, (int)b - col * nsb, v[0], xw);
 #pragma unroll
-  for (int q = 0; q < 9; ++q) v[q] = xq[b * 9 + q];
+    for (int q = 0; q < 8; ++q) v[1 + q] = xw[q];
+  } else {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(xq) + b * 9;  // the block's record
+#pragma unroll
+    for (int q = 0; q < 9; ++q) v[q] = src[q];
+  }
   // k takes the fp8 (e4m3) pair (ql, 16 qh), both exact (the hardware's own
   // conversion, so the encoding is the one the products read)
   uint32_t o[16];
@@ -1367,10 +1463,14 @@ hipError_t launch_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n,
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* xq, hipStream_t s) {
+hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* xq, bool pt,
+                                hipStream_t s) {
   const int64_t nb = c * (k / 32);
-  hipLaunchKernelGGL(k_quantize_q8_1, dim3((unsigned)((nb * 32 + 255) / 256)), dim3(256), 0, s, x,
-                     xq, nb);
+  const dim3 grid((unsigned)((nb * 32 + 255) / 256));
+  if (pt)
+    hipLaunchKernelGGL(k_quantize_q8_1<true>, grid, dim3(256), 0, s, x, xq, nb, (int)(k / 32));
+  else
+    hipLaunchKernelGGL(k_quantize_q8_1<false>, grid, dim3(256), 0, s, x, xq, nb, (int)(k / 32));
   return hipGetLastError();
 }
 
@@ -1385,44 +1485,48 @@ constexpr int TP_D = 2;
 // launch) otherwise.  SB: PTQ1_1 superblocks with their tables.
 template <int C, bool SB>
 hipError_t launch_ternary_ksplit(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k,
-                                 int64_t c, float* out, const SbTables& sbt, hipStream_t s) {
+                                 int64_t c, float* out, const SbTables& sbt, bool pt, hipStream_t s) {
   constexpr int S = 2;
   const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8 +
                       4 * 8 * C * 4 + (SB ? sb_lds_words(sbt.n_esc) * 4 : 0);
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
-  static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
-  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S, SB>),
-                                         lds_ok, 160 * 1024);
+  const void* fn = pt ? reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S, SB, true>)
+                      : reinterpret_cast<const void*>(&k_gemv_ternary_ksplit<C, TP_D, S, SB, false>);
+  static std::atomic<uint64_t> lds_ok[2];  // devices where the kernel may use all of the LDS
+  const hipError_t e = allow_dynamic_lds(fn, lds_ok[pt], 160 * 1024);
   if (e != hipSuccess) return e;
   const int64_t nrg = (n + 7) / 8;
   const int64_t grid = (nrg + (4 / S) - 1) / (4 / S);
-  hipLaunchKernelGGL((k_gemv_ternary_ksplit<C, TP_D, S, SB>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
-                     wp, xq, out, (int)n, (int)k, (int)c, sbt);
-  return hipGetLastError();
+  int n_arg = (int)n, k_arg = (int)k, c_arg = (int)c;
+  SbTables t = sbt;
+  void* args[] = {const_cast<uint32_t**>(&wp), const_cast<uint8_t**>(&xq), &out, &n_arg, &k_arg, &c_arg, &t};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, (size_t)lds, s);
 }
 
 // Persistent launch when x fits in LDS; returns hipErrorInvalidValue (no
 // launch) otherwise.
 template <int C, bool SB>
 hipError_t launch_ternary_persist(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k,
-                                  int64_t c, float* out, const SbTables& sbt, hipStream_t s) {
+                                  int64_t c, float* out, const SbTables& sbt, bool pt, hipStream_t s) {
   const int64_t lds = 256 * LUT_COPIES * 4 + C * (k / 128) * XB_WORDS * 4 + C * (k / 32) * 8 +
                       (SB ? sb_lds_words(sbt.n_esc) * 4 : 0);
   if (lds > 160 * 1024 || n * (k / 128) * PT_BYTES >= (int64_t(1) << 31) || n >= (int64_t(1) << 30))
     return hipErrorInvalidValue;
-  static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
-  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR, SB>),
-                                         lds_ok, 160 * 1024);
+  const void* fn = pt ? reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR, SB, true>)
+                      : reinterpret_cast<const void*>(&k_gemv_ternary_persist<C, TP_D, TP_LPR, SB, false>);
+  static std::atomic<uint64_t> lds_ok[2];  // devices where the kernel may use all of the LDS
+  const hipError_t e = allow_dynamic_lds(fn, lds_ok[pt], 160 * 1024);
   if (e != hipSuccess) return e;
   const int64_t nrg = (n + 64 / TP_LPR - 1) / (64 / TP_LPR);
   // workgroups resident at once: LDS and the waves per SIMD the register
   // budget allows
   const int per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(SB ? TP_WAVES_SB : TP_WAVES, (160 * 1024) / lds));
   const int64_t grid = std::min<int64_t>((nrg + 3) / 4, (int64_t)device_cu_count() * per_cu);
-  hipLaunchKernelGGL((k_gemv_ternary_persist<C, TP_D, TP_LPR, SB>), dim3((unsigned)grid), dim3(256), (size_t)lds, s,
-                     wp, xq, out, (int)n, (int)k, (int)c, sbt);
-  return hipGetLastError();
+  int n_arg = (int)n, k_arg = (int)k, c_arg = (int)c;
+  SbTables t = sbt;
+  void* args[] = {const_cast<uint32_t**>(&wp), const_cast<uint8_t**>(&xq), &out, &n_arg, &k_arg, &c_arg, &t};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, (size_t)lds, s);
 }
 
 // Largest number of 8-row groups one wave of k_gemv_ternary_mq touches, over
@@ -1444,7 +1548,7 @@ int tm_slots(int64_t n, int grid, int nit) {
 // hipErrorInvalidValue (no launch) otherwise.
 template <int C, bool SB>
 hipError_t launch_ternary_mq(const uint32_t* wp, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
-                             float* out, const SbTables& sbt, hipStream_t s) {
+                             float* out, const SbTables& sbt, bool pt, hipStream_t s) {
   constexpr int D = 2;
   if (n >= (int64_t(1) << 30) || k >= (int64_t(1) << 24)) return hipErrorInvalidValue;
   const int64_t bpr = k / 128;
@@ -1461,9 +1565,10 @@ hipError_t launch_ternary_mq(const uint32_t* wp, const uint8_t* xq, int64_t n, i
       65536, TM_LUT_BYTES + bpr * tm_record(C) + (SB ? sb_lds_words(sbt.n_esc) * 4 : 0) +
                  (int64_t)TM_NW * spw * 8 * C * 4 + TM_NW * 3 * 4);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const void* fn = reinterpret_cast<const void*>(&k_gemv_ternary_mq<C, D, SB>);
-  static std::atomic<uint64_t> lds_ok;  // devices where the kernel may use all of the LDS
-  const hipError_t e = allow_dynamic_lds(fn, lds_ok, 160 * 1024);
+  const void* fn = pt ? reinterpret_cast<const void*>(&k_gemv_ternary_mq<C, D, SB, true>)
+                      : reinterpret_cast<const void*>(&k_gemv_ternary_mq<C, D, SB, false>);
+  static std::atomic<uint64_t> lds_ok[2];  // devices where the kernel may use all of the LDS
+  const hipError_t e = allow_dynamic_lds(fn, lds_ok[pt], 160 * 1024);
   if (e != hipSuccess) return e == hipErrorInvalidValue ? hipErrorNotSupported : e;
   int n_arg = (int)n, k_arg = (int)k, c_arg = (int)c, spw_arg = spw;
   SbTables t = sbt;
@@ -1473,7 +1578,7 @@ hipError_t launch_ternary_mq(const uint32_t* wp, const uint8_t* xq, int64_t n, i
 
 // Up to 16 columns on the vector units.
 hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
-                                 int64_t c, float* out, hipStream_t s) {
+                                 int64_t c, float* out, bool pt, hipStream_t s) {
   const uint32_t* wp0 = reinterpret_cast<const uint32_t*>(w);
   {
     // one column: the K-split kernel (wider splits spilled registers; the
@@ -1482,27 +1587,33 @@ hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n,
     const SbTables none{};
     hipError_t e = hipErrorInvalidValue;
     if (c == 1) {
-      e = launch_ternary_ksplit<1, false>(wp0, xq, n, k, c, out, none, s);
+      e = launch_ternary_ksplit<1, false>(wp0, xq, n, k, c, out, none, pt, s);
       if (e != hipErrorInvalidValue) return e;
     }
     switch (c) {
       case 1: break;
-      case 2: e = launch_ternary_mq<2, false>(wp0, xq, n, k, c, out, none, s); break;
-      case 3: case 4: e = launch_ternary_mq<4, false>(wp0, xq, n, k, c, out, none, s); break;
-      default: if (c <= 8) e = launch_ternary_mq<8, false>(wp0, xq, n, k, c, out, none, s); break;
+      case 2: e = launch_ternary_mq<2, false>(wp0, xq, n, k, c, out, none, pt, s); break;
+      case 3: case 4: e = launch_ternary_mq<4, false>(wp0, xq, n, k, c, out, none, pt, s); break;
+      default: if (c <= 8) e = launch_ternary_mq<8, false>(wp0, xq, n, k, c, out, none, pt, s); break;
     }
     if (e != hipErrorInvalidValue) return e;
     switch (c) {
       case 1: break;
-      case 2: e = launch_ternary_persist<2, false>(wp0, xq, n, k, c, out, none, s); break;
-      case 3: case 4: e = launch_ternary_persist<4, false>(wp0, xq, n, k, c, out, none, s); break;
-      default: if (c <= 8) e = launch_ternary_persist<8, false>(wp0, xq, n, k, c, out, none, s); break;
+      case 2: e = launch_ternary_persist<2, false>(wp0, xq, n, k, c, out, none, pt, s); break;
+      case 3: case 4: e = launch_ternary_persist<4, false>(wp0, xq, n, k, c, out, none, pt, s); break;
+      default: if (c <= 8) e = launch_ternary_persist<8, false>(wp0, xq, n, k, c, out, none, pt, s); break;
     }
     if (e != hipErrorInvalidValue) return e;
   }
   const unsigned blocks = (unsigned)((n + 31) / 32);
   const uint32_t* wp = reinterpret_cast<const uint32_t*>(w);
-#define WQ_TG(C) hipLaunchKernelGGL(k_gemv_ternary<C>, dim3(blocks), dim3(256), 0, s, wp, xq, out, n, k, (int)c)
+#define WQ_TG(C)                                                                                    \
+  do {                                                                                              \
+    if (pt)                                                                                         \
+      hipLaunchKernelGGL((k_gemv_ternary<C, true>), dim3(blocks), dim3(256), 0, s, wp, xq, out, n, k, (int)c); \
+    else                                                                                            \
+      hipLaunchKernelGGL((k_gemv_ternary<C, false>), dim3(blocks), dim3(256), 0, s, wp, xq, out, n, k, (int)c); \
+  } while (0)
   switch (c) {
     case 1: WQ_TG(1); break;
     case 2: WQ_TG(2); break;
@@ -1520,13 +1631,17 @@ hipError_t launch_ternary_narrow(const uint8_t* w, const uint8_t* xq, int64_t n,
 size_t gemm_ternary_workspace(int64_t n, int64_t k, int64_t c) { return tern_ws(n, k, c).bytes; }
 
 // x unpacked and the product, once the weights are in the workspace
-static hipError_t gemm_ternary_unpacked(const uint8_t* xq, int64_t n, int64_t k, int64_t c, float* out,
-                                        uint8_t* base, hipStream_t s) {
+static hipError_t gemm_ternary_unpacked(const uint8_t* xq, bool pt, int64_t n, int64_t k, int64_t c,
+                                        float* out, uint8_t* base, hipStream_t s) {
   const TernWs L = tern_ws(n, k, c);
   const int64_t nbx = c * (k / 32);
-  hipLaunchKernelGGL(k_unpack_q8_1_fp8, dim3((unsigned)((nbx + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<const uint32_t*>(xq), nbx, reinterpret_cast<uint4*>(base + L.x),
-                     reinterpret_cast<float*>(base + L.dx));
+  const dim3 ugrid((unsigned)((nbx + 255) / 256));
+  if (pt)
+    hipLaunchKernelGGL(k_unpack_q8_1_fp8<true>, ugrid, dim3(256), 0, s, xq, nbx,
+                       reinterpret_cast<uint4*>(base + L.x), reinterpret_cast<float*>(base + L.dx), (int)(k / 32));
+  else
+    hipLaunchKernelGGL(k_unpack_q8_1_fp8<false>, ugrid, dim3(256), 0, s, xq, nbx,
+                       reinterpret_cast<uint4*>(base + L.x), reinterpret_cast<float*>(base + L.dx), (int)(k / 32));
   const int tiles_m = (int)((c + TG_BM - 1) / TG_BM), tiles_n = (int)((n + TG_BN - 1) / TG_BN);
   hipLaunchKernelGGL(k_gemm_ternary, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s, base,
                      reinterpret_cast<const float*>(base + L.dw), base + L.x,
@@ -1534,15 +1649,15 @@ static hipError_t gemm_ternary_unpacked(const uint8_t* xq, int64_t n, int64_t k,
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
-                               float* out, void* ws, hipStream_t s) {
+hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, bool pt, int64_t n, int64_t k,
+                               int64_t c, float* out, void* ws, hipStream_t s) {
   const TernWs L = tern_ws(n, k, c);
   uint8_t* base = static_cast<uint8_t*>(ws);
   const int64_t nbw = n * (k / 128);
   hipLaunchKernelGGL(k_unpack_ptq1_0_fp4, dim3((unsigned)((nbw + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(w), nbw, reinterpret_cast<uint4*>(base),
                      reinterpret_cast<float*>(base + L.dw));
-  return gemm_ternary_unpacked(xq, n, k, c, out, base, s);
+  return gemm_ternary_unpacked(xq, pt, n, k, c, out, base, s);
 }
 
 // The GEMM's workspace comes from a memory pool of this library's own, one
@@ -1603,12 +1718,12 @@ static hipError_t scratch_address(void** ptr) {
 
 hipError_t launch_gemv_ternary_noalloc(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                        int64_t c, float* out, hipStream_t s) {
-  if (c < 64) return launch_gemv_ternary(w, xq, n, k, c, out, s);  // no workspace below 64 columns
+  if (c < 64) return launch_gemv_ternary(w, xq, false, n, k, c, out, s);  // no workspace below 64 columns
   if (gemm_ternary_workspace(n, k, c) > kTernScratchBytes) return hipErrorInvalidValue;
   void* ws = nullptr;
   const hipError_t e = scratch_address(&ws);
   if (e != hipSuccess) return e;
-  return launch_gemm_ternary(w, xq, n, k, c, out, ws, s);
+  return launch_gemm_ternary(w, xq, false, n, k, c, out, ws, s);
 }
 
 // run(ws) with a workspace of `bytes` from the pool, freed in stream order
@@ -1625,15 +1740,15 @@ static hipError_t with_pool_workspace(size_t bytes, hipStream_t s, F run) {
   return e != hipSuccess ? e : f;
 }
 
-hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
+hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, bool pt, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s) {
   if (c >= 64)  // a batch wide enough for the matrix cores
     return with_pool_workspace(gemm_ternary_workspace(n, k, c), s,
-                               [&](void* ws) { return launch_gemm_ternary(w, xq, n, k, c, out, ws, s); });
+                               [&](void* ws) { return launch_gemm_ternary(w, xq, pt, n, k, c, out, ws, s); });
   // 17..63 columns: passes of at most 16 over x[c0:c0+16] -> out[c0:c0+16]
   for (int64_t c0 = 0; c0 < c; c0 += 16) {
     const hipError_t e = launch_ternary_narrow(w, xq + c0 * (k / 32) * Q8_BYTES, n, k,
-                                               std::min<int64_t>(16, c - c0), out + c0 * n, s);
+                                               std::min<int64_t>(16, c - c0), out + c0 * n, pt, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1644,7 +1759,7 @@ hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, i
 // the vector kernels); hipErrorInvalidValue when even one column does not
 // fit (the entry point bounds k so that it does).
 hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, const int32_t* esc_idx,
-                                  const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq,
+                                  const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq, bool pt,
                                   int64_t n, int64_t k, int64_t c, float* out, hipStream_t s) {
   const uint32_t* wp = reinterpret_cast<const uint32_t*>(w);
   const SbTables t{codebook, esc_idx, esc_patt, (int)n_esc};
@@ -1656,7 +1771,7 @@ hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, con
       hipLaunchKernelGGL(k_unpack_ptq1_1_fp4, dim3((unsigned)((nbw + 255) / 256)), dim3(256), 0, s, wp,
                          nbw, (int)(k / 128), t, reinterpret_cast<uint4*>(base),
                          reinterpret_cast<float*>(base + L.dw));
-      return gemm_ternary_unpacked(xq, n, k, c, out, base, s);
+      return gemm_ternary_unpacked(xq, pt, n, k, c, out, base, s);
     });
   }
   for (int64_t c0 = 0; c0 < c; ) {
@@ -1668,20 +1783,20 @@ hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, con
     if (left == 1) {
       // the matrix-core kernel (its two-column form, column 0 repeated: 7%
       // faster than the K-split kernel here), else the K-split kernel
-      e = launch_ternary_mq<2, true>(wp, xp, n, k, 1, op, t, s);
-      if (e == hipErrorInvalidValue) e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, s);
+      e = launch_ternary_mq<2, true>(wp, xp, n, k, 1, op, t, pt, s);
+      if (e == hipErrorInvalidValue) e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, pt, s);
       done = 1;
     } else {
       // widest pass first, the matrix-core kernel before the vector one; a
       // pass that does not fit its x in LDS launches nothing
       const int64_t w8 = std::min<int64_t>(8, left), w4 = std::min<int64_t>(4, left);
-      if (left >= 5) { e = launch_ternary_mq<8, true>(wp, xp, n, k, w8, op, t, s); done = w8; }
-      if (e == hipErrorInvalidValue && left >= 5) { e = launch_ternary_persist<8, true>(wp, xp, n, k, w8, op, t, s); done = w8; }
-      if (e == hipErrorInvalidValue && left >= 3) { e = launch_ternary_mq<4, true>(wp, xp, n, k, w4, op, t, s); done = w4; }
-      if (e == hipErrorInvalidValue && left >= 3) { e = launch_ternary_persist<4, true>(wp, xp, n, k, w4, op, t, s); done = w4; }
-      if (e == hipErrorInvalidValue) { e = launch_ternary_mq<2, true>(wp, xp, n, k, 2, op, t, s); done = 2; }
-      if (e == hipErrorInvalidValue) { e = launch_ternary_persist<2, true>(wp, xp, n, k, 2, op, t, s); done = 2; }
-      if (e == hipErrorInvalidValue) { e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, s); done = 1; }
+      if (left >= 5) { e = launch_ternary_mq<8, true>(wp, xp, n, k, w8, op, t, pt, s); done = w8; }
+      if (e == hipErrorInvalidValue && left >= 5) { e = launch_ternary_persist<8, true>(wp, xp, n, k, w8, op, t, pt, s); done = w8; }
+      if (e == hipErrorInvalidValue && left >= 3) { e = launch_ternary_mq<4, true>(wp, xp, n, k, w4, op, t, pt, s); done = w4; }
+      if (e == hipErrorInvalidValue && left >= 3) { e = launch_ternary_persist<4, true>(wp, xp, n, k, w4, op, t, pt, s); done = w4; }
+      if (e == hipErrorInvalidValue) { e = launch_ternary_mq<2, true>(wp, xp, n, k, 2, op, t, pt, s); done = 2; }
+      if (e == hipErrorInvalidValue) { e = launch_ternary_persist<2, true>(wp, xp, n, k, 2, op, t, pt, s); done = 2; }
+      if (e == hipErrorInvalidValue) { e = launch_ternary_ksplit<1, true>(wp, xp, n, k, 1, op, t, pt, s); done = 1; }
     }
     if (e != hipSuccess) return e;
     c0 += done;

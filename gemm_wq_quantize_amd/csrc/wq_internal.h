@@ -136,15 +136,16 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint8_t* b, const uint16_t
 
 hipError_t launch_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
                               uint8_t* blocks, hipStream_t s);
-hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* xq,
+// pt: activations in the PT plane layout instead of block_q8_1 records
+hipError_t launch_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* xq, bool pt,
                                 hipStream_t s);
-hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
+hipError_t launch_gemv_ternary(const uint8_t* w, const uint8_t* xq, bool pt, int64_t n, int64_t k,
                                int64_t c, float* out, hipStream_t s);
 // The c >= 64 product with a caller-provided workspace of
 // gemm_ternary_workspace(n, k, c) bytes (256-byte aligned).
 size_t gemm_ternary_workspace(int64_t n, int64_t k, int64_t c);
-hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k, int64_t c,
-                               float* out, void* ws, hipStream_t s);
+hipError_t launch_gemm_ternary(const uint8_t* w, const uint8_t* xq, bool pt, int64_t n, int64_t k,
+                               int64_t c, float* out, void* ws, hipStream_t s);
 // launch_gemv_ternary with the c >= 64 workspace in the library's static
 // scratch (nothing allocated); hipErrorInvalidValue when the workspace
 // exceeds it.
@@ -152,7 +153,7 @@ constexpr size_t kTernScratchBytes = size_t(64) << 20;
 hipError_t launch_gemv_ternary_noalloc(const uint8_t* w, const uint8_t* xq, int64_t n, int64_t k,
                                        int64_t c, float* out, hipStream_t s);
 hipError_t launch_gemv_ternary_sb(const uint8_t* w, const uint8_t* codebook, const int32_t* esc_idx,
-                                  const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq,
+                                  const uint8_t* esc_patt, int64_t n_esc, const uint8_t* xq, bool pt,
                                   int64_t n, int64_t k, int64_t c, float* out, hipStream_t s);
 
 }  // namespace wq

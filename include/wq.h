@@ -52,6 +52,13 @@
  *  bits 2*(e >> 1) .. +1.  Weights are [N][K/128] blocks, row-major.
  *  block_q8_1, 36 bytes per 32 activations: fp16 d, fp16 s = d * sum(q),
  *  int8 q[32].  Activations are [c][K/32] blocks.
+ *  PT layout of the activations ([3.1 data format]; the *_pt entry points):
+ *  the same bytes per column (9K/8), regrouped by 128-element block i
+ *  (K/128 of them) into nine planes of K/128 slots of 16 bytes.  Element e
+ *  (0..127) of block i is byte 16 * ((e / 16) * K/128 + i) + e % 16 (plane
+ *  e / 16); slot i of plane 8 holds the (d, s) words of the block's four
+ *  q8_1 sub-blocks in order (the post draws plane 8 only as "all (d, s)").
+ *  A batch is c consecutive PT arrays.  Requires K % 128 == 0.
  */
 #ifndef WQ_H
 #define WQ_H
@@ -197,6 +204,14 @@ int wq_pack_ptq1_0(const int8_t* trits, const uint16_t* d, int64_t n, int64_t k,
 int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* stream);
 
 /*
+ * wq_quantize_q8_1_pt -- wq_quantize_q8_1 writing the PT plane layout
+ * (Ternary post [3.1]): the same blocks, bytes moved as the format section
+ * above states.  x_pt [c][9k/8] uint8 out.  Requires k % 128 == 0,
+ * k <= 2^30, x 16-byte aligned, x_pt 4-byte aligned.
+ */
+int wq_quantize_q8_1_pt(const float* x, int64_t c, int64_t k, uint8_t* x_pt, void* stream);
+
+/*
  * wq_gemv_ternary -- out[j][r] = sum_b d_w[r][b/4] * d_x[j][b] * S[r][j][b]
  * with the exact integer sums S = sum_{i<32} t * q over each activation
  * block b (Ternary post [3 MMVQ], [3.1], [3.2]).  The stored s of the
@@ -218,6 +233,17 @@ int wq_quantize_q8_1(const float* x, int64_t c, int64_t k, uint8_t* x_q8, void* 
  */
 int wq_gemv_ternary(const uint8_t* w_blocks, const uint8_t* x_q8, int64_t n, int64_t k,
                     int64_t c, float* out, void* stream);
+
+/*
+ * wq_gemv_ternary_pt -- wq_gemv_ternary with the activations in the PT
+ * plane layout (Ternary post [3.1]: the layout the post's mmvq operator
+ * reads x in).  x_pt [c][9k/8] uint8, as wq_quantize_q8_1_pt writes it; the
+ * kernels, limits and errors are wq_gemv_ternary's (k <= 2^30 in addition),
+ * and the results are bit-identical to wq_gemv_ternary on the same blocks in
+ * record order.
+ */
+int wq_gemv_ternary_pt(const uint8_t* w_blocks, const uint8_t* x_pt, int64_t n, int64_t k,
+                       int64_t c, float* out, void* stream);
 
 /*
  * wq_gemv_ternary_noalloc -- wq_gemv_ternary for callers that cannot
@@ -298,6 +324,17 @@ int wq_gemv_ternary_ptq1_1(const uint8_t* superblocks, const uint8_t* codebook,
                            const int32_t* esc_idx, const uint8_t* esc_patt, int64_t n_esc,
                            const uint8_t* x_q8, int64_t n, int64_t k, int64_t c, float* out,
                            void* stream);
+
+/*
+ * wq_gemv_ternary_ptq1_1_pt -- wq_gemv_ternary_ptq1_1 with the activations
+ * in the PT plane layout (Ternary post [3.1]); x_pt [c][9k/8] uint8.  Same
+ * kernels, limits and errors; results bit-identical to
+ * wq_gemv_ternary_ptq1_1 on the same blocks in record order.
+ */
+int wq_gemv_ternary_ptq1_1_pt(const uint8_t* superblocks, const uint8_t* codebook,
+                              const int32_t* esc_idx, const uint8_t* esc_patt, int64_t n_esc,
+                              const uint8_t* x_pt, int64_t n, int64_t k, int64_t c, float* out,
+                              void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("wq_pack_int4", "wq_quantize_pack_int4", "wq_gemv_w4", "wq_gemm_w4a16",
                  "wq_pack_ptq1_0", "wq_quantize_q8_1", "wq_gemv_ternary", "wq_gemv_ternary_noalloc", "wq_status_string",
+                 "wq_quantize_q8_1_pt", "wq_gemv_ternary_pt", "wq_gemv_ternary_ptq1_1_pt",
                  "wq_abi_version", "wq_peak_read", "wq_peak_read_sink_words", "wq_peak_mfma_bf16",
                  "wq_peak_valu_fma"):
         assert want in names
@@ -155,3 +156,22 @@ def test_ptq1_1_validation_without_gpu(lib):
     assert lib.wq_gemv_ternary_ptq1_1(FAKE, FAKE, None, None, 3, FAKE, 8, 1024, 1, FAKE, None) == g.WQ_EINVAL
     assert lib.wq_gemv_ternary_ptq1_1(ODD, FAKE, FAKE, FAKE, 0, FAKE, 8, 1024, 1, FAKE, None) == g.WQ_EALIGN
     assert lib.wq_gemv_ternary_ptq1_1(*args(1024, 0, c=0)) == 0
+
+
+def test_pt_layout_validation_without_gpu(lib):
+    # the PT-layout entry points: the checks of their row-layout twins, and
+    # the quantiser's k a multiple of 128 (whole 128-element blocks)
+    import gemm_wq_quantize_amd as g
+    assert lib.wq_quantize_q8_1_pt(None, 0, 128, None, None) == 0
+    assert lib.wq_quantize_q8_1_pt(FAKE, 2, 96, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_quantize_q8_1_pt(FAKE, 2, 256, None, None) == g.WQ_EINVAL
+    assert lib.wq_quantize_q8_1_pt(ODD, 2, 256, FAKE, None) == g.WQ_EALIGN
+    assert lib.wq_quantize_q8_1_pt(FAKE, 1, (1 << 30) + 128, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary_pt(None, None, 10, 128, 0, None, None) == 0
+    assert lib.wq_gemv_ternary_pt(FAKE, FAKE, 4, 100, 1, FAKE, None) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary_pt(FAKE, ODD, 4, 128, 1, FAKE, None) == g.WQ_EALIGN
+    assert lib.wq_gemv_ternary_pt(FAKE, FAKE, 64, 4096, 1 << 20, FAKE, None) == g.WQ_ESHAPE
+    args = lambda k, ne, c=1: (FAKE, FAKE, FAKE, FAKE, ne, FAKE, 8, k, c, FAKE, None)
+    assert lib.wq_gemv_ternary_ptq1_1_pt(*args(512, 0)) == g.WQ_ESHAPE
+    assert lib.wq_gemv_ternary_ptq1_1_pt(*args(1024, 2049)) == g.WQ_EUNSUPPORTED
+    assert lib.wq_gemv_ternary_ptq1_1_pt(*args(1024, 0, c=0)) == 0

@@ -76,12 +76,15 @@ def test_ternary_gemv(k, n):
 
 
 @pytest.mark.parametrize("k,n,c", [(5120, 4000, 8), (17280, 300, 8), (5120, 4000, 1), (384, 77, 1),
-                                   (17280, 300, 1), (65536, 40, 1), (17280, 300, 6)])
+                                   (17280, 300, 1), (65536, 40, 1), (17280, 300, 6), (12288, 300, 8),
+                                   (24576, 200, 3)])
 def test_ternary_unit_scale_exact(k, n, c):
     # one column: the kernel that splits each row's blocks between two
     # waves (k = 384: three blocks, so the second wave of a row has none);
-    # 8 columns: the matrix-core kernel where x fits its LDS (k = 5120),
-    # past it the persistent vector kernel (8 and 6 columns at k = 17280)
+    # 8 columns: the matrix-core kernel where x and its digit table fit in
+    # LDS (k = 5120), past it the persistent vector kernel (k = 12288; and
+    # 3 columns at k = 24576), past that the tiled vector kernel (8 and 6
+    # columns at k = 17280)
     say("ternary unit scale", k, n, c)
     p = wq_inputs.ternary_gemv(k, n, cmax=8, unit_scale=True)
     wb = gpu_blocks(p.trits, p.d_bits)
