@@ -124,3 +124,56 @@ def test_graph_pack_and_q8_1():
     codes = rand_codes(n, k, gen)
     pk, pk2 = (torch.empty((n, k // 2), dtype=torch.uint8, device="cuda") for _ in range(2))
     replay_matches_eager(lambda o: g.wq_pack_int4(codes, g.LAYOUT_GFX950, o), pk, pk2)
+
+
+def _ternary_operands(n, k, c, gen):
+    g = G()
+    trits = torch.randint(-1, 2, (n, k), dtype=torch.int8, generator=gen).cuda()
+    d = (0.01 + 0.04 * torch.rand((n, k // 128), generator=gen)).half().cuda()
+    wb = torch.empty((n, k // 128, 28), dtype=torch.uint8, device="cuda")
+    g.wq_pack_ptq1_0(trits, d, wb)
+    x = torch.randn((c, k), generator=gen).cuda()
+    return wb, x
+
+
+@pytest.mark.parametrize("c", [1, 4, 64])
+def test_graph_ternary_pt_layout(c):
+    say("graph wq_quantize_q8_1_pt / wq_gemv_ternary_pt", c)
+    g = G()
+    gen = torch.Generator().manual_seed(200 + c)
+    n, k = 2000, 5120
+    wb, x = _ternary_operands(n, k, c, gen)
+    xp, xp2 = (torch.empty((c, 9 * k // 8), dtype=torch.uint8, device="cuda") for _ in range(2))
+    replay_matches_eager(lambda o: g.wq_quantize_q8_1_pt(x, o), xp, xp2)
+    out = torch.empty((c, n), dtype=torch.float32, device="cuda")
+    replay_matches_eager(lambda o: g.wq_gemv_ternary_pt(wb, xp, k, o), out, torch.empty_like(out))
+
+
+@pytest.mark.parametrize("c", [1, 8, 64])
+def test_graph_gemv_ternary_ptq1_1(c):
+    say("graph wq_gemv_ternary_ptq1_1 / _pt", c)
+    g = G()
+    gen = torch.Generator().manual_seed(300 + c)
+    n, k = 1000, 5120
+    wb, x = _ternary_operands(n, k, c, gen)
+    sup, book, ei, ep = (torch.from_numpy(a).cuda() for a in g.wq_ptq1_1_encode(wb.cpu().numpy()))
+    xq = torch.empty((c, k // 32, 36), dtype=torch.uint8, device="cuda")
+    g.wq_quantize_q8_1(x, xq)
+    xp = torch.empty((c, 9 * k // 8), dtype=torch.uint8, device="cuda")
+    g.wq_quantize_q8_1_pt(x, xp)
+    out = torch.empty((c, n), dtype=torch.float32, device="cuda")
+    replay_matches_eager(lambda o: g.wq_gemv_ternary_ptq1_1(sup, book, ei, ep, xq, k, o), out, torch.empty_like(out))
+    replay_matches_eager(lambda o: g.wq_gemv_ternary_ptq1_1_pt(sup, book, ei, ep, xp, k, o), out,
+                         torch.empty_like(out))
+
+
+def test_graph_gemv_ternary_noalloc():
+    say("graph wq_gemv_ternary_noalloc", 64)
+    g = G()
+    gen = torch.Generator().manual_seed(400)
+    n, k, c = 1000, 5120, 64
+    wb, x = _ternary_operands(n, k, c, gen)
+    xq = torch.empty((c, k // 32, 36), dtype=torch.uint8, device="cuda")
+    g.wq_quantize_q8_1(x, xq)
+    out = torch.empty((c, n), dtype=torch.float32, device="cuda")
+    replay_matches_eager(lambda o: g.wq_gemv_ternary_noalloc(wb, xq, k, o), out, torch.empty_like(out))
