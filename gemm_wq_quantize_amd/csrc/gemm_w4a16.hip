@@ -44,10 +44,16 @@
 // q * s - z * s = (q - z) * s with one FMA -- exact, the product needs at
 // most 17 significant bits -- and rounds the pair to bf16 (RNE) for the
 // MFMA.  No row sums are needed; the only rounding beyond the float32
-// accumulation is that of (q - z) * s to bf16.  This dequantisation is about
-// 23 VALU instructions per B word, so the waves split the tile by columns:
+// accumulation is that of (q - z) * s to bf16.  When the constant zero is a
+// multiple of 2^-5 below 1024 in magnitude (8 in the quantiser's format) the
+// codes come out as fp16 magic numbers instead and v_fma_mix_f32 applies the
+// scale, with the same exact results (unpack8_scaled_mix).  This
+// dequantisation is about 17 VALU instructions per B word (23 with the byte
+// converts), so the waves split the tile by columns:
 // each B word is then converted once per workgroup (with 2 x 2 waves, twice)
 // at the cost of twice the A fragment reads from LDS.
+#include <cmath>
+
 #include "wq_internal.h"
 
 namespace wq {
@@ -138,6 +144,37 @@ __device__ __forceinline__ bf16x8 unpack8_scaled(uint32_t w, float s, float c) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// The same eight weights with the codes taken as fp16 magic numbers: a nibble
+// masked into the low mantissa bits under 0x6400 (1024) reads 1024 + q, one
+// masked into bits 4..7 reads 1024 + 16 q, so four v_and_or_b32 and one
+// shift give all eight codes as fp16 halves, and v_fma_mix_f32 (fp16 source,
+// fp32 scale and addend) forms (1024 + q) * s + c0 and (1024 + 16 q) * s/16 +
+// c1 with c0 = -(1024 + z) * s and c1 = -(64 + z) * s.  Both equal (q - z) * s
+// exactly when z is a multiple of 2^-5 below 1024 in magnitude (the products
+// need at most 19 significant bits and the addends at most 24), so the
+// results are those of unpack8_scaled: 17 VALU instructions per word instead
+// of 23.
+__device__ __forceinline__ bf16x8 unpack8_scaled_mix(uint32_t w, float s, float s16, float c0, float c1,
+                                                     uint32_t magic_v) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint32_t t = w >> 8;
+  const h2 p[4] = {__builtin_bit_cast(h2, and_or(w, 0x000F000Fu, magic_v)),   // elements 0, 1
+                   __builtin_bit_cast(h2, and_or(w, 0x00F000F0u, magic_v)),   // 2, 3 (x 16)
+                   __builtin_bit_cast(h2, and_or(t, 0x000F000Fu, magic_v)),   // 4, 5
+                   __builtin_bit_cast(h2, and_or(t, 0x00F000F0u, magic_v))};  // 6, 7 (x 16)
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float sj = (j & 1) ? s16 : s, cj = (j & 1) ? c1 : c0;
+    const f2 v = {fmaf((float)p[j].x, sj, cj), fmaf((float)p[j].y, sj, cj)};
+    r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // A-tile swizzle: physical 16-byte column of k-chunk c in row r is c ^ swz(r)
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -155,9 +192,10 @@ static_assert(128 * C_PITCH <= NSTAGE * stage_bytes<false, false>(), "epilogue s
 // that the row-sum split below indexes fragments at compile time; GS selects
 // group scales (applied while unpacking B) over one scale per column
 // (applied in the epilogue).
-template <int WN, bool GS, bool GZ>
+template <int WN, bool GS, bool GZ, bool MX>
 __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (*rsx)[4][32]) {
   static_assert(GS || !GZ, "stored zeros of groups come with group scales");
+  static_assert(!MX || (GS && !GZ), "the fp16-magic dequantisation serves group scales with a constant zero");
   constexpr int STAGE = stage_bytes<GS, GZ>();
   constexpr int LOADS_PER_STAGE = loads_per_stage<GS, GZ>();
   // ---- tile order: XCD-aware renumbering, then bands of 8 tile-rows
@@ -287,7 +325,7 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 
   const int lr = lane & 31;   // operand row (A) / column (B) within a 32-block
   const int lh = lane >> 5;   // k half: chunks 4 lh .. 4 lh + 3 of every step
-  const uint32_t magic_v = vconst(0x43004300u);
+  const uint32_t magic_v = vconst(MX ? 0x64006400u : 0x43004300u);
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 
   // LDS byte offsets (within a stage) of this lane's operands
@@ -319,14 +357,21 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   // word -> float scale and offset term: the scale of column n for group g
   // is the high half when n * groups + g is odd (n and lr share parity)
   const float zb = 128.f + p.zero_const;
-  float gsc[NJ], gof[NJ];
+  const float zm0 = -(1024.f + p.zero_const), zm1 = -(64.f + p.zero_const);  // exact when MX
+  float gsc[NJ], gof[NJ], gsc16[NJ], gof16[NJ];
   auto set_s = [&](int kt, const uint32_t (&sw)[NJ], const uint32_t (&zw)[NJ]) {
     const bool hi = (((lr & p.ngroups) ^ (kt >> p.gshift)) & 1) != 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       gsc[j] = __uint_as_float(hi ? (sw[j] & 0xFFFF0000u) : (sw[j] << 16));
-      const float z = GZ ? __uint_as_float(hi ? (zw[j] & 0xFFFF0000u) : (zw[j] << 16)) : p.zero_const;
-      gof[j] = -z * gsc[j];
+      if constexpr (MX) {
+        gsc16[j] = gsc[j] * 0.0625f;
+        gof[j] = zm0 * gsc[j];
+        gof16[j] = zm1 * gsc[j];
+      } else {
+        const float z = GZ ? __uint_as_float(hi ? (zw[j] & 0xFFFF0000u) : (zw[j] << 16)) : p.zero_const;
+        gof[j] = -z * gsc[j];
+      }
     }
   };
   auto read_a = [&](int kt, int ks, bf16x8 (&af)[MI]) {
@@ -371,7 +416,8 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const uint32_t w = ks == 0 ? bw[j].x : ks == 1 ? bw[j].y : ks == 2 ? bw[j].z : bw[j].w;
-      bfr[j] = unpack8_scaled(w, gsc[j], gof[j]);
+      bfr[j] = MX ? unpack8_scaled_mix(w, gsc[j], gsc16[j], gof[j], gof16[j], magic_v)
+                  : unpack8_scaled(w, gsc[j], gof[j]);
     }
   };
   auto mm = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ]) {
@@ -531,14 +577,14 @@ __device__ __forceinline__ void gemm_tile(const GArgs& p, uint8_t* smem, float (
   }
 }
 
-template <bool GS, bool GZ>
+template <bool GS, bool GZ, bool MX>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4a16(GArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * stage_bytes<GS, GZ>()];
   __shared__ __attribute__((aligned(16))) float rsx[2][4][32];  // row sums [wm][row block][row]
   // wave-uniform branch (the wave index is moved to a scalar register)
-  if constexpr (GS) gemm_tile<0, GS, GZ>(p, smem, rsx);
-  else if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1, GS, GZ>(p, smem, rsx);
-  else gemm_tile<0, GS, GZ>(p, smem, rsx);
+  if constexpr (GS) gemm_tile<0, GS, GZ, MX>(p, smem, rsx);
+  else if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) gemm_tile<1, GS, GZ, MX>(p, smem, rsx);
+  else gemm_tile<0, GS, GZ, MX>(p, smem, rsx);
 }
 
 }  // namespace
@@ -562,12 +608,17 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint8_t* b, const uint16_t
   p.gshift = 0;
   while ((int64_t(BK) << p.gshift) < group) ++p.gshift;
   const unsigned nwg = (unsigned)(p.tiles_m * p.tiles_n);
+  // the fp16-magic dequantisation needs z a multiple of 2^-5 with |z| < 1024
+  const float zs = zero_const * 32.f;
+  const bool mix = std::fabs(zero_const) < 1024.f && zs == std::nearbyint(zs);
   if (group == k)
-    hipLaunchKernelGGL((k_gemm_w4a16<false, false>), dim3(nwg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_w4a16<false, false, false>), dim3(nwg), dim3(256), 0, s, p);
   else if (zeros)
-    hipLaunchKernelGGL((k_gemm_w4a16<true, true>), dim3(nwg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_w4a16<true, true, false>), dim3(nwg), dim3(256), 0, s, p);
+  else if (mix)
+    hipLaunchKernelGGL((k_gemm_w4a16<true, false, true>), dim3(nwg), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((k_gemm_w4a16<true, false>), dim3(nwg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_w4a16<true, false, false>), dim3(nwg), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

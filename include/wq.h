@@ -156,8 +156,11 @@ int wq_gemv_w4(const uint8_t* packed, int layout, const void* scales, int scale_
  * 4-byte words of the scale array, so the 2 bytes after its last element
  * may be read and are ignored).  Any m and n (ragged tiles are masked).
  * With one scale per column the zero point folds out exactly through the
- * row sums of A; integer zero points with group scales are exact up to the
- * bf16 rounding of (q - z) * s.
+ * row sums of A.  With group scales each weight is bf16_rne of the exact
+ * (q - z) * s whenever z * s is exact in float32 (z an integer, or any value
+ * with at most 16 significant bits, e.g. a bf16 value); for other zero_const
+ * values (7.3f, 0.1f) the weight is bf16_rne(q * s - fl32(z * s)), whose one
+ * extra float32 rounding can move a weight by one bf16 ulp.
  */
 int wq_gemm_w4a16(const uint16_t* a, const uint8_t* b, int layout, const uint16_t* scales,
                   int64_t group, float zero_const, int64_t m, int64_t n, int64_t k,

@@ -126,23 +126,50 @@ def test_gemm_group_scales(m, n, k, group):
     check_bf16_rownorm(c, o4.gemm_w4a16_rows(a, packed, 1, s, 8.0, group))
 
 
-def test_gemm_group_scales_integer_exact():
+@pytest.mark.parametrize("zc", [8.0, 7.5, -3.25, 0.0])
+def test_gemm_group_scales_integer_exact(zc):
     # power-of-two scales that change per group: every weight is exact in
-    # bf16 and every partial sum a multiple of 1/4 below 2^22, so C must be
+    # bf16 and every partial sum a multiple of 1/8 below 2^21, so C must be
     # the RNE bf16 of the exact sum; taking a scale from the wrong group or
-    # the wrong half of a scale word changes the result
-    say("gemm group scales, integer exact")
+    # the wrong half of a scale word changes the result.  Constant zeros that
+    # are multiples of 1/32 (integer, half-integer, negative, zero) take the
+    # fp16-magic dequantisation.
+    say("gemm group scales, integer exact, zero", zc)
     rng = np.random.default_rng(14)
     m, n, k, group = 256, 264, 1408, 128
     a = rng.integers(-4, 5, (m, k)).astype(np.float32)
     codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
     e = rng.integers(-2, 3, (n, k // group))
     s_bits = fpformat.f32_to_bf16_bits((2.0 ** e).astype(np.float32))
-    c = run(fpformat.f32_to_bf16_bits(a), codes, s_bits, group=group)
-    w = (codes.astype(np.float64) - 8) * np.repeat(2.0 ** e, group, axis=1)
+    c = run(fpformat.f32_to_bf16_bits(a), codes, s_bits, zc=zc, group=group)
+    w = (codes.astype(np.float64) - zc) * np.repeat(2.0 ** e, group, axis=1)
     exact = a.astype(np.float64) @ w.T
     want = fpformat.f32_to_bf16_bits(exact.astype(np.float32))
     assert np.array_equal(c.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+@pytest.mark.parametrize("zc", [7.3, 0.1, 1500.0])
+@pytest.mark.parametrize("m,n,k,group", [(300, 520, 512, 128), (129, 333, 1152, 64)])
+def test_gemm_group_scales_any_zero(m, n, k, group, zc):
+    # constant zeros that are not multiples of 1/32 below 1024 keep the
+    # float32 code convert and one FMA per weight; zc is the float32 the
+    # entry point receives.  For 7.3f and 0.1f, z * s is not exact in float32,
+    # so a weight can sit one bf16 ulp from bf16_rne((q - z) * s): the bar is
+    # the bf16 one, 1e-2 of the row norm of the exact product.  1500 is an
+    # integer (the weights are exact before their bf16 rounding), and with
+    # every weight near -1500 s that rounding alone is about 1% of the row
+    # norm, so it is held to the elementwise bound against the rounded weights
+    say("gemm group scales, zero", m, n, k, group, zc)
+    zc = float(np.float32(zc))
+    p = wq_inputs.grouped_gemm(m, n, k, group, seed=m + n + 2)
+    c = run(p.a_bits, p.codes, p.scale_bits, zc=zc, group=group).float().cpu().numpy()
+    a = fpformat.bf16_bits_to_f32(p.a_bits)
+    s = fpformat.bf16_bits_to_f32(p.scale_bits)
+    packed = o4.pack(p.codes, 1)
+    if zc == int(zc):
+        check_bf16_rows(c, o4.gemm_w4a16_rows_bf16w(a, packed, 1, s, zc, group))
+    else:
+        check_bf16_rownorm(c, o4.gemm_w4a16_rows(a, packed, 1, s, zc, group))
 
 
 def test_gemm_on_quantiser_output():
