@@ -832,27 +832,31 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
 
   // x staging loads go out before the weight prologue (loads complete in
   // issue order, so waiting for x does not wait for the weights).  A lane
-  // stages 16-byte pieces u = (column, chunk, piece) in [C][nchp][4] order,
-  // u = tid + i * NT rotated by a per-workgroup offset: every CU reads the same x, and in the
-  // same order they would all ask the same L2 channel at once.  The four
-  // pieces of a chunk stay on four consecutive lanes (the offset is a
-  // multiple of 4).
+  // stages 16-byte pieces u = (chunk, column, piece) in [nchp][C][4] order,
+  // u = tid + i * NT rotated by a per-workgroup offset: every CU reads the
+  // same x, and in the same order they would all ask the same L2 channel at
+  // once.  The four pieces of a chunk stay on four consecutive lanes (the
+  // offset is a multiple of 4).  Chunk and column come from a division by
+  // the constant C, and the loads are buffer loads without a branch (an
+  // invalid piece reads zeros): with a division by a runtime count and a
+  // branch per load, the address arithmetic of the staging was about 700
+  // instructions per wave ahead of the first weight load.
   const int npieces = C * nchp * 4;
   const int xrot = (int)(((uint32_t)b * 2654435761u) % (uint32_t)(npieces >> 2)) * 4;
   auto piece = [&](int i) {
     const int v = tid + i * QK_NT + xrot;
     return v >= npieces ? v - npieces : v;
   };
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.x, 0, (int)(p.c * p.k * 2), 0x00020000);
   uint4 xr[QK_XP];
 #pragma unroll
   for (int i = 0; i < QK_XP; ++i) {
     const int u = piece(i);
-    const int col = u / (nchp * 4);
-    const int ch = (u >> 2) - col * nchp;
+    const int ch = (u >> 2) / C, col = (u >> 2) - ch * C;
     const bool ok = tid + i * QK_NT < npieces && col < p.c && ch < nchunks;
-    xr[i] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) +
-                                                 (int64_t)col * p.k + ch * 32 + (u & 3) * 8)
-               : make_uint4(0, 0, 0, 0);
+    const uint32_t xo = ok ? (uint32_t)((col * (int)p.k + ch * 32 + (u & 3) * 8) * 2) : OOB;
+    xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0));
   }
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
@@ -873,7 +877,7 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
     sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0xB1, 0xF, 0xF, false));  // quad xor 1
     sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0x4E, 0xF, 0xF, false));  // quad xor 2
     if (tid + i * QK_NT < npieces) {
-      const int col = u / (nchp * 4), ch = (u >> 2) - col * nchp;
+      const int ch = (u >> 2) / C, col = (u >> 2) - ch * C;
       xs[ch * XPC + col * 4 + (u & 3)] = v;
       if ((u & 3) == 0) zs[ch * 4 + col] = sx * zfold;
     }
