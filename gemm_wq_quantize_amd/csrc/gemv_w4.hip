@@ -547,18 +547,22 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
   // lanes of one LDS write cover consecutive chunks of one piece plane:
   // no bank conflicts (lanes writing the four pieces of one chunk would hit
   // the same banks, the planes being a multiple of 256 bytes apart).
+  // Unit u = tid + i * NT is chunk u / C of column u % C: a division by the
+  // constant C (a division by a runtime count put some 140 more instructions
+  // per wave ahead of the first weight load).  The loads stay conditional:
+  // most units are past x (3 per lane cover the widest x), and the waves
+  // with none skip their loads.
   constexpr int XCU = PERSIST_XCHUNKS;  // chunks per lane (the launcher bounds x)
   const int cunits = C * nch;
   uint4 xr[XCU][4];
 #pragma unroll
   for (int i = 0; i < XCU; ++i) {
     const int cidx = tid + i * NT;
-    const int col = cidx / nch;
-    const int kk = (cidx - col * nch) * 32;
-    const bool ok = cidx < cunits && col < p.c && kk < p.k;
+    const int ch = cidx / C, col = cidx - ch * C;
+    const bool ok = cidx < cunits && col < p.c && ch < nchunks;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      xr[i][q] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) + col * p.k + kk + 8 * q)
+      xr[i][q] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.x) + col * p.k + ch * 32 + 8 * q)
                     : make_uint4(0, 0, 0, 0);
   }
   // weight prologue: D items in flight per half-wave
@@ -571,8 +575,7 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_persist(KArgs p, int sph) {
     const int cidx = tid + i * NT;
     if (i * NT >= cunits) break;  // uniform over the workgroup
     if (cidx < cunits) {
-      const int col = cidx / nch;
-      const int ch = cidx - col * nch;
+      const int ch = cidx / C, col = cidx - ch * C;
       float pq[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -849,13 +852,15 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
   };
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.x, 0, (int)(p.c * p.k * 2), 0x00020000);
+  const uint32_t xcols = (uint32_t)p.c, xrow = (uint32_t)p.k * 2u;
   uint4 xr[QK_XP];
 #pragma unroll
   for (int i = 0; i < QK_XP; ++i) {
     const int u = piece(i);
-    const int ch = (u >> 2) / C, col = (u >> 2) - ch * C;
-    const bool ok = tid + i * QK_NT < npieces && col < p.c && ch < nchunks;
-    const uint32_t xo = ok ? (uint32_t)((col * (int)p.k + ch * 32 + (u & 3) * 8) * 2) : OOB;
+    const uint32_t cc = (uint32_t)u >> 2, ch = cc / C, col = cc - ch * C;
+    // (& rather than &&: no branch around the load)
+    const bool ok = (tid + i * QK_NT < npieces) & (col < xcols) & (ch < (uint32_t)nchunks);
+    const uint32_t xo = ok ? col * xrow + ch * 64u + (uint32_t)(u & 3) * 16u : OOB;
     xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0));
   }
 #pragma unroll
@@ -877,7 +882,7 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
     sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0xB1, 0xF, 0xF, false));  // quad xor 1
     sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0x4E, 0xF, 0xF, false));  // quad xor 2
     if (tid + i * QK_NT < npieces) {
-      const int ch = (u >> 2) / C, col = (u >> 2) - ch * C;
+      const uint32_t cc = (uint32_t)u >> 2, ch = cc / C, col = cc - ch * C;
       xs[ch * XPC + col * 4 + (u & 3)] = v;
       if ((u & 3) == 0) zs[ch * 4 + col] = sx * zfold;
     }
