@@ -1167,10 +1167,18 @@ __global__ __launch_bounds__(NT) void k_gemv_w4_mfma(KArgs p, int rows_per_wg) {
             t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xc[cb][m]), wb[m], t, 0, 0, 0);
           floatx4 u;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) u[i] = sc * fmaf(-zb, sx[cb][i], t[i]);
+          for (int i = 0; i < 4; ++i) u[i] = fmaf(-zb, sx[cb][i], t[i]);
+          // acc += s * u on the one tile's accumulator, behind a uniform
+          // branch (the empty asm keeps the compiler from updating every
+          // tile's accumulator and selecting, about 60 VALU instructions per
+          // item at six tiles)
 #pragma unroll
           for (int rt = 0; rt < NRT; ++rt)
-            if (rt == crt) acc[rt][cb] += u;  // uniform
+            if (rt == crt) {
+              asm volatile("");
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[rt][cb][i] = fmaf(sc, u[i], acc[rt][cb][i]);
+            }
         }
         if (++crt == nrt) {  // next k group: its x was loaded one group ahead
           crt = 0;
