@@ -853,40 +853,51 @@ __global__ __launch_bounds__(QK_NT) void k_gemv_w4_quad(KArgs p, int spw) {
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.x, 0, (int)(p.c * p.k * 2), 0x00020000);
   const uint32_t xcols = (uint32_t)p.c, xrow = (uint32_t)p.k * 2u;
-  uint4 xr[QK_XP];
-#pragma unroll
-  for (int i = 0; i < QK_XP; ++i) {
-    const int u = piece(i);
-    const uint32_t cc = (uint32_t)u >> 2, ch = cc / C, col = cc - ch * C;
-    // (& rather than &&: no branch around the load)
-    const bool ok = (tid + i * QK_NT < npieces) & (col < xcols) & (ch < (uint32_t)nchunks);
-    const uint32_t xo = ok ? col * xrow + ch * 64u + (uint32_t)(u & 3) * 16u : OOB;
-    xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0));
-  }
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue(d);
-
-  // x into LDS; per chunk the offset term of the zero-point fold
-  // -(128 + z) * sum x (with stored zeros: sum x, scaled per row later)
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
   const float zfold = HZ ? 1.f : -(128.f + p.zero_const);
+  // R rounds of x loads (R * NT >= npieces), the weight prologue, then x
+  // into LDS with per chunk the offset term of the zero-point fold
+  // -(128 + z) * sum x (with stored zeros: sum x, scaled per row later).
+  // R is a compile-time count chosen from the x size below: rounds past x
+  // would still take address-unit time ahead of the weight loads (an
+  // out-of-range buffer load is not free), and with a runtime count the
+  // compiler waits for every x load before the first LDS write.
+  auto stage = [&](auto rounds) {
+    constexpr int R = decltype(rounds)::value;
+    uint4 xr[R];
 #pragma unroll
-  for (int i = 0; i < QK_XP; ++i) {
-    if (i * QK_NT >= npieces) break;  // uniform
-    const int u = piece(i);
-    const uint4 v = xr[i];
-    float sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), ones, 0.f, false);
-    sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), ones, sx, false);
-    sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), ones, sx, false);
-    sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), ones, sx, false);
-    sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0xB1, 0xF, 0xF, false));  // quad xor 1
-    sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0x4E, 0xF, 0xF, false));  // quad xor 2
-    if (tid + i * QK_NT < npieces) {
+    for (int i = 0; i < R; ++i) {
+      const int u = piece(i);
       const uint32_t cc = (uint32_t)u >> 2, ch = cc / C, col = cc - ch * C;
-      xs[ch * XPC + col * 4 + (u & 3)] = v;
-      if ((u & 3) == 0) zs[ch * 4 + col] = sx * zfold;
+      // (& rather than &&: no branch around the load)
+      const bool ok = (tid + i * QK_NT < npieces) & (col < xcols) & (ch < (uint32_t)nchunks);
+      const uint32_t xo = ok ? col * xrow + ch * 64u + (uint32_t)(u & 3) * 16u : OOB;
+      xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xo, 0, 0));
     }
-  }
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (i * QK_NT >= npieces) break;  // uniform
+      const int u = piece(i);
+      const uint4 v = xr[i];
+      float sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), ones, 0.f, false);
+      sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), ones, sx, false);
+      sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), ones, sx, false);
+      sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), ones, sx, false);
+      sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0xB1, 0xF, 0xF, false));  // quad xor 1
+      sx += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sx), 0x4E, 0xF, 0xF, false));  // quad xor 2
+      if (tid + i * QK_NT < npieces) {
+        const uint32_t cc = (uint32_t)u >> 2, ch = cc / C, col = cc - ch * C;
+        xs[ch * XPC + col * 4 + (u & 3)] = v;
+        if ((u & 3) == 0) zs[ch * 4 + col] = sx * zfold;
+      }
+    }
+  };
+  static_assert(QK_XP >= 5, "round counts");
+  if (npieces <= 2 * QK_NT) stage(std::integral_constant<int, 2>{});
+  else if (npieces <= 5 * QK_NT) stage(std::integral_constant<int, 5>{});
+  else stage(std::integral_constant<int, QK_XP>{});
   __syncthreads();
 
   const float zconst = 128.f + p.zero_const;
